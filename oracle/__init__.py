@@ -1,0 +1,34 @@
+"""CPU oracle for tree verification — TEST INFRASTRUCTURE ONLY.
+
+Plain, slow, obviously-correct NumPy (fp64) definitions of what the hot path
+computes: tree metadata, tree-masked attention over a paged prefix, the
+multi-step speculative-sampling walk with siblings drawn without replacement,
+and longest-accepted-path selection. Each function cites the passage of the
+source pages it follows:
+
+  [survey]    "Tree-based speculative decoding: draft trees win latency, lose
+              batches, return cost-aware" (speculative-decoding.pages.dev)
+  [TreeSpark] TreeSpark: Markov-conditioned draft trees (paperpeel 2609.22098)
+  [explainer] tree-vs-chain interview explainer (zenaique, io-tree-spec-decoding)
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import
+this package. The HIP library shares no code with it, and the product path
+never calls it.
+"""
+from .tree import (check_tree, depths, ancestors_or_self, children,
+                   ancestor_bitsets, first_child_next_sibling)
+from .attention import tree_attention, tree_attention_rows, decode_values
+from .sampler import (softmax_T, proposal_without, residual_update,
+                      acceptance_ratio, inverse_cdf, greedy_request,
+                      walk_request, tree_spec_sample)
+from .path import accept_path_request, tree_accept_path
+from .enumerate import enumerate_node_laws
+
+__all__ = [
+    "check_tree", "depths", "ancestors_or_self", "children", "ancestor_bitsets",
+    "first_child_next_sibling", "tree_attention", "tree_attention_rows",
+    "decode_values", "softmax_T", "proposal_without", "residual_update",
+    "acceptance_ratio", "inverse_cdf", "greedy_request", "walk_request",
+    "tree_spec_sample", "accept_path_request", "tree_accept_path",
+    "enumerate_node_laws",
+]
