@@ -1,0 +1,272 @@
+"""Tree-verification benchmark on one MI355X.
+
+One step = one pass of the whole hot path over one batch:
+  tree_verify_attn (one attention layer, every tree row of every request)
+  -> tree_spec_sample (greedy / without-replacement rejection walk)
+  -> tree_accept_path (longest accepted path, emitted tokens, KV keep-list).
+Workload (default): "highload" — 64 requests, prefixes U{512..8192}, per-request
+budget from {8-row chain, 16-row tree, 32-row tree}, 32 q / 8 kv heads, D 128,
+bf16 paged KV; sampler over V = 151936 with per-request T in {0, 0.5, 1}.
+Inputs are synthetic, seeded, and resident in HBM before timing starts.
+
+Prints ONE JSON line: value = tree nodes verified per second (whole step),
+plus the attention kernel's roofline and the CPU oracle's rate on a sample.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "tree-verify nodes/s per layer + achieved HBM GB/s (% of MI355X peak), 1 GPU"
+HBM_PEAK_GBS = 8000.0
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "attn_mfma_highload_counters.md")
+ATTN_SOURCE = os.path.join(ROOT, "tree_verification_verify_amd", "csrc", "tree_attn.hip")
+
+
+def attn_algorithmic_bytes(inp):
+    """KV read once per kv head + Q in + O out (bf16: 2 bytes/element)."""
+    s = 2 if inp.dtype == "bf16" else 4
+    total = 0
+    for r in range(inp.batch):
+        L = inp.kv_len(r)
+        N = inp.nodes(r)
+        total += L * inp.num_kv_heads * inp.head_dim * 2 * s
+        total += 2 * N * inp.num_q_heads * inp.head_dim * s
+    return total
+
+
+def attn_algorithmic_flops(cfg):
+    import oracle
+    inp = cfg.attn
+    f = 0
+    for r, parent in enumerate(cfg.trees):
+        d = oracle.depths(parent)
+        f += int(sum(4 * inp.num_q_heads * inp.head_dim * (inp.prefix_len[r] + di + 1) for di in d))
+    return f
+
+
+def sampler_algorithmic_bytes(sinp, out_len):
+    """Rows the walk must read: every target row at T = 0 (eager greedy
+    flags); the target and draft row of each visited node at T > 0."""
+    V = sinp.vocab
+    total = 0
+    for r in range(sinp.batch):
+        n = int(sinp.node_indptr[r + 1] - sinp.node_indptr[r])
+        if float(sinp.temperature[r]) == 0.0:
+            total += n * V * 4
+        else:
+            total += int(out_len[r]) * V * 4 * 2
+    return total
+
+
+def read_traffic():
+    """HBM bytes per attention launch from the committed counter summary,
+    or None when the kernel source changed since the counters were taken."""
+    if not os.path.exists(PROFILE_COUNTERS):
+        return None
+    text = open(PROFILE_COUNTERS).read()
+    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_b:
+        return None
+    sha = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
+    if sha != m_sha.group(1):
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(cfg, budget_s=12.0):
+    """The oracle as it stands on the first requests of the same workload,
+    until ~budget_s of CPU time; returns nodes/s and what was sampled."""
+    import oracle
+    from workloads.inputs import SamplerInputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    inp, s = cfg.attn, cfg.sampler
+    t0 = time.perf_counter()
+    nodes = 0
+    done = 0
+    for r in range(inp.batch):
+        n = inp.nodes(r)
+        oracle.tree_attention_rows(inp, [(r, i) for i in range(n)])
+        a, b = int(s.node_indptr[r]), int(s.node_indptr[r + 1])
+        one = SamplerInputs(vocab=s.vocab, target_logits=s.target_logits[a:b],
+                            draft_logits=None if s.draft_logits is None else s.draft_logits[a:b],
+                            tokens=s.tokens[a:b], node_indptr=np.array([0, b - a], np.int32),
+                            parent=s.parent[a:b], temperature=s.temperature[r:r + 1],
+                            uniforms=s.uniforms[a:b])
+        f, nt, _ = oracle.tree_spec_sample(one)
+        oracle.tree_accept_path(one.node_indptr, one.parent, one.tokens, f, nt,
+                                [int(inp.prefix_len[r])], 16)
+        nodes += n
+        done += 1
+        if time.perf_counter() - t0 > budget_s and done >= 2:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": nodes / dt, "unit": "nodes/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {done} of {inp.batch} requests ({nodes} tree rows): fp64 NumPy "
+                      f"attention + sampling walk + path, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="highload")
+    ap.add_argument("--temperature", default="mixed")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead of the workload, time a plain device copy of this many "
+                         "bytes (calibrates the HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU; --gpus must be 1 "
+                                   "(requests and kv heads shard across GPUs with no "
+                                   "exchange, see the design notes)"}))
+        sys.exit(2)
+
+    import torch
+    if args.copy_bytes:
+        src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
+        print(json.dumps({"copy_bytes": src.numel() * 4, "ms": dt * 1e3,
+                          "GBs_read_plus_write": 2 * src.numel() * 4 / dt / 1e9}))
+        return
+    import tree_verification_verify_amd as tv
+    from workloads import make_config
+    from workloads.device import attention_tensors, sampler_tensors
+
+    temp = args.temperature if args.temperature == "mixed" else float(args.temperature)
+    cfg = make_config(args.config, temperature=temp)
+    inp, s = cfg.attn, cfg.sampler
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    a = attention_tensors(inp, dev)
+    desc = tv.attn_desc(inp.batch, inp.num_q_heads, inp.num_kv_heads, inp.head_dim,
+                        inp.max_nodes, inp.max_depth, inp.max_kv_len, inp.num_pages, inp.dtype)
+    aws = tv.alloc_workspace(tv.attn_workspace_size(desc), dev)
+    out = torch.empty_like(a["q"])
+    have_sampler = s is not None
+    if have_sampler:
+        st = sampler_tensors(s, dev)
+        md = max(8, inp.max_depth)
+        sdesc = tv.sample_desc(s.batch, s.vocab, s.max_nodes, md)
+        sws = tv.alloc_workspace(tv.sample_workspace_size(sdesc), dev)
+        T = int(s.node_indptr[-1])
+        flag = torch.empty(T, dtype=torch.int8, device=dev)
+        nt = torch.empty(T, dtype=torch.int32, device=dev)
+        B = s.batch
+        pn = torch.empty(B * (md + 1), dtype=torch.int32, device=dev)
+        ot, kk = torch.empty_like(pn), torch.empty_like(pn)
+        ol = torch.empty(B, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+    def step(e=None):
+        if e:
+            e[0].record(stream)
+        tv.tree_verify_attn(desc, a["q"], a["k_pages"], a["v_pages"], a["page_indptr"],
+                            a["page_indices"], a["prefix_len"], a["node_indptr"], a["parent"],
+                            out, aws)
+        if e:
+            e[1].record(stream)
+        if have_sampler:
+            tv.tree_spec_sample(sdesc, st["target_logits"], st["draft_logits"], st["tokens"],
+                                st["node_indptr"], st["parent"], st["temperature"],
+                                st["uniforms"], flag, nt, sws)
+            if e:
+                e[2].record(stream)
+            tv.tree_accept_path(B, md, st["node_indptr"], st["parent"], st["tokens"], flag, nt,
+                                a["prefix_len"], pn, ot, ol, kk, sws)
+        if e:
+            e[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    for ws_ in (aws,) + ((sws,) if have_sampler else ()):
+        status, bits = tv.device_status(ws_)
+        if status != 0:
+            raise SystemExit(f"device status {status} bits {bits}")
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for k in range(args.steps):
+        step(ev[k])
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    attn_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    samp_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) if have_sampler else 0.0
+    path_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev])) if have_sampler else 0.0
+
+    nodes = inp.total_nodes
+    abytes = attn_algorithmic_bytes(inp)
+    aflops = attn_algorithmic_flops(cfg)
+    achieved = abytes / (attn_ms * 1e-3) / 1e9
+    traffic = read_traffic()
+    res = {
+        "metric": METRIC,
+        "value": nodes / (ms_step * 1e-3),
+        "unit": "nodes/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": inp.dtype,
+        "data": "synthetic (seeded; shapes of the pages' workloads)",
+        "config": {"workload": f"{args.config}: {inp.batch} requests, {nodes} tree rows, "
+                               f"prefix {int(inp.prefix_len.min())}-{int(inp.prefix_len.max())}, "
+                               f"Hq {inp.num_q_heads}/Hkv {inp.num_kv_heads}/D {inp.head_dim} "
+                               f"{inp.dtype} paged KV"
+                               + (f"; sampler V {s.vocab}, T {args.temperature}" if have_sampler else ""),
+                   "batch": inp.batch, "tree_rows": nodes, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic,
+                     "kernel": "attn_mfma_kernel<128> (tree_verify_attn)",
+                     "algorithmic_bytes": abytes, "algorithmic_flops": aflops,
+                     "kernel_ms": attn_ms,
+                     "tflops": aflops / (attn_ms * 1e-3) / 1e12},
+        "breakdown_ms": {"tree_verify_attn": attn_ms, "tree_spec_sample": samp_ms,
+                         "tree_accept_path": path_ms},
+        "attn_nodes_per_s": nodes / (attn_ms * 1e-3),
+    }
+    if have_sampler:
+        out_len = ol.cpu().numpy()
+        sbytes = sampler_algorithmic_bytes(s, out_len)
+        res["sampler"] = {"algorithmic_bytes": sbytes,
+                          "achieved_GBs": sbytes / (samp_ms * 1e-3) / 1e9 if samp_ms > 0 else None,
+                          "mean_emitted": float(out_len.mean()), "dtype": "f64"}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,241 @@
+/*
+ * tree_verify.h — C ABI of libtreeverify, tree verification for tree-based
+ * speculative decoding on AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages; sections named, not line numbers):
+ *   [survey]    "Tree-based speculative decoding: draft trees win latency,
+ *               lose batches, return cost-aware", sections Timeline,
+ *               Taxonomy, Systems.
+ *   [TreeSpark] TreeSpark: Markov-conditioned draft trees (paper 2609.22098),
+ *               §3.1, §3.2 (step 3), §3.3 (Proposition 1), §4, §5.1.
+ *   [explainer] tree-vs-chain explainer, "Red flags & common mistakes".
+ *
+ * Conventions (all entry points)
+ *   - Array arguments are DEVICE pointers unless the name ends in _host.
+ *   - The caller owns every buffer, the workspace included. The library never
+ *     allocates device memory, never synchronises (tv_device_status aside)
+ *     and keeps no per-call state outside the workspace. Host-side argument
+ *     errors are returned before anything is launched.
+ *   - Calls are stream-ordered and re-entrant; concurrent streams need
+ *     distinct workspaces. A workspace must be zero-filled once
+ *     (tv_workspace_init) before its first use; calls leave its
+ *     synchronisation counters at zero when they complete.
+ *   - Anomalies found on the device (bad parent, page id out of range, too
+ *     few pages, NaN/Inf logits, two accepted siblings, a stalled team
+ *     barrier) set bits of a status word at the start of the workspace; they
+ *     never fault. Read it with tv_device_status; clear it with
+ *     tv_workspace_init.
+ *   - Trees are flattened in topological order: request r owns rows
+ *     node_indptr[r] .. node_indptr[r+1]-1; parent[] holds request-local
+ *     indices with parent[0] = -1 and 0 <= parent[i] < i; siblings appear in
+ *     ascending index in draw order ([survey] Timeline: tree tokens stored in
+ *     the KV cache by topology; [TreeSpark] §1: sibling draw order).
+ */
+#ifndef TREE_VERIFY_H
+#define TREE_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TV_OK = 0,
+  TV_ERR_NULL = 1,       /* a required pointer is NULL */
+  TV_ERR_SHAPE = 2,      /* inconsistent or unsupported sizes */
+  TV_ERR_DTYPE = 3,      /* unsupported element type */
+  TV_ERR_WORKSPACE = 4,  /* workspace too small or misaligned */
+  TV_ERR_TREE = 5,       /* parent array violates the topological rules */
+  TV_ERR_PAGES = 6,      /* page table does not cover a request or id out of range */
+  TV_ERR_HIP = 7,        /* a HIP runtime call failed (tv_last_hip_error) */
+  TV_ERR_LOGITS = 8,     /* NaN or Inf logits, or draft logits missing at T > 0 */
+  TV_ERR_PATH = 9,       /* two accepted siblings */
+  TV_ERR_TIMEOUT = 10    /* a team barrier exceeded its spin limit */
+} tv_status;
+
+typedef enum { TV_FP32 = 0, TV_BF16 = 1 } tv_dtype;
+
+/* Bits of the device status word (first 4 bytes of a workspace). */
+enum {
+  TV_DEV_TREE = 1u << 0,
+  TV_DEV_PAGES = 1u << 1,
+  TV_DEV_LOGITS = 1u << 2,
+  TV_DEV_PATH = 1u << 3,
+  TV_DEV_TIMEOUT = 1u << 4,
+  TV_DEV_SHAPE = 1u << 5
+};
+
+/* Attention problem description (host memory). Maxima bound every request
+ * and size the launch and the workspace; the device rejects requests that
+ * exceed them (status bit TV_DEV_SHAPE) instead of reading past a buffer. */
+typedef struct {
+  int32_t batch;         /* B >= 1 */
+  int32_t num_q_heads;   /* Hq, a multiple of num_kv_heads */
+  int32_t num_kv_heads;  /* Hkv; q head h reads kv head h / (Hq/Hkv) */
+  int32_t head_dim;      /* D: 64 or 128 */
+  int32_t page_size;     /* must be 16 */
+  int32_t max_nodes;     /* >= max_r N_r, <= 1024 */
+  int32_t max_depth;     /* >= deepest node (edges from the root) */
+  int32_t max_kv_len;    /* >= max_r (P_r + N_r) */
+  int32_t num_pages;     /* physical pages in k_pages / v_pages */
+  tv_dtype dtype;        /* TV_BF16 (MFMA path) or TV_FP32 (VALU path) */
+  float sm_scale;        /* softmax scale; 0 means 1/sqrt(D) */
+} tv_attn_desc;
+
+/* Sampler problem description (host memory). */
+typedef struct {
+  int32_t batch;         /* B >= 1 */
+  int32_t vocab;         /* V >= 1 */
+  int32_t max_nodes;     /* >= max_r N_r, <= 65536 */
+  int32_t max_depth;     /* >= deepest node */
+} tv_sample_desc;
+
+/* ---- workspace -------------------------------------------------------- */
+
+/* Bytes of workspace tree_verify_attn needs for desc (0 if desc is invalid).
+ * Holds the status word, split-merge counters and fp32 partial results. */
+size_t tv_attn_workspace_size(const tv_attn_desc* desc);
+
+/* Bytes of workspace tree_spec_sample needs (0 if desc is invalid). */
+size_t tv_sample_workspace_size(const tv_sample_desc* desc);
+
+/* Zero-fill a workspace on stream (a fill kernel, safe under graph capture).
+ * Required once before first use, and after any call that reported a
+ * device error. */
+tv_status tv_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Synchronise stream, read the status word of workspace, return the
+ * highest-priority error it holds (TV_OK if none) and, if bits_out is not
+ * NULL, the raw TV_DEV_* bits. Does not clear them. */
+tv_status tv_device_status(const void* workspace, hipStream_t stream, uint32_t* bits_out);
+
+/* ---- the hot path ----------------------------------------------------- */
+
+/* Tree-masked attention, one layer ([survey] Timeline: SpecInfer's
+ * tree-based parallel decoding — tree tokens in the KV cache in topological
+ * order, attention masked to ancestors; [TreeSpark] §3.2 step 3: one target
+ * pass with a tree attention mask; §4: ancestor-bitmask mask).
+ *
+ * For request r, q head h, local row i (logical position P_r + i):
+ *   visible(i) = {0 .. P_r-1} U {P_r + j : j ancestor of i or j == i}
+ *   out[i,h]   = sum_{t in visible(i)} softmax_t(sm_scale * q[i,h].K[t,g]) V[t,g],
+ *   g = h / (Hq / Hkv).
+ * Arguments:
+ *   q        [T][Hq][D] in desc->dtype, T = node_indptr[B]
+ *   k_pages, v_pages [num_pages][Hkv][16][D] in desc->dtype; logical position
+ *            t of request r lives in physical page
+ *            page_indices[page_indptr[r] + t/16], slot t%16. The caller has
+ *            already written the tree's own K/V at P_r .. P_r+N_r-1 (with
+ *            RoPE at per-depth positions applied before the call).
+ *   page_indptr [B+1], page_indices [page_indptr[B]]  (int32)
+ *   prefix_len [B]   P_r >= 0 (int32)
+ *   node_indptr [B+1], parent [T]  (int32; see the tree conventions above)
+ *   out      [T][Hq][D] in desc->dtype (bf16 rounded to nearest even from fp32)
+ *   workspace >= tv_attn_workspace_size(desc) bytes, 256-byte aligned.
+ * Returns TV_OK after launching; device-side problems go to the status word
+ * (the affected rows are then unspecified, never out-of-bounds). */
+tv_status tree_verify_attn(const tv_attn_desc* desc,
+                           const void* q, const void* k_pages, const void* v_pages,
+                           const int32_t* page_indptr, const int32_t* page_indices,
+                           const int32_t* prefix_len, const int32_t* node_indptr,
+                           const int32_t* parent, void* out,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Multi-step speculative sampling over the tree ([survey] Timeline and
+ * Taxonomy rules (a) and (c); [TreeSpark] §1 and §3.3, Proposition 1).
+ *
+ * Row i of the logits is the distribution of the token AFTER node i
+ * ([TreeSpark] §3.1, LM-shifted alignment). Per request r with T = temperature[r]:
+ *   T == 0 (greedy exact match): next_token[i] = argmax target row i (lowest
+ *     index on ties) for EVERY node; accept_flag[i] = (tokens[i] ==
+ *     next_token[parent[i]]); accept_flag[root] = 1.
+ *   T > 0 (rejection walk without replacement): starting at the root v, with
+ *     p = softmax(target_v / T), q = softmax(draft_v / T), the children
+ *     c_1 < c_2 < ... of v (draw order) are tested in turn: c_j is accepted
+ *     iff uniforms[c_j][0] < p_j(x_j) / q_j(x_j), where q_j is q with the
+ *     tokens x_1..x_{j-1} removed and renormalised and p_j the residual
+ *     (p_1 = p; after a rejection p_{j+1} = max(p_j - q_j, 0) renormalised).
+ *     An accepted child becomes v. When no child is accepted (or v is a
+ *     leaf) the walk stops: next_token[v] = smallest y with
+ *     cumsum(p_final)[y] > uniforms[v][1] * sum(p_final), p_final being the
+ *     residual (the target p at a leaf or when v has no children).
+ *     accept_flag: 1 for the root and accepted nodes, 0 otherwise (tested
+ *     and rejected, or never tested); next_token = -1 except at the stop node.
+ * Arguments:
+ *   target_logits, draft_logits [T][V] fp32; draft_logits may be NULL when
+ *     every temperature is 0 (a T > 0 request then sets TV_DEV_LOGITS).
+ *   tokens [T] int32 token of each node (root ignored); siblings distinct.
+ *   node_indptr [B+1], parent [T] int32; temperature [B] fp32 >= 0;
+ *   uniforms [T][2] fp32 in [0,1).
+ *   accept_flag [T] int8, next_token [T] int32: outputs.
+ * Arithmetic is fp64 (exp, sums, ratios); decisions therefore match an fp64
+ * reference except within ~1e-12 of a threshold. */
+tv_status tree_spec_sample(const tv_sample_desc* desc,
+                           const float* target_logits, const float* draft_logits,
+                           const int32_t* tokens, const int32_t* node_indptr,
+                           const int32_t* parent, const float* temperature,
+                           const float* uniforms, int8_t* accept_flag,
+                           int32_t* next_token,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Longest accepted path ([TreeSpark] §3.2 step 3: commit the longest
+ * surviving root path plus one correction/bonus token; §5.1: tau = accepted
+ * length + 1; [explainer] exactly one path is accepted; [survey] Systems:
+ * the accepted slots feed KV compaction).
+ * Per request: follow accept_flag from the root through the unique flagged
+ * child. Outputs, each [B][max_depth+1] int32 padded with -1:
+ *   path_nodes: request-local rows of the path, root first
+ *   out_tokens: tokens of the path's non-root nodes, then next_token[stop]
+ *   kv_keep:    logical KV positions prefix_len[r] + node of the path rows
+ * and out_len [B] = path length (accepted drafts + 1). A node with two
+ * flagged children sets out_len[r] = -1 and, if status_workspace is not
+ * NULL, TV_DEV_PATH in its status word. */
+tv_status tree_accept_path(int32_t batch, int32_t max_depth,
+                           const int32_t* node_indptr, const int32_t* parent,
+                           const int32_t* tokens, const int8_t* accept_flag,
+                           const int32_t* next_token, const int32_t* prefix_len,
+                           int32_t* path_nodes, int32_t* out_tokens,
+                           int32_t* out_len, int32_t* kv_keep,
+                           void* status_workspace, hipStream_t stream);
+
+/* Tree metadata ([TreeSpark] §3.2 step 3 and §4: per-depth position ids and
+ * ancestor bitmasks). For every row: depth (edges from the root),
+ * anc_bits [T][ceil(max_nodes/32)] (bit j of word j/32 set iff j is an
+ * ancestor of the row or the row itself), and children in draw order as
+ * first_child / next_sibling (request-local, -1 = none). Any output may be
+ * NULL. Bad parents set TV_DEV_TREE in status_workspace (if not NULL). */
+tv_status tv_tree_meta(int32_t batch, int32_t max_nodes,
+                       const int32_t* node_indptr, const int32_t* parent,
+                       int32_t* depth, uint32_t* anc_bits,
+                       int32_t* first_child, int32_t* next_sibling,
+                       void* status_workspace, hipStream_t stream);
+
+/* ---- host-side validators (host arrays; no GPU needed) ---------------- */
+
+/* TV_ERR_TREE unless every request's parent array is topological, has a
+ * single root at row 0, N_r <= max_nodes and depth <= max_depth. */
+tv_status tv_validate_tree(int32_t batch, const int32_t* node_indptr_host,
+                           const int32_t* parent_host, int32_t max_nodes,
+                           int32_t max_depth);
+
+/* TV_ERR_PAGES unless each request's listed pages cover P_r + N_r tokens and
+ * every page id is in [0, num_pages). */
+tv_status tv_validate_pages(int32_t batch, const int32_t* page_indptr_host,
+                            const int32_t* page_indices_host,
+                            const int32_t* prefix_len_host,
+                            const int32_t* node_indptr_host, int32_t num_pages,
+                            int32_t page_size);
+
+const char* tv_status_string(tv_status status);
+/* Message of the last failed HIP call on this thread ("" if none). */
+const char* tv_last_hip_error(void);
+int32_t tv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREE_VERIFY_H */

@@ -1,0 +1,54 @@
+"""Run the HIP path through the C ABI on generated inputs (GPU tests only)."""
+import numpy as np
+
+
+def run_attention(inp, repeat=1, sm_scale=0.0):
+    import torch
+    import tree_verification_verify_amd as tv
+    from workloads.device import attention_tensors
+    t = attention_tensors(inp)
+    desc = tv.attn_desc(inp.batch, inp.num_q_heads, inp.num_kv_heads, inp.head_dim,
+                        max(1, inp.max_nodes), inp.max_depth, max(inp.max_kv_len, inp.max_nodes),
+                        inp.num_pages, inp.dtype, sm_scale)
+    ws = tv.alloc_workspace(tv.attn_workspace_size(desc))
+    outs = []
+    for _ in range(repeat):
+        out = torch.full_like(t["q"], float("nan"))
+        tv.tree_verify_attn(desc, t["q"], t["k_pages"], t["v_pages"], t["page_indptr"],
+                            t["page_indices"], t["prefix_len"], t["node_indptr"],
+                            t["parent"], out, ws)
+        outs.append(out)
+    st, bits = tv.device_status(ws)
+    res = [o.float().cpu().numpy().astype(np.float64) for o in outs]
+    return (res if repeat > 1 else res[0]), st, bits
+
+
+def run_sampler(inp, max_depth=None, prefix_lens=None):
+    import torch
+    import tree_verification_verify_amd as tv
+    from workloads.device import sampler_tensors
+    t = sampler_tensors(inp)
+    md = max_depth if max_depth is not None else inp.max_nodes
+    desc = tv.sample_desc(inp.batch, inp.vocab, inp.max_nodes, md)
+    ws = tv.alloc_workspace(tv.sample_workspace_size(desc))
+    T = int(inp.node_indptr[-1])
+    flag = torch.full((T,), -7, dtype=torch.int8, device="cuda")
+    nt = torch.full((T,), -7, dtype=torch.int32, device="cuda")
+    tv.tree_spec_sample(desc, t["target_logits"], t["draft_logits"], t["tokens"],
+                        t["node_indptr"], t["parent"], t["temperature"], t["uniforms"],
+                        flag, nt, ws)
+    B, W = inp.batch, md + 1
+    pn = torch.empty(B * W, dtype=torch.int32, device="cuda")
+    ot = torch.empty_like(pn)
+    kk = torch.empty_like(pn)
+    ol = torch.empty(B, dtype=torch.int32, device="cuda")
+    if prefix_lens is None:
+        prefix_lens = [0] * B
+    prefix = torch.tensor(prefix_lens, dtype=torch.int32, device="cuda")
+    tv.tree_accept_path(B, md, t["node_indptr"], t["parent"], t["tokens"], flag, nt, prefix,
+                        pn, ot, ol, kk, ws)
+    st, bits = tv.device_status(ws)
+    return dict(flag=flag.cpu().numpy(), next_token=nt.cpu().numpy(),
+                path_nodes=pn.cpu().numpy().reshape(B, W), out_tokens=ot.cpu().numpy().reshape(B, W),
+                out_len=ol.cpu().numpy(), kv_keep=kk.cpu().numpy().reshape(B, W),
+                status=st, bits=bits, max_depth=md)

@@ -1,0 +1,155 @@
+"""GPU parity: tree_verify_attn (HIP, via the C ABI) against the fp64 oracle.
+
+Tolerances: max |GPU - oracle| <= 2e-2 for bf16 inputs (bf16 output rounding
+plus bf16 P in the PV product) and <= 1e-5 for fp32 inputs.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from workloads import (make_config, make_attention_inputs, random_tree, chain_tree,
+                       star_tree, expansion_vector_tree)
+from workloads.inputs import repage
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "fp32": 1e-5}
+
+
+def _run(inp, **kw):
+    from gpu_run import run_attention
+    return run_attention(inp, **kw)
+
+
+def _check(inp, got, st, ref=None, picks=None):
+    assert st == 0
+    if picks is None:
+        ref = oracle.tree_attention(inp) if ref is None else ref
+        err = np.abs(got - ref).max()
+    else:
+        ref = oracle.tree_attention_rows(inp, picks)
+        rows = np.stack([got[int(inp.node_indptr[r]) + i] for r, i in picks])
+        err = np.abs(rows - ref).max()
+    assert np.isfinite(got).all() if picks is None else True
+    assert err <= TOL[inp.dtype], err
+    return err
+
+
+def test_tiny_fp32():
+    cfg = make_config("tiny", sampler=False)
+    got, st, _ = _run(cfg.attn)
+    _check(cfg.attn, got, st)
+
+
+def test_eagle2_full():
+    cfg = make_config("eagle2", sampler=False)
+    got, st, _ = _run(cfg.attn)
+    _check(cfg.attn, got, st)
+
+
+def test_batched_full():
+    cfg = make_config("batched", sampler=False)
+    got, st, _ = _run(cfg.attn)
+    _check(cfg.attn, got, st)
+
+
+def test_sequoia_sampled_rows():
+    cfg = make_config("sequoia", sampler=False)
+    got, st, _ = _run(cfg.attn)
+    rng = np.random.default_rng(0)
+    depth = oracle.depths(cfg.trees[0])
+    picks = [(0, 0), (0, 767), (0, int(np.argmax(depth)))] + \
+            [(0, int(i)) for i in rng.choice(768, 45, replace=False)]
+    _check(cfg.attn, got, st, picks=picks)
+    assert np.isfinite(got).all()
+
+
+def test_highload_sampled():
+    cfg = make_config("highload", sampler=False)
+    inp = cfg.attn
+    got, st, _ = _run(inp)
+    rng = np.random.default_rng(1)
+    picks = []
+    for r in rng.choice(inp.batch, 8, replace=False):
+        n = inp.nodes(int(r))
+        picks += [(int(r), int(i)) for i in rng.choice(n, min(n, 6), replace=False)]
+    _check(inp, got, st, picks=picks)
+    assert np.isfinite(got).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("heads", [(4, 4), (8, 2), (32, 8), (16, 1)])
+def test_random_small(dtype, D, heads):
+    """Several tiles, ragged tails, prefixes not page-aligned, G in {1,4,16}."""
+    rng = np.random.default_rng(D * 100 + heads[0] + (dtype == "bf16"))
+    Hq, Hkv = heads
+    trees = [random_tree(rng, int(rng.integers(1, 40)), depth_cap=int(rng.integers(1, 9)))
+             for _ in range(5)]
+    prefixes = [int(x) for x in rng.integers(0, 700, size=5)]
+    inp = make_attention_inputs(rng, rng, trees, prefixes, Hq, Hkv, D, dtype=dtype,
+                                spare_pages=3)
+    got, st, _ = _run(inp)
+    _check(inp, got, st)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_special_trees(dtype):
+    """Chain (= causal), single node (= decode), star, expansion vector, and a
+    request with no prefix, all in one batch."""
+    rng = np.random.default_rng(5)
+    trees = [chain_tree(40), np.array([-1]), star_tree(33), expansion_vector_tree([1, 1, 3, 1, 1]),
+             random_tree(rng, 17, depth_cap=16)]
+    prefixes = [255, 1, 64, 0, 17]
+    inp = make_attention_inputs(rng, rng, trees, prefixes, 8, 2, 128, dtype=dtype)
+    got, st, _ = _run(inp)
+    _check(inp, got, st)
+
+
+def test_max_nodes_tree():
+    """1024-row tree (the supported maximum): several row blocks and bitset words."""
+    rng = np.random.default_rng(9)
+    trees = [random_tree(rng, 1024, depth_cap=20)]
+    inp = make_attention_inputs(rng, rng, trees, [300], 8, 2, 128, dtype="bf16")
+    got, st, _ = _run(inp)
+    picks = [(0, int(i)) for i in rng.choice(1024, 40, replace=False)] + [(0, 1023)]
+    _check(inp, got, st, picks=picks)
+
+
+def test_deterministic_and_page_placement_invariant():
+    cfg = make_config("batched", sampler=False, batch=4)
+    inp = cfg.attn
+    (a, b), st, _ = _run(inp, repeat=2)
+    assert st == 0
+    np.testing.assert_array_equal(a, b)
+    moved = repage(inp, np.random.default_rng(3), spare_pages=11)
+    c, st, _ = _run(moved)
+    np.testing.assert_array_equal(a, c)
+
+
+def test_custom_scale():
+    rng = np.random.default_rng(2)
+    inp = make_attention_inputs(rng, rng, [random_tree(rng, 20, depth_cap=4)], [100], 8, 2, 64,
+                                dtype="fp32")
+    inp.sm_scale = 0.3
+    got, st, _ = _run(inp, sm_scale=0.3)
+    _check(inp, got, st)
+
+
+def test_device_errors_are_reported_not_faulted():
+    """Out-of-range page ids and bad parents set status bits (host-forced;
+    every access stays in bounds because the kernel clamps)."""
+    import tree_verification_verify_amd as tv
+    rng = np.random.default_rng(4)
+    inp = make_attention_inputs(rng, rng, [random_tree(rng, 12, depth_cap=3)], [40], 4, 1, 64,
+                                dtype="bf16")
+    bad = repage(inp, rng)
+    bad.page_indices = bad.page_indices.copy()
+    bad.page_indices[1] = bad.num_pages + 5
+    _, st, bits = _run(bad)
+    assert st == 6 and bits & 2
+    bad2 = repage(inp, rng)
+    bad2.parent = bad2.parent.copy()
+    bad2.parent[5] = 7
+    _, st, bits = _run(bad2)
+    assert st == 5 and bits & 1

@@ -1,0 +1,179 @@
+"""GPU parity: tree_spec_sample + tree_accept_path (HIP, via the C ABI)
+against the fp64 oracle. Decisions are bit-exact; a request whose oracle log
+holds a decision within EPS of its threshold (or a degenerate residual) is
+excluded from the bit-exact comparison and counted (none is expected at
+EPS = 1e-9: both sides compute in fp64)."""
+import numpy as np
+import pytest
+
+import oracle
+from oracle.sampler import near_threshold
+from workloads import make_config, make_sampler_inputs, random_tree, chain_tree, star_tree
+
+pytestmark = pytest.mark.gpu
+
+EPS = 1e-9
+
+
+def _run(inp, **kw):
+    from gpu_run import run_sampler
+    return run_sampler(inp, **kw)
+
+
+def _compare(inp, got, prefix_lens=None, allow_near=0):
+    assert got["status"] == 0, (got["status"], got["bits"])
+    flags, nts, logs = oracle.tree_spec_sample(inp)
+    md = got["max_depth"]
+    B = inp.batch
+    prefix_lens = prefix_lens if prefix_lens is not None else [0] * B
+    pn, ot, ol, kk = oracle.tree_accept_path(inp.node_indptr, inp.parent, inp.tokens, flags,
+                                             nts, prefix_lens, md)
+    near = 0
+    for r in range(B):
+        a, b = int(inp.node_indptr[r]), int(inp.node_indptr[r + 1])
+        if near_threshold(logs[r], EPS):
+            near += 1
+            continue
+        np.testing.assert_array_equal(got["flag"][a:b], flags[a:b], err_msg=f"request {r}")
+        np.testing.assert_array_equal(got["next_token"][a:b], nts[a:b], err_msg=f"request {r}")
+        assert got["out_len"][r] == ol[r], r
+        np.testing.assert_array_equal(got["path_nodes"][r], pn[r])
+        np.testing.assert_array_equal(got["out_tokens"][r], ot[r])
+        np.testing.assert_array_equal(got["kv_keep"][r], kk[r])
+    assert near <= allow_near, near
+    return near
+
+
+def test_tiny():
+    cfg = make_config("tiny", attention=False)
+    _compare(cfg.sampler, _run(cfg.sampler, max_depth=5, prefix_lens=cfg.prefix_lens),
+             cfg.prefix_lens)
+
+
+@pytest.mark.parametrize("temp", ["mixed", 0.0, 0.5, 1.0])
+def test_highload_full_vocab(temp):
+    cfg = make_config("highload", attention=False, temperature=temp)
+    _compare(cfg.sampler, _run(cfg.sampler, max_depth=8, prefix_lens=cfg.prefix_lens),
+             cfg.prefix_lens)
+
+
+def test_highload_independent_logits():
+    """The literal independent N(0,2) reading: short walks, many rejections."""
+    cfg = make_config("highload", attention=False, temperature=1.0, mode="independent", batch=16)
+    _compare(cfg.sampler, _run(cfg.sampler, max_depth=8))
+
+
+def test_sequoia_sampler():
+    cfg = make_config("sequoia", attention=False)
+    _compare(cfg.sampler, _run(cfg.sampler, max_depth=12, prefix_lens=cfg.prefix_lens),
+             cfg.prefix_lens)
+
+
+@pytest.mark.parametrize("V", [7, 64, 1000, 4099])
+@pytest.mark.parametrize("batch", [1, 5, 40])
+def test_random_small(V, batch):
+    rng = np.random.default_rng(V + batch)
+    # at most V children per node: a node cannot have more distinct siblings than tokens
+    trees = [random_tree(rng, int(rng.integers(1, min(25, V + 1) + 1)),
+                         depth_cap=int(rng.integers(1, 6)))
+             for _ in range(batch)]
+    temps = rng.choice([0.0, 0.25, 0.5, 1.0, 2.0], size=batch)
+    mode = "independent" if V < 100 else "correlated"
+    inp = make_sampler_inputs(rng, rng, rng, trees, V, temps, mode=mode)
+    _compare(inp, _run(inp, max_depth=6))
+
+
+def test_greedy_ties_take_lowest_index():
+    V = 50
+    trees = [star_tree(6), chain_tree(4)]
+    rng = np.random.default_rng(0)
+    inp = make_sampler_inputs(rng, rng, rng, trees, V, [0.0, 0.0])
+    inp.target_logits[:] = 0.0
+    inp.target_logits[:, 7] = 3.0
+    inp.target_logits[:, 31] = 3.0   # tie with 7: argmax must be 7
+    inp.tokens[:] = [0, 9, 31, 7, 2, 5, 0, 7, 7, 1]
+    got = _run(inp, max_depth=4)
+    assert (got["next_token"] == 7).all()
+    _compare(inp, got)
+
+
+def test_alignment_probe():
+    """Row i is the distribution after node i: a one-hot target row on the
+    token only one child carries makes that child accepted."""
+    V = 128
+    trees = [np.array([-1, 0, 0, 1, 2])]
+    rng = np.random.default_rng(1)
+    inp = make_sampler_inputs(rng, rng, rng, trees, V, [1.0])
+    inp.tokens[:] = [0, 5, 7, 3, 9]
+    inp.target_logits[:] = -30.0
+    inp.target_logits[0, 7] = 30.0
+    inp.target_logits[2, 9] = 30.0
+    inp.target_logits[[1, 3, 4], 11] = 30.0
+    got = _run(inp, max_depth=3)
+    assert list(got["flag"]) == [1, 0, 1, 0, 1]
+    assert got["out_len"][0] == 3
+    _compare(inp, got)
+
+
+def test_q_equals_p_accepts_first_child():
+    rng = np.random.default_rng(2)
+    trees = [random_tree(rng, 20, depth_cap=4) for _ in range(10)]
+    inp = make_sampler_inputs(rng, rng, rng, trees, 512, [1.0] * 10)
+    inp.draft_logits = inp.target_logits.copy()
+    inp.uniforms = (inp.uniforms * np.float32(0.999)).astype(np.float32)
+    got = _run(inp, max_depth=4)
+    _compare(inp, got)
+    for r, t in enumerate(trees):
+        a = int(inp.node_indptr[r])
+        for v in range(len(t)):
+            ch = [i for i in range(len(t)) if t[i] == v]
+            if ch and got["flag"][a + v] == 1:
+                assert got["flag"][a + ch[0]] == 1
+
+
+def test_two_accepted_siblings_reported():
+    """tree_accept_path flags a node with two accepted children (host-forced flags)."""
+    import torch
+    import tree_verification_verify_amd as tv
+    ni = torch.tensor([0, 3, 6], dtype=torch.int32, device="cuda")
+    par = torch.tensor([-1, 0, 0, -1, 0, 1], dtype=torch.int32, device="cuda")
+    tok = torch.tensor([0, 4, 5, 0, 6, 7], dtype=torch.int32, device="cuda")
+    flag = torch.tensor([1, 1, 1, 1, 1, 1], dtype=torch.int8, device="cuda")
+    nt = torch.tensor([-1, 11, 12, -1, -1, 13], dtype=torch.int32, device="cuda")
+    pre = torch.tensor([10, 20], dtype=torch.int32, device="cuda")
+    desc = tv.sample_desc(2, 16, 3, 2)
+    ws = tv.alloc_workspace(tv.sample_workspace_size(desc))
+    pn = torch.empty(6, dtype=torch.int32, device="cuda")
+    ot, kk = torch.empty_like(pn), torch.empty_like(pn)
+    ol = torch.empty(2, dtype=torch.int32, device="cuda")
+    tv.tree_accept_path(2, 2, ni, par, tok, flag, nt, pre, pn, ot, ol, kk, ws)
+    st, bits = tv.device_status(ws)
+    assert st == 9 and bits & 8
+    assert ol.cpu().tolist() == [-1, 3]
+    assert ot.cpu().tolist()[3:] == [6, 7, 13]
+    assert kk.cpu().tolist()[3:] == [20, 21, 22]
+
+
+def test_monte_carlo_tv_on_gpu():
+    """P10 on the GPU path: 3000 independent one-level walks (root with 3
+    children drawn without replacement); the first emitted token's TV to p is
+    within the 99th percentile of direct sampling's TV at equal n."""
+    rng = np.random.default_rng(11)
+    V, k, n = 16, 3, 3000
+    logits = (rng.standard_normal(V) * 1.2).astype(np.float32)
+    dl = (logits + rng.standard_normal(V).astype(np.float32) * 0.4).astype(np.float32)
+    trees = [star_tree(k + 1)] * n
+    inp = make_sampler_inputs(rng, rng, rng, trees, V, [1.0] * n)
+    inp.target_logits[:] = logits
+    inp.draft_logits[:] = dl
+    from workloads import gumbel_topk_tokens
+    for r in range(n):
+        inp.tokens[r * (k + 1) + 1:(r + 1) * (k + 1)] = gumbel_topk_tokens(rng, dl, k, 1.0)
+    got = _run(inp, max_depth=1)
+    first = got["out_tokens"][:, 0]
+    p = np.exp(logits.astype(np.float64) - logits.max())
+    p /= p.sum()
+    tv_walk = 0.5 * np.abs(np.bincount(first, minlength=V) / n - p).sum()
+    tvs = [0.5 * np.abs(rng.multinomial(n, p) / n - p).sum() for _ in range(300)]
+    assert tv_walk <= np.percentile(tvs, 99), (tv_walk, np.percentile(tvs, 99))
+    _compare(inp, got)

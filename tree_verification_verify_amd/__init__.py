@@ -1,0 +1,215 @@
+"""Tree verification for tree-based speculative decoding on AMD MI355X.
+
+A thin Python binding over libtreeverify (include/tree_verify.h). Every step
+of the hot path runs in the library's HIP kernels; this module only checks
+and marshals arguments (torch tensors are used for device memory and the
+current stream) and raises TVError on a non-OK status. There is no CPU
+fallback: if the library is missing, calls raise.
+
+Entry points (same names as the C ABI):
+  tree_verify_attn   tree-masked paged attention, one layer
+  tree_spec_sample   greedy / without-replacement rejection walk
+  tree_accept_path   longest accepted path, emitted tokens, KV keep-list
+  tv_tree_meta       depth, ancestor bitsets, children lists
+"""
+import ctypes
+
+import numpy as np
+
+from . import _lib
+from ._lib import AttnDesc, SampleDesc, TV_BF16, TV_FP32, STATUS_NAMES, DEV_BITS
+
+__all__ = [
+    "TVError", "AttnDesc", "SampleDesc", "TV_BF16", "TV_FP32", "attn_desc",
+    "sample_desc", "attn_workspace_size", "sample_workspace_size", "alloc_workspace",
+    "workspace_init", "device_status", "tree_verify_attn", "tree_spec_sample",
+    "tree_accept_path", "tv_tree_meta", "validate_tree", "validate_pages", "library",
+]
+
+
+class TVError(RuntimeError):
+    def __init__(self, status, where=""):
+        lib = _lib.load()
+        msg = lib.tv_status_string(status).decode()
+        if status == 7:
+            msg += " (" + lib.tv_last_hip_error().decode() + ")"
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+def library():
+    return _lib.load()
+
+
+def _check(status, where):
+    if status != 0:
+        raise TVError(status, where)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dtype=None, device=True):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if device and t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def attn_desc(batch, num_q_heads, num_kv_heads, head_dim, max_nodes, max_depth,
+              max_kv_len, num_pages, dtype="bf16", sm_scale=0.0):
+    return AttnDesc(batch, num_q_heads, num_kv_heads, head_dim, 16, max_nodes, max_depth,
+                    max_kv_len, num_pages, TV_BF16 if dtype == "bf16" else TV_FP32,
+                    float(sm_scale))
+
+
+def sample_desc(batch, vocab, max_nodes, max_depth):
+    return SampleDesc(batch, vocab, max_nodes, max_depth)
+
+
+def attn_workspace_size(desc):
+    n = _lib.load().tv_attn_workspace_size(ctypes.byref(desc))
+    if n == 0:
+        raise TVError(2, "tv_attn_workspace_size")
+    return n
+
+
+def sample_workspace_size(desc):
+    n = _lib.load().tv_sample_workspace_size(ctypes.byref(desc))
+    if n == 0:
+        raise TVError(2, "tv_sample_workspace_size")
+    return n
+
+
+def alloc_workspace(nbytes, device="cuda"):
+    """A 256-byte aligned uint8 device buffer of nbytes, zero-initialised by
+    the library's fill kernel."""
+    import torch
+    raw = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    off = (-raw.data_ptr()) % 256
+    ws = raw[off:off + nbytes]
+    workspace_init(ws)
+    return ws
+
+
+def workspace_init(ws, stream=None):
+    _need(ws, "workspace", None)
+    _check(_lib.load().tv_workspace_init(_ptr(ws), ws.numel() * ws.element_size(),
+                                         _stream(stream)), "tv_workspace_init")
+
+
+def device_status(ws, stream=None):
+    """(status, bits) of the workspace's device status word; synchronises."""
+    bits = ctypes.c_uint32(0)
+    st = _lib.load().tv_device_status(_ptr(ws), _stream(stream), ctypes.byref(bits))
+    return st, bits.value
+
+
+def tree_verify_attn(desc, q, k_pages, v_pages, page_indptr, page_indices, prefix_len,
+                     node_indptr, parent, out, workspace, stream=None):
+    import torch
+    dt = torch.bfloat16 if desc.dtype == TV_BF16 else torch.float32
+    for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"), (out, "out")):
+        _need(t, n, dt)
+    for t, n in ((page_indptr, "page_indptr"), (page_indices, "page_indices"),
+                 (prefix_len, "prefix_len"), (node_indptr, "node_indptr"), (parent, "parent")):
+        _need(t, n, torch.int32)
+    _need(workspace, "workspace", torch.uint8)
+    if q.shape != out.shape:
+        raise ValueError("q and out shapes differ")
+    if tuple(k_pages.shape[1:]) != (desc.num_kv_heads, 16, desc.head_dim) or \
+            k_pages.shape != v_pages.shape or k_pages.shape[0] != desc.num_pages:
+        raise ValueError("k_pages / v_pages must be [num_pages][Hkv][16][D]")
+    if q.dim() != 3 or q.shape[1] != desc.num_q_heads or q.shape[2] != desc.head_dim:
+        raise ValueError("q must be [T][Hq][D]")
+    _check(_lib.load().tree_verify_attn(
+        ctypes.byref(desc), _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(page_indptr),
+        _ptr(page_indices), _ptr(prefix_len), _ptr(node_indptr), _ptr(parent), _ptr(out),
+        _ptr(workspace), workspace.numel(), _stream(stream)), "tree_verify_attn")
+
+
+def tree_spec_sample(desc, target_logits, draft_logits, tokens, node_indptr, parent,
+                     temperature, uniforms, accept_flag, next_token, workspace, stream=None):
+    import torch
+    _need(target_logits, "target_logits", torch.float32)
+    if draft_logits is not None:
+        _need(draft_logits, "draft_logits", torch.float32)
+    for t, n in ((tokens, "tokens"), (node_indptr, "node_indptr"), (parent, "parent"),
+                 (next_token, "next_token")):
+        _need(t, n, torch.int32)
+    _need(temperature, "temperature", torch.float32)
+    _need(uniforms, "uniforms", torch.float32)
+    _need(accept_flag, "accept_flag", torch.int8)
+    _need(workspace, "workspace", torch.uint8)
+    if target_logits.dim() != 2 or target_logits.shape[1] != desc.vocab:
+        raise ValueError("target_logits must be [T][V]")
+    _check(_lib.load().tree_spec_sample(
+        ctypes.byref(desc), _ptr(target_logits), _ptr(draft_logits), _ptr(tokens),
+        _ptr(node_indptr), _ptr(parent), _ptr(temperature), _ptr(uniforms), _ptr(accept_flag),
+        _ptr(next_token), _ptr(workspace), workspace.numel(), _stream(stream)),
+        "tree_spec_sample")
+
+
+def tree_accept_path(batch, max_depth, node_indptr, parent, tokens, accept_flag, next_token,
+                     prefix_len, path_nodes, out_tokens, out_len, kv_keep,
+                     status_workspace=None, stream=None):
+    import torch
+    for t, n in ((node_indptr, "node_indptr"), (parent, "parent"), (tokens, "tokens"),
+                 (next_token, "next_token"), (prefix_len, "prefix_len"),
+                 (path_nodes, "path_nodes"), (out_tokens, "out_tokens"), (out_len, "out_len"),
+                 (kv_keep, "kv_keep")):
+        _need(t, n, torch.int32)
+    _need(accept_flag, "accept_flag", torch.int8)
+    for t in (path_nodes, out_tokens, kv_keep):
+        if t.numel() < batch * (max_depth + 1):
+            raise ValueError("path outputs must hold [B][max_depth+1]")
+    _check(_lib.load().tree_accept_path(
+        batch, max_depth, _ptr(node_indptr), _ptr(parent), _ptr(tokens), _ptr(accept_flag),
+        _ptr(next_token), _ptr(prefix_len), _ptr(path_nodes), _ptr(out_tokens), _ptr(out_len),
+        _ptr(kv_keep), _ptr(status_workspace), _stream(stream)), "tree_accept_path")
+
+
+def tv_tree_meta(batch, max_nodes, node_indptr, parent, depth=None, anc_bits=None,
+                 first_child=None, next_sibling=None, status_workspace=None, stream=None):
+    import torch
+    _need(node_indptr, "node_indptr", torch.int32)
+    _need(parent, "parent", torch.int32)
+    _check(_lib.load().tv_tree_meta(
+        batch, max_nodes, _ptr(node_indptr), _ptr(parent), _ptr(depth), _ptr(anc_bits),
+        _ptr(first_child), _ptr(next_sibling), _ptr(status_workspace), _stream(stream)),
+        "tv_tree_meta")
+
+
+def _host_i32(a):
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def validate_tree(node_indptr, parent, max_nodes, max_depth):
+    """Host-side check of the tree rules; returns the status code."""
+    ni, pni = _host_i32(node_indptr)
+    pa, ppa = _host_i32(parent)
+    return _lib.load().tv_validate_tree(len(ni) - 1, pni, ppa, max_nodes, max_depth)
+
+
+def validate_pages(page_indptr, page_indices, prefix_len, node_indptr, num_pages):
+    a, pa = _host_i32(page_indptr)
+    b, pb = _host_i32(page_indices if len(page_indices) else np.zeros(1, np.int32))
+    c, pc = _host_i32(prefix_len)
+    d, pd = _host_i32(node_indptr)
+    return _lib.load().tv_validate_pages(len(a) - 1, pa, pb, pc, pd, num_pages, 16)

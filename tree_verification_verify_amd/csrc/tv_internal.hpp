@@ -1,0 +1,82 @@
+// Host-side plans and launcher declarations shared by api.cpp and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "tree_verify.h"
+
+namespace tv {
+
+// Launch geometry of tree_verify_attn, derived from the descriptor only, so
+// the workspace size is known without touching the GPU.
+struct AttnPlan {
+  bool mfma;          // bf16 MFMA kernel (true) or fp32 VALU kernel
+  int group;          // G = Hq / Hkv
+  int rows_pb;        // rows (node x grouped head) per workgroup
+  int rb_max;         // row blocks per (request, kv head)
+  int chunk_len;      // keys per split (multiple of 32)
+  int c_max;          // splits per (request, kv head) at max_kv_len
+  int words;          // 32-bit words per ancestor bitset row
+  size_t slots;       // B * Hkv * rb_max * c_max
+  size_t grid;        // slots rounded up to a multiple of 8 (XCD remap)
+  size_t off_counters, off_ml, off_o, total_bytes;
+};
+
+struct SamplePlan {
+  int threads;        // threads per workgroup
+  int part_stride;    // doubles per (team, member, parity) partial slot
+  size_t off_team_ctr, off_part, total_bytes;
+};
+
+bool plan_attn(const tv_attn_desc& d, AttnPlan* out);
+bool plan_sample(const tv_sample_desc& d, SamplePlan* out);
+
+struct AttnArgs {
+  const void* q;
+  const void* k_pages;
+  const void* v_pages;
+  const int32_t* page_indptr;
+  const int32_t* page_indices;
+  const int32_t* prefix_len;
+  const int32_t* node_indptr;
+  const int32_t* parent;
+  void* out;
+  void* workspace;
+};
+
+hipError_t launch_attn(const tv_attn_desc& d, const AttnPlan& plan, const AttnArgs& a,
+                       hipStream_t stream);
+
+struct SampleArgs {
+  const float* target;
+  const float* draft;
+  const int32_t* tokens;
+  const int32_t* node_indptr;
+  const int32_t* parent;
+  const float* temperature;
+  const float* uniforms;
+  int8_t* flag;
+  int32_t* next_token;
+  void* workspace;
+};
+
+hipError_t launch_sample(const tv_sample_desc& d, const SamplePlan& plan, const SampleArgs& a,
+                         hipStream_t stream);
+
+hipError_t launch_accept_path(int32_t batch, int32_t max_depth, const int32_t* node_indptr,
+                              const int32_t* parent, const int32_t* tokens,
+                              const int8_t* flag, const int32_t* next_token,
+                              const int32_t* prefix_len, int32_t* path_nodes,
+                              int32_t* out_tokens, int32_t* out_len, int32_t* kv_keep,
+                              uint32_t* status, hipStream_t stream);
+
+hipError_t launch_tree_meta(int32_t batch, int32_t max_nodes, const int32_t* node_indptr,
+                            const int32_t* parent, int32_t* depth, uint32_t* anc_bits,
+                            int32_t* first_child, int32_t* next_sibling, uint32_t* status,
+                            hipStream_t stream);
+
+hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream);
+
+}  // namespace tv
