@@ -49,7 +49,8 @@ def attn_algorithmic_flops(cfg):
     f = 0
     for r, parent in enumerate(cfg.trees):
         d = oracle.depths(parent)
-        f += int(sum(4 * inp.num_q_heads * inp.head_dim * (inp.prefix_len[r] + di + 1) for di in d))
+        P = int(inp.prefix_len[r])
+        f += sum(4 * inp.num_q_heads * inp.head_dim * (P + int(di) + 1) for di in d)
     return f
 
 
@@ -249,7 +250,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic,
-                     "kernel": "attn_mfma_kernel<128> (tree_verify_attn)",
+                     "kernel": "attn_stream_kernel<128> (tree_verify_attn)",
                      "algorithmic_bytes": abytes, "algorithmic_flops": aflops,
                      "kernel_ms": attn_ms,
                      "tflops": aflops / (attn_ms * 1e-3) / 1e12},

@@ -125,11 +125,18 @@ tv_status tv_device_status(const void* workspace, hipStream_t stream, uint32_t* 
  *   g = h / (Hq / Hkv).
  * Arguments:
  *   q        [T][Hq][D] in desc->dtype, T = node_indptr[B]
- *   k_pages, v_pages [num_pages][Hkv][16][D] in desc->dtype; logical position
- *            t of request r lives in physical page
- *            page_indices[page_indptr[r] + t/16], slot t%16. The caller has
- *            already written the tree's own K/V at P_r .. P_r+N_r-1 (with
- *            RoPE at per-depth positions applied before the call).
+ *   k_pages  [num_pages][Hkv][16][D] in desc->dtype (one 16-token page per
+ *            page and kv head, a key's D channels contiguous)
+ *   v_pages  [num_pages][Hkv][D][16] in desc->dtype: V transposed within
+ *            each page (one channel's 16 tokens contiguous), so a V tile
+ *            is already in the layout the PV matrix product consumes.
+ *            Logical position t of request r lives in physical page
+ *            pg = page_indices[page_indptr[r] + t/16], slot s = t%16:
+ *            K[t] = k_pages[pg][g][s][:], V[t] = v_pages[pg][g][:][s].
+ *            The caller has already written the tree's own K/V at
+ *            P_r .. P_r+N_r-1 (with RoPE at per-depth positions applied
+ *            before the call). Slots past P_r+N_r in the last page are
+ *            never used (their contents do not matter).
  *   page_indptr [B+1], page_indices [page_indptr[B]]  (int32)
  *   prefix_len [B]   P_r >= 0 (int32)
  *   node_indptr [B+1], parent [T]  (int32; see the tree conventions above)

@@ -8,8 +8,10 @@ for request r, query head h, tree row i,
   o[i,h]     = sum_{t in visible(i)} softmax_t(scale * <q[i,h], K[t, h//G]>) V[t, h//G]
 
 with K/V of logical position t read from physical page
-page_indices[page_indptr[r] + t // 16], slot t % 16, and scale = 1/sqrt(D)
-unless given. The tree's own K/V sit at logical positions P_r .. P_r+N_r-1.
+pg = page_indices[page_indptr[r] + t // 16], slot s = t % 16, as
+K[t, g, :] = k_pages[pg, g, s, :] and V[t, g, :] = v_pages[pg, g, :, s]
+(V is stored transposed within each page), and scale = 1/sqrt(D) unless
+given. The tree's own K/V sit at logical positions P_r .. P_r+N_r-1.
 Inputs are widened exactly (bf16 bit patterns or fp32) to fp64.
 """
 import numpy as np
@@ -94,8 +96,8 @@ def tree_attention_rows(inp, picks):
         Ksub = decode_values(inp.k_pages[pages], inp.dtype)
         Vsub = decode_values(inp.v_pages[pages], inp.dtype)
         Hkv, D = inp.num_kv_heads, inp.head_dim
-        K = Ksub.transpose(0, 2, 1, 3).reshape(-1, Hkv, D)[:L]
-        V = Vsub.transpose(0, 2, 1, 3).reshape(-1, Hkv, D)[:L]
+        K = Ksub.transpose(0, 2, 1, 3).reshape(-1, Hkv, D)[:L]   # [page][slot][g][d]
+        V = Vsub.transpose(0, 3, 1, 2).reshape(-1, Hkv, D)[:L]   # [page][slot][g][d]
         rows = _request_rows(inp, r, [i for _, i in lst], K, V, Q)
         for (n, _), row in zip(lst, rows):
             out[n] = row

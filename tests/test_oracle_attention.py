@@ -20,10 +20,15 @@ def _sdpa_rows(q_rows, K, V, scale):
 
 
 def _logical(inp, r, which):
-    pool = oracle.decode_values(inp.k_pages if which == "k" else inp.v_pages, inp.dtype)
+    """[L][Hkv][D] logical K or V of request r, read slot by slot (K pages
+    are [page][g][slot][d], V pages [page][g][d][slot])."""
     L = inp.kv_len(r)
     base = int(inp.page_indptr[r])
-    return np.stack([pool[inp.page_indices[base + t // 16], :, t % 16, :] for t in range(L)])
+    if which == "k":
+        pool = oracle.decode_values(inp.k_pages, inp.dtype)
+        return np.stack([pool[inp.page_indices[base + t // 16], :, t % 16, :] for t in range(L)])
+    pool = oracle.decode_values(inp.v_pages, inp.dtype)
+    return np.stack([pool[inp.page_indices[base + t // 16], :, :, t % 16] for t in range(L)])
 
 
 def _make(trees, prefixes, Hq=4, Hkv=2, D=32, dtype="fp32", seed=0):
@@ -126,7 +131,7 @@ def test_relabel_permutes_rows_and_repaging_changes_nothing():
         vp = np.zeros_like(rel.v_pages)
         for t in range(L):
             kp[rel.page_indices[t // 16], :, t % 16] = Kn[t]
-            vp[rel.page_indices[t // 16], :, t % 16] = Vn[t]
+            vp[rel.page_indices[t // 16], :, :, t % 16] = Vn[t]
         rel.k_pages, rel.v_pages = kp, vp
         rel.q = np.empty_like(inp.q)
         rel.q[new_of_old] = inp.q

@@ -132,9 +132,10 @@ def tree_verify_attn(desc, q, k_pages, v_pages, page_indptr, page_indices, prefi
     _need(workspace, "workspace", torch.uint8)
     if q.shape != out.shape:
         raise ValueError("q and out shapes differ")
-    if tuple(k_pages.shape[1:]) != (desc.num_kv_heads, 16, desc.head_dim) or \
-            k_pages.shape != v_pages.shape or k_pages.shape[0] != desc.num_pages:
-        raise ValueError("k_pages / v_pages must be [num_pages][Hkv][16][D]")
+    if tuple(k_pages.shape) != (desc.num_pages, desc.num_kv_heads, 16, desc.head_dim):
+        raise ValueError("k_pages must be [num_pages][Hkv][16][D]")
+    if tuple(v_pages.shape) != (desc.num_pages, desc.num_kv_heads, desc.head_dim, 16):
+        raise ValueError("v_pages must be [num_pages][Hkv][D][16] (V transposed within a page)")
     if q.dim() != 3 or q.shape[1] != desc.num_q_heads or q.shape[2] != desc.head_dim:
         raise ValueError("q must be [T][Hq][D]")
     _check(_lib.load().tree_verify_attn(

@@ -14,13 +14,19 @@ namespace tv {
 struct AttnPlan {
   bool mfma;          // bf16 MFMA kernel (true) or fp32 VALU kernel
   int group;          // G = Hq / Hkv
-  int rows_pb;        // rows (node x grouped head) per workgroup
+  int rows_pb;        // rows (node x grouped head) per row block
   int rb_max;         // row blocks per (request, kv head)
+  int words;          // 32-bit words per ancestor bitset row
+  // fp32 VALU kernel: one workgroup per (request, kv head, row block, split)
   int chunk_len;      // keys per split (multiple of 32)
   int c_max;          // splits per (request, kv head) at max_kv_len
-  int words;          // 32-bit words per ancestor bitset row
-  size_t slots;       // B * Hkv * rb_max * c_max
-  size_t grid;        // slots rounded up to a multiple of 8 (XCD remap)
+  // bf16 MFMA kernel: persistent workgroups, each streaming an equal share of
+  // the 64-key tiles of all (request, kv head, row block) pairs
+  int nwg;            // workgroups (a power of two >= 8)
+  int lg_nwg;         // log2(nwg)
+  size_t slots;       // partial-result slots
+  size_t grid;        // launch size (multiple of 8: XCD-aware remap)
+  size_t dyn_lds;     // dynamic LDS bytes per workgroup
   size_t off_counters, off_ml, off_o, total_bytes;
 };
 

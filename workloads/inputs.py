@@ -3,7 +3,8 @@
 Layouts (the boundary's layouts; see include/tree_verify.h):
   q        [T][Hq][D]                 T = node_indptr[B]
   k_pages  [num_pages][Hkv][16][D]    one 16-token page per (page, kv head)
-  v_pages  [num_pages][Hkv][16][D]
+  v_pages  [num_pages][Hkv][D][16]    V transposed within each page: the 16
+                                      values of one channel are contiguous
   page_indptr [B+1], page_indices [page_indptr[B]]   logical -> physical page
   prefix_len [B]; node i of request r sits at logical position P_r + i
   node_indptr [B+1]; parent [T] request-local, parent[0] = -1
@@ -134,15 +135,13 @@ def make_attention_inputs(rng_qkv, rng_pages, trees, prefix_lens, num_q_heads,
     T = int(node_indptr[-1])
     if dtype == "bf16":
         gen = _normal_bf16
-        q = gen(rng_qkv, (T, num_q_heads, head_dim))
-        k = gen(rng_qkv, (num_pages, num_kv_heads, PAGE, head_dim))
-        v = gen(rng_qkv, (num_pages, num_kv_heads, PAGE, head_dim))
     elif dtype == "fp32":
-        q = _normal_f32(rng_qkv, (T, num_q_heads, head_dim))
-        k = _normal_f32(rng_qkv, (num_pages, num_kv_heads, PAGE, head_dim))
-        v = _normal_f32(rng_qkv, (num_pages, num_kv_heads, PAGE, head_dim))
+        gen = _normal_f32
     else:
         raise ValueError(dtype)
+    q = gen(rng_qkv, (T, num_q_heads, head_dim))
+    k = gen(rng_qkv, (num_pages, num_kv_heads, PAGE, head_dim))
+    v = gen(rng_qkv, (num_pages, num_kv_heads, head_dim, PAGE))
     return AttentionInputs(
         dtype=dtype, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
         head_dim=head_dim, q=q, k_pages=k, v_pages=v, page_indptr=page_indptr,
@@ -159,7 +158,7 @@ def repage(inp, rng, spare_pages=0):
     num_pages = n_used + int(spare_pages)
     perm = rng.permutation(num_pages).astype(np.int32)
     k = np.zeros((num_pages,) + inp.k_pages.shape[1:], dtype=inp.k_pages.dtype)
-    v = np.zeros_like(k)
+    v = np.zeros((num_pages,) + inp.v_pages.shape[1:], dtype=inp.v_pages.dtype)
     new_idx = perm[:n_used]
     k[new_idx] = inp.k_pages[inp.page_indices]
     v[new_idx] = inp.v_pages[inp.page_indices]
