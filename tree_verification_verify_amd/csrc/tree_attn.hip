@@ -13,10 +13,11 @@
 //    A fixed grid of persistent workgroups splits that list into equal
 //    contiguous shares (stream-K), so uneven prefixes balance exactly. A
 //    pair wholly inside one share is finished in registers and written out;
-//    a pair cut by share boundaries leaves fp32 partials (m, l, acc) and the
-//    last workgroup to finish it merges them in share order (deterministic).
-//    Shares are laid out XCD by XCD, so the row blocks of one kv head run on
-//    one XCD and share its L2.
+//    a pair cut by share boundaries leaves fp32 partials (offset, l, acc),
+//    which a second, small kernel merges in share order (deterministic; the
+//    kernel boundary makes the partials visible, so the streaming kernel
+//    needs no fences, counters or waiting). Shares are laid out XCD by XCD,
+//    so the row blocks of one kv head run on one XCD and share its L2.
 //  * 4 waves x 32 rows. S^T = K Q^T and O^T += V^T P^T on
 //    v_mfma_f32_16x16x32_bf16; both keep a row on lane%16, so the online
 //    softmax rescale is lane-local and P never leaves registers (the PV key
@@ -153,55 +154,144 @@ __device__ inline size_t cut_slot(int T, int w, int lg, int ps) {
   return ps < share_begin(T, w, lg) ? size_t(2 * w) : size_t(2 * w + 1);
 }
 
+// Block-wide tile offsets of every request: off[r] = first tile of request
+// r in the flat (request, kv head, row block, tile) order, off[B] = T.
+// Rejected requests (reported once when `report`) contribute no tiles.
+__device__ inline int scan_tiles(const AttnParams& p, int* off, int* s_scan, bool report) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = ceil_div(p.B, 256);
+  const int r0 = min(p.B, tid * per), r1 = min(p.B, r0 + per);
+  int mine = 0;
+  for (int r = r0; r < r1; ++r) {
+    const int t = request_tiles(p, r, report);
+    off[r] = t;
+    mine += t;
+  }
+  int inc = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += t;
+  }
+  if (lane == 63) s_scan[wave] = inc;
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    base += (w < wave) ? s_scan[w] : 0;
+    total += s_scan[w];
+  }
+  int run = base + inc - mine;
+  for (int r = r0; r < r1; ++r) {
+    const int t = off[r];
+    off[r] = run;
+    run += t;
+  }
+  if (tid == 0) off[p.B] = total;
+  __syncthreads();
+  return off[p.B];
+}
+
+// Last r with off[r] <= x (x < off[B]).
+__device__ inline int request_of(const int* off, int B, int x) {
+  int lo = 0, hi = B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (off[mid] <= x) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// Merge kernel: workgroup w merges the cut pair whose first inner share
+// boundary is a_w (a_{w-1} <= ps < a_w < pe), combining the partials of
+// every share that holds part of it, in share order (deterministic).
 template <int D>
-__device__ inline void merge_pair(const AttnParams& p, int T, int ps, int pe, int nbeg, int g,
-                                  int row0, int rows_here, float* s_M, float* s_invL) {
-  const int w0 = share_of(T, ps, p.lg_nwg);
-  const int w1 = share_of(T, pe - 1, p.lg_nwg);
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
+  constexpr int D4 = D / 4;
+  constexpr int IPT = kRowsPB * D4 / 256;  // float4 items per thread
+  __shared__ float s_M[kRowsPB];
+  __shared__ float s_invL[kRowsPB];
+  __shared__ int s_scan[4];
+  extern __shared__ int off[];  // [B + 1]
+  const int w = blockIdx.x;
+  if (w == 0) return;
+  const int T = scan_tiles(p, off, s_scan, false);
+  const int aw = share_begin(T, w, p.lg_nwg);
+  if (aw >= T) return;
+  const int r = request_of(off, p.B, aw);
+  const int nbeg = p.node_indptr[r];
+  const int N = p.node_indptr[r + 1] - nbeg;
+  const int L = p.prefix_len[r] + N;
+  const int R = N * p.G;
+  const int nrb = ceil_div(R, kRowsPB);
+  const int nt = ceil_div(L, kStage);
+  const int pir = (aw - off[r]) / nt;
+  const int ps = off[r] + pir * nt, pe = ps + nt;
+  if (!(ps < aw && share_begin(T, w - 1, p.lg_nwg) <= ps)) return;
+  const int g = pir / nrb;
+  const int row0 = (pir - g * nrb) * kRowsPB;
+  const int rows_here = min(kRowsPB, R - row0);
+  const int w0 = share_of(T, ps, p.lg_nwg), w1 = share_of(T, pe - 1, p.lg_nwg);
+
   for (int row = threadIdx.x; row < rows_here; row += blockDim.x) {
     float M = -INFINITY;
-    for (int w = w0; w <= w1; ++w) {
-      if (share_begin(T, w + 1, p.lg_nwg) == share_begin(T, w, p.lg_nwg)) continue;
-      const float* ml = p.part_ml + (cut_slot(T, w, p.lg_nwg, ps) * kRowsPB + row) * 2;
-      M = fmaxf(M, ml[0]);
+    for (int v = w0; v <= w1; ++v) {
+      if (share_begin(T, v + 1, p.lg_nwg) == share_begin(T, v, p.lg_nwg)) continue;
+      M = fmaxf(M, p.part_ml[(cut_slot(T, v, p.lg_nwg, ps) * kRowsPB + row) * 2]);
     }
-    float L = 0.f;
+    float Ls = 0.f;
     if (M != -INFINITY) {
-      for (int w = w0; w <= w1; ++w) {
-        if (share_begin(T, w + 1, p.lg_nwg) == share_begin(T, w, p.lg_nwg)) continue;
-        const float* ml = p.part_ml + (cut_slot(T, w, p.lg_nwg, ps) * kRowsPB + row) * 2;
-        L += ml[1] * exp2f(ml[0] - M);
+      for (int v = w0; v <= w1; ++v) {
+        if (share_begin(T, v + 1, p.lg_nwg) == share_begin(T, v, p.lg_nwg)) continue;
+        const float* ml = p.part_ml + (cut_slot(T, v, p.lg_nwg, ps) * kRowsPB + row) * 2;
+        Ls += ml[1] * exp2f(ml[0] - M);
       }
     }
     s_M[row] = M;
-    s_invL[row] = L > 0.f ? 1.f / L : 0.f;
+    s_invL[row] = Ls > 0.f ? 1.f / Ls : 0.f;
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < rows_here * (D / 4); idx += blockDim.x) {
-    const int row = idx / (D / 4);
-    const int d4 = (idx - row * (D / 4)) * 4;
-    const float M = s_M[row];
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (M != -INFINITY) {
-      for (int w = w0; w <= w1; ++w) {
-        if (share_begin(T, w + 1, p.lg_nwg) == share_begin(T, w, p.lg_nwg)) continue;
-        const size_t base = cut_slot(T, w, p.lg_nwg, ps) * kRowsPB + row;
-        const float s = exp2f(p.part_ml[base * 2] - M);
-        const float4 a = *reinterpret_cast<const float4*>(p.part_o + base * D + d4);
-        o.x += s * a.x;
-        o.y += s * a.y;
-        o.z += s * a.z;
-        o.w += s * a.w;
-      }
+  float4 acc[IPT];
+#pragma unroll
+  for (int k = 0; k < IPT; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int v = w0; v <= w1; ++v) {
+    if (share_begin(T, v + 1, p.lg_nwg) == share_begin(T, v, p.lg_nwg)) continue;
+    const size_t slot = cut_slot(T, v, p.lg_nwg, ps);
+    float4 o[IPT];
+    float m[IPT];
+#pragma unroll
+    for (int k = 0; k < IPT; ++k) {  // all loads of this share first
+      const int idx = threadIdx.x + 256 * k;
+      const int row = idx / D4;
+      const size_t base = slot * kRowsPB + row;
+      o[k] = row < rows_here ? *reinterpret_cast<const float4*>(p.part_o + base * D + (idx - row * D4) * 4)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+      m[k] = row < rows_here ? p.part_ml[base * 2] : -INFINITY;
     }
+#pragma unroll
+    for (int k = 0; k < IPT; ++k) {
+      const int row = (threadIdx.x + 256 * k) / D4;
+      const float Mr = row < rows_here ? s_M[row] : -INFINITY;
+      const float sc = (m[k] == -INFINITY) ? 0.f : exp2f(m[k] - Mr);
+      acc[k].x += sc * o[k].x;
+      acc[k].y += sc * o[k].y;
+      acc[k].z += sc * o[k].z;
+      acc[k].w += sc * o[k].w;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < IPT; ++k) {
+    const int idx = threadIdx.x + 256 * k;
+    const int row = idx / D4;
+    if (row >= rows_here) continue;
     const float inv = s_invL[row];
     uint2 pk;
-    pk.x = pack_bf16x2(o.x * inv, o.y * inv);
-    pk.y = pack_bf16x2(o.z * inv, o.w * inv);
+    pk.x = pack_bf16x2(acc[k].x * inv, acc[k].y * inv);
+    pk.y = pack_bf16x2(acc[k].z * inv, acc[k].w * inv);
     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + qo_offset(p, nbeg, g, row0 + row, D) +
-                              d4) = pk;
+                              (idx - row * D4) * 4) = pk;
   }
-  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
@@ -218,10 +308,7 @@ __global__ __launch_bounds__(256, 2) void attn_stream_kernel(AttnParams p) {
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kStage * KS];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][D * VS];
-  __shared__ float s_M[kRowsPB];
-  __shared__ float s_invL[kRowsPB];
   __shared__ int s_scan[4];
-  __shared__ int s_flag;
   extern __shared__ int dyn_lds[];
   int* off = dyn_lds;                                                 // [B + 1]
   int* par = dyn_lds + p.B + 1;                                       // [max_nodes]
@@ -234,55 +321,12 @@ __global__ __launch_bounds__(256, 2) void attn_stream_kernel(AttnParams p) {
   const int lg = lane >> 4;
   const int lw = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
 
-  // Tile offsets of every request (block-wide exclusive scan).
-  {
-    const int per = ceil_div(p.B, 256);
-    const int r0 = min(p.B, tid * per), r1 = min(p.B, r0 + per);
-    int mine = 0;
-    for (int r = r0; r < r1; ++r) {
-      const int t = request_tiles(p, r, lw == 0);
-      off[r] = t;
-      mine += t;
-    }
-    int inc = mine;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int t = __shfl_up(inc, o, kWave);
-      if (lane >= o) inc += t;
-    }
-    if (lane == 63) s_scan[wave] = inc;
-    __syncthreads();
-    int base = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      base += (w < wave) ? s_scan[w] : 0;
-      total += s_scan[w];
-    }
-    int run = base + inc - mine;
-    for (int r = r0; r < r1; ++r) {
-      const int t = off[r];
-      off[r] = run;
-      run += t;
-    }
-    if (tid == 0) off[p.B] = total;
-    __syncthreads();
-  }
-  const int T = off[p.B];
+  const int T = scan_tiles(p, off, s_scan, lw == 0);
   const int a = share_begin(T, lw, p.lg_nwg);
   const int b = share_begin(T, lw + 1, p.lg_nwg);
   if (a >= b) return;
 
-  // Request holding tile a: last r with off[r] <= a.
-  int r;
-  {
-    int lo = 0, hi = p.B;  // off[lo] <= a < off[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (off[mid] <= a) lo = mid;
-      else hi = mid;
-    }
-    r = lo;
-  }
+  int r = request_of(off, p.B, a);  // request holding tile a
 
   const uint16_t* qb = static_cast<const uint16_t*>(p.q);
   const uint16_t* kp = static_cast<const uint16_t*>(p.k_pages);
@@ -634,25 +678,6 @@ __global__ __launch_bounds__(256, 2) void attn_stream_kernel(AttnParams p) {
         }
       }
     }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      int nseg = 0;
-      const int w0 = share_of(T, ps, p.lg_nwg);
-      const int w1 = share_of(T, pe - 1, p.lg_nwg);
-      for (int w = w0; w <= w1; ++w)
-        nseg += share_begin(T, w + 1, p.lg_nwg) > share_begin(T, w, p.lg_nwg) ? 1 : 0;
-      uint32_t* ctr = p.counters + (size_t(r) * p.Hkv + g) * p.rb_max + rb;
-      const uint32_t old = atomicAdd(ctr, 1u);
-      const bool last = old == uint32_t(nseg - 1);
-      if (last) *ctr = 0u;  // every part has arrived: nobody touches it again
-      s_flag = last ? 1 : 0;
-    }
-    __syncthreads();
-    if (s_flag) {
-      __threadfence();
-      merge_pair<D>(p, T, ps, pe, nbeg, g, row0, rows_here, s_M, s_invL);
-    }
   }
 }
 
@@ -982,10 +1007,16 @@ hipError_t launch_attn(const tv_attn_desc& d, const AttnPlan& pl, const AttnArgs
   const dim3 grid(unsigned(pl.grid)), block(256);
   const size_t lds = pl.dyn_lds;
   if (pl.mfma) {
-    if (d.head_dim == 128)
+    // Streaming pass (whole pairs written, cut pairs left as partials), then
+    // the merge of the cut pairs; the kernel boundary orders the two.
+    const size_t merge_lds = size_t(d.batch + 1) * sizeof(int);
+    if (d.head_dim == 128) {
       hipLaunchKernelGGL(attn_stream_kernel<128>, grid, block, lds, stream, p);
-    else
+      hipLaunchKernelGGL(attn_merge_kernel<128>, grid, block, merge_lds, stream, p);
+    } else {
       hipLaunchKernelGGL(attn_stream_kernel<64>, grid, block, lds, stream, p);
+      hipLaunchKernelGGL(attn_merge_kernel<64>, grid, block, merge_lds, stream, p);
+    }
   } else {
     if (d.head_dim == 128)
       hipLaunchKernelGGL(attn_valu_kernel<128>, grid, block, lds, stream, p);
