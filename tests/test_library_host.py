@@ -94,7 +94,7 @@ def test_sampler_host_errors():
         assert call(d, p) == NULL, i
     assert call(d, ok_ptrs, need - 1) == WORKSPACE
     for bad in (tv.sample_desc(0, 10, 4, 2), tv.sample_desc(1, 0, 4, 2),
-                tv.sample_desc(1, 10, 5000, 2)):
+                tv.sample_desc(1, 10, 70000, 2)):
         assert lib.tv_sample_workspace_size(ctypes.byref(bad)) == 0
         assert call(bad, ok_ptrs) == SHAPE
 

@@ -8,23 +8,28 @@
 // at the stop node (TreeSpark §3.2 step 3).
 //
 // Design (gfx950):
-//  * One team of W workgroups per request; the team splits the vocabulary,
-//    so every vocab-wide reduction is W-way parallel. Teams synchronise with a
-//    device-scope counter (bounded spin; the launch is cooperative whenever
-//    W > 1, so every member is resident). Partials are combined by every
-//    member in the same fixed order, so all members take bit-identical
-//    decisions without a broadcast step.
-//  * No residual vector is ever stored. After rejecting siblings x_1..x_j the
+//  * One team of W workgroups per request, all on one XCD (so team traffic
+//    stays in that XCD's L2); the team splits the vocabulary into W slices,
+//    so every vocab-wide reduction is W-way parallel. Members publish
+//    partials and meet at a device-scope counter (bounded spin; the launch
+//    is cooperative when W > 1, so every member is resident). Partials are
+//    combined by every member in the same fixed order, so all members take
+//    bit-identical decisions without a broadcast.
+//  * No residual vector is stored. After rejecting siblings x_1..x_j the
 //    residual is max(p - a q, 0) / B with scalars a_{j+1} = a_j + B_j / S_j,
 //    B_{j+1} = sum_y max(p(y) - a_{j+1} q(y), 0), S_j = 1 - sum_{i<j} q(x_i)
-//    (the drawn tokens' residual is already 0, so removing them from the
-//    proposal is implicit). Each rejection therefore costs exactly one
-//    vocab-wide pass over the two logit rows and a handful of scalars.
-//  * Arithmetic is fp64 (logits widened exactly): exp, sums, ratios and the
-//    inverse-CDF prefix sums, so decisions agree with an fp64 reference except
-//    within ~1e-12 of a threshold.
-//  * T = 0 requests: argmax (lowest index on ties) of every row, then the
-//    exact-match flags for every node; no draft logits are read.
+//    (a rejected token's residual is already 0, so removing it from the
+//    proposal is implicit). Each rejection costs one vocab-wide pass over
+//    the two logit rows. The per-slice sums of that pass (or of p, at a leaf)
+//    locate the slice of the correction/bonus draw, so the draw rescans one
+//    slice only.
+//  * Arithmetic is fp64 (logits widened exactly). exp uses Tang's table
+//    method (2^(j/64) table in LDS, degree-5 polynomial, ~1 ulp), about half
+//    the instructions of the library routine. Decisions therefore agree with
+//    an fp64 reference except within ~1e-12 of a threshold.
+//  * Sweeps keep 8 independent 16-byte loads per thread in flight.
+//  * T = 0 requests: the team splits the rows; argmax (lowest index on ties)
+//    of every row, then the exact-match flags; no draft logits are read.
 #include <math.h>
 
 #include "tv_device.hpp"
@@ -34,9 +39,10 @@ namespace tv {
 
 namespace {
 
-constexpr int kThreads = 512;
+constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kMaxChildren = 4096;
+constexpr int kMaxTeam = 8;              // members per team (one XCD holds a team)
+constexpr int kUnroll = 4;               // float4 loads per row per sweep step
 constexpr uint32_t kSpinLimit = 1u << 25;
 
 struct SampleParams {
@@ -55,6 +61,30 @@ struct SampleParams {
   int B, V, W, max_nodes, part_stride;
 };
 
+// ---------------------------------------------------------------------------
+// exp(a) for a <= 0 in fp64: a = (64 k + j) ln2/64 + r, |r| <= ln2/128,
+// e^a = 2^k * 2^(j/64) * P(r) with P the degree-5 Taylor polynomial
+// (remainder below 2^-53 on that interval). tbl[j] = 2^(j/64).
+constexpr double kInvLn2x64 = 92.33248261689366;
+constexpr double kLn2by64Hi = 0.01083042469326756;  // low mantissa bits zero: n*hi exact
+constexpr double kLn2by64Lo = 2.9815858269852933e-12;
+
+__device__ inline double exp_nonpos(double a, const double* tbl) {
+  a = fmax(a, -746.0);  // -inf and anything below underflow to 0 through ldexp
+  const double n = rint(a * kInvLn2x64);
+  const double r = fma(-n, kLn2by64Lo, fma(-n, kLn2by64Hi, a));
+  double p = fma(r, 1.0 / 120.0, 1.0 / 24.0);
+  p = fma(p, r, 1.0 / 6.0);
+  p = fma(p, r, 0.5);
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
+  const int ni = int(n);
+  return ldexp(tbl[ni & 63] * p, ni >> 6);
+}
+
+// ---------------------------------------------------------------------------
+// Team synchronisation.
+
 struct Team {
   uint32_t* ctr;
   uint32_t target;
@@ -70,25 +100,37 @@ __device__ inline double* member_slot(Team& tm, int member) {
   return tm.part + (size_t(tm.phase & 1) * tm.W + member) * tm.stride;
 }
 
+// Partials travel through device-coherent (agent-scope) atomic stores and
+// loads, which bypass the non-coherent caches; so the barrier needs no L2
+// write-back or invalidate, only ordering: a member's partial stores
+// complete before its counter increment (release at workgroup scope is a
+// wait for them), and no partial is read before the counter says all
+// members have arrived.
+__device__ inline void put_partial(double* slot, int k, double v) {
+  __hip_atomic_store(slot + k, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline double get_partial(const double* slot, int k) {
+  return __hip_atomic_load(const_cast<double*>(slot) + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // All members have published their partial for the current phase.
 __device__ void team_sync(Team& tm) {
   __syncthreads();
   if (tm.W > 1) {
     tm.target += uint32_t(tm.W);
     if (threadIdx.x == 0) {
-      __threadfence();
-      atomicAdd(tm.ctr, 1u);
+      __hip_atomic_fetch_add(tm.ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
       uint32_t spins = 0;
-      while (__hip_atomic_load(tm.ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < tm.target) {
-        __builtin_amdgcn_s_sleep(2);
+      while (__hip_atomic_load(tm.ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < tm.target) {
+        __builtin_amdgcn_s_sleep(1);
         if (++spins > kSpinLimit) {
           raise_status(tm.status, TV_DEV_TIMEOUT);
           break;
         }
       }
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
     }
     __syncthreads();
-    __threadfence();
   }
 }
 
@@ -97,20 +139,21 @@ __device__ void team_sync(Team& tm) {
 __device__ void team_exit(Team& tm) {
   __syncthreads();
   if (tm.W > 1 && threadIdx.x == 0) {
-    __threadfence();
-    const uint32_t old = atomicAdd(tm.ctr, 1u);
-    if (old == tm.target + uint32_t(tm.W) - 1u) atomicExch(tm.ctr, 0u);
+    const uint32_t old = __hip_atomic_fetch_add(tm.ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == tm.target + uint32_t(tm.W) - 1u)
+      __hip_atomic_store(tm.ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-// Wave sum; every lane returns lane 0's value (bit-identical across lanes).
+// ---------------------------------------------------------------------------
+// Block reductions (fixed order: wave shuffles, then waves in index order).
+
 __device__ inline double wave_sum(double v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += shfl_xor_d(v, off);
   return __shfl(v, 0, kWave);
 }
 
-// Block sum in a fixed order (wave sums, then waves in index order).
 __device__ inline double block_sum(double v, double* sh) {
   v = wave_sum(v);
   const int wave = threadIdx.x / kWave;
@@ -123,27 +166,23 @@ __device__ inline double block_sum(double v, double* sh) {
 }
 
 // (max, sum of exp(x - max)) pairs.
-__device__ inline void ms_combine(double& m, double& s, double m2, double s2) {
+__device__ inline void ms_combine(double& m, double& s, double m2, double s2, const double* tbl) {
   if (m2 > m) {
-    s = s * exp(m - m2) + s2;
+    s = s * exp_nonpos(m - m2, tbl) + s2;
     m = m2;
   } else if (m2 != -INFINITY) {
-    s += s2 * exp(m2 - m);
+    s += s2 * exp_nonpos(m2 - m, tbl);
   }
 }
 
-__device__ inline void wave_ms(double& m, double& s) {
+__device__ inline void block_ms(double& m, double& s, double* sh, const double* tbl) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     const double m2 = shfl_xor_d(m, off), s2 = shfl_xor_d(s, off);
-    ms_combine(m, s, m2, s2);
+    ms_combine(m, s, m2, s2, tbl);
   }
   m = __shfl(m, 0, kWave);
   s = __shfl(s, 0, kWave);
-}
-
-__device__ inline void block_ms(double& m, double& s, double* sh) {
-  wave_ms(m, s);
   const int wave = threadIdx.x / kWave;
   if ((threadIdx.x & 63) == 0) {
     sh[2 * wave] = m;
@@ -152,195 +191,207 @@ __device__ inline void block_ms(double& m, double& s, double* sh) {
   __syncthreads();
   m = -INFINITY;
   s = 0.0;
-  for (int w = 0; w < kWaves; ++w) ms_combine(m, s, sh[2 * w], sh[2 * w + 1]);
+  for (int w = 0; w < kWaves; ++w) ms_combine(m, s, sh[2 * w], sh[2 * w + 1], tbl);
   __syncthreads();
-}
-
-// Online (max, sum) update with one element x.
-__device__ inline void ms_push(double& m, double& s, double x) {
-  if (x > m) {
-    s = s * exp(m - x) + 1.0;
-    m = x;
-  } else {
-    s += exp(x - m);
-  }
 }
 
 // argmax with the lowest index on ties.
 __device__ inline void am_combine(float& v, int& i, float v2, int i2) {
-  if (v2 > v || (v2 == v && i2 < i)) {
-    v = v2;
-    i = i2;
-  }
+  const bool take = v2 > v || (v2 == v && i2 < i);
+  v = take ? v2 : v;
+  i = take ? i2 : i;
 }
 
-__device__ int block_argmax(const float* row, int V, uint32_t* status, float* shv, int* shi) {
-  float bv = -INFINITY;
-  int bi = 0x7fffffff;
-  bool bad = false;
-  if ((V & 3) == 0) {
-    const float4* r4 = reinterpret_cast<const float4*>(row);
-    for (int i = threadIdx.x; i < V / 4; i += kThreads) {
-      const float4 a = r4[i];
-      bad |= !isfinite(a.x) || !isfinite(a.y) || !isfinite(a.z) || !isfinite(a.w);
-      am_combine(bv, bi, a.x, 4 * i);
-      am_combine(bv, bi, a.y, 4 * i + 1);
-      am_combine(bv, bi, a.z, 4 * i + 2);
-      am_combine(bv, bi, a.w, 4 * i + 3);
-    }
-  } else {
-    for (int i = threadIdx.x; i < V; i += kThreads) {
-      const float a = row[i];
-      bad |= !isfinite(a);
-      am_combine(bv, bi, a, i);
-    }
-  }
-  if (bad) raise_status(status, TV_DEV_LOGITS);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const float v2 = __shfl_xor(bv, off, kWave);
-    const int i2 = __shfl_xor(bi, off, kWave);
-    am_combine(bv, bi, v2, i2);
-  }
-  const int wave = threadIdx.x / kWave;
-  if ((threadIdx.x & 63) == 0) {
-    shv[wave] = bv;
-    shi[wave] = bi;
-  }
-  __syncthreads();
-  float v = -INFINITY;
-  int idx = 0x7fffffff;
-  for (int w = 0; w < kWaves; ++w) am_combine(v, idx, shv[w], shi[w]);
-  __syncthreads();
-  return idx == 0x7fffffff ? 0 : idx;
-}
-
-// Per-node softmax statistics of one row slice: max and sum of exp of x/T.
-struct RowStats {
-  double m, z;
-};
-
-__device__ void slice_stats(const float* row, int lo, int hi, double invT, bool vec4,
-                            double& m, double& s, bool& bad) {
+// ---------------------------------------------------------------------------
+// Vocabulary sweeps over [lo, hi) of one or two rows. Each step issues
+// kUnroll 16-byte loads per row per thread before using any of them; then
+// f(t, d, y, valid) sees every element once (d = 0 when only one row is
+// read). Indices past hi are clamped to a valid address and passed with
+// valid = false, so the loop body never branches. lo is a multiple of 4 in
+// the vectorised form (rows are 16-byte aligned when V % 4 == 0).
+template <bool TWO, class F>
+__device__ inline void sweep(const float* tr, const float* dr, int lo, int hi, bool vec4, F&& f) {
   if (vec4) {
-    for (int i = lo + 4 * threadIdx.x; i < hi; i += 4 * kThreads) {
-      const float4 a = *reinterpret_cast<const float4*>(row + i);
-      bad |= !isfinite(a.x) || !isfinite(a.y) || !isfinite(a.z) || !isfinite(a.w);
-      const double x0 = double(a.x) * invT, x1 = double(a.y) * invT;
-      const double x2 = double(a.z) * invT, x3 = double(a.w) * invT;
-      const double lm = fmax(fmax(x0, x1), fmax(x2, x3));
-      if (lm > m) {
-        s *= exp(m - lm);
-        m = lm;
+    const float4* t4 = reinterpret_cast<const float4*>(tr + lo);
+    const float4* d4 = reinterpret_cast<const float4*>(dr + lo);
+    const int n4 = (hi - lo) >> 2;
+    for (int base = threadIdx.x; base < n4; base += kUnroll * kThreads) {
+      float4 tv[kUnroll], dv[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int i = min(base + u * kThreads, n4 - 1);
+        tv[u] = t4[i];
+        if (TWO) dv[u] = d4[i];
       }
-      s += exp(x0 - m) + exp(x1 - m) + exp(x2 - m) + exp(x3 - m);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int i = base + u * kThreads;
+        const bool ok = i < n4;
+        const int y = lo + 4 * i;
+        f(tv[u].x, TWO ? dv[u].x : 0.f, y, ok);
+        f(tv[u].y, TWO ? dv[u].y : 0.f, y + 1, ok);
+        f(tv[u].z, TWO ? dv[u].z : 0.f, y + 2, ok);
+        f(tv[u].w, TWO ? dv[u].w : 0.f, y + 3, ok);
+      }
     }
   } else {
-    for (int i = lo + threadIdx.x; i < hi; i += kThreads) {
-      const float a = row[i];
-      bad |= !isfinite(a);
-      ms_push(m, s, double(a) * invT);
+    for (int base = lo + threadIdx.x; base < hi; base += kUnroll * kThreads) {
+      float tv[kUnroll], dv[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int y = min(base + u * kThreads, hi - 1);
+        tv[u] = tr[y];
+        if (TWO) dv[u] = dr[y];
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int y = base + u * kThreads;
+        f(tv[u], TWO ? dv[u] : 0.f, y, y < hi);
+      }
     }
   }
 }
 
-// Residual weight of token y: max(p(y) - a q(y), 0) with
-// p(y) = exp(t_y/T - Mt)/Zt, q(y) = exp(d_y/T - Md)/Zd. With a == 0 the draft
-// row is not read.
+// Residual weight max(p(y) - a q(y), 0) with p(y) = exp(t/T - Mt)/Zt and
+// q(y) = exp(d/T - Md)/Zd (plain p(y) when a == 0; the draft row is then
+// not needed).
 struct Resid {
-  const float* trow;
-  const float* drow;
   double invT, Mt, invZt, Md, invZd, a;
-  __device__ inline double p(int y) const { return exp(fma(double(trow[y]), invT, -Mt)) * invZt; }
-  __device__ inline double q(int y) const { return exp(fma(double(drow[y]), invT, -Md)) * invZd; }
-  __device__ inline double w(int y) const {
-    const double pv = p(y);
-    if (a == 0.0) return pv;
-    const double r = pv - a * q(y);
+  __device__ inline double p(float t, const double* tbl) const {
+    return exp_nonpos(fma(double(t), invT, -Mt), tbl) * invZt;
+  }
+  __device__ inline double q(float d, const double* tbl) const {
+    return exp_nonpos(fma(double(d), invT, -Md), tbl) * invZd;
+  }
+  __device__ inline double w(float t, float d, const double* tbl) const {
+    const double r = p(t, tbl) - a * q(d, tbl);  // a == 0: plain p (d is not needed)
     return r > 0.0 ? r : 0.0;
   }
 };
 
-__device__ double slice_resid_sum(const Resid& R, int lo, int hi, bool vec4) {
-  double acc = 0.0;
-  if (vec4) {
-    for (int i = lo + 4 * threadIdx.x; i < hi; i += 4 * kThreads) {
-      const float4 tv = *reinterpret_cast<const float4*>(R.trow + i);
-      const float4 dv = *reinterpret_cast<const float4*>(R.drow + i);
-      const float tt[4] = {tv.x, tv.y, tv.z, tv.w};
-      const float dd[4] = {dv.x, dv.y, dv.z, dv.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const double pv = exp(fma(double(tt[e]), R.invT, -R.Mt)) * R.invZt;
-        const double qv = exp(fma(double(dd[e]), R.invT, -R.Md)) * R.invZd;
-        const double r = pv - R.a * qv;
-        acc += r > 0.0 ? r : 0.0;
-      }
-    }
-  } else {
-    for (int i = lo + threadIdx.x; i < hi; i += kThreads) acc += R.w(i);
-  }
-  return acc;
-}
-
-__device__ inline int wave_chunk_begin(int lo, int hi, int wv) {
+// Smallest y in [lo, hi) where the running sum of weights passes thr
+// (ascending token id), searched by the whole block. Each wave owns a
+// contiguous quarter of [lo, hi) and sums it in blocks of 64 x 8 tokens
+// (8 loads per lane in flight); the quarter holding thr is then scanned
+// block by block with an in-order prefix over the block's tokens. Falls
+// back to the last token with positive weight. Result in *s_y.
+__device__ void slice_search(const float* tr, const float* dr, int lo, int hi, const Resid& R,
+                             double thr, const double* tbl, double* sh, int* s_y) {
+  constexpr int K = 8;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x / kWave;
   const int n = hi - lo;
   int per = (n + kWaves - 1) / kWaves;
-  per = (per + 63) / 64 * 64;
-  return min(hi, lo + wv * per);
-}
-
-// Sum of residual weights over this wave's contiguous chunk, in 64-token
-// steps (the same step structure the search below replays).
-__device__ double wave_chunk_sum(const Resid& R, int cb, int ce) {
-  const int lane = threadIdx.x & 63;
-  double run = 0.0;
-  for (int base = cb; base < ce; base += 64) {
-    const int y = base + lane;
-    const double w = (y < ce) ? R.w(y) : 0.0;
-    run += wave_sum(w);
-  }
-  return run;
-}
-
-// Smallest token in [cb, ce) where the running sum exceeds thr (token ids
-// ascending). Falls back to the last token with positive weight.
-__device__ int wave_chunk_search(const Resid& R, int cb, int ce, double thr) {
-  const int lane = threadIdx.x & 63;
-  double run = 0.0;
-  int last_pos = -1;
-  for (int base = cb; base < ce; base += 64) {
-    const int y = base + lane;
-    const double w = (y < ce) ? R.w(y) : 0.0;
-    const double step = wave_sum(w);
-    const unsigned long long posmask = __ballot(w > 0.0);
-    if (posmask) last_pos = base + 63 - __clzll(posmask);
-    if (run + step > thr) {
-      double incl = w;
+  per = (per + 64 * K - 1) / (64 * K) * (64 * K);
+  const int cb = min(hi, lo + wave * per), ce = min(hi, cb + per);
+  // weights of block [base, base + 64K): element k of lane l is y = base + 64k + l
+  auto block_w = [&](int base, double* w) {
+    float tv[K], dv[K];
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const double o = __shfl_up(incl, off, kWave);
-        if (lane >= off) incl += o;
-      }
-      const unsigned long long hit = __ballot(run + incl > thr && w > 0.0);
-      if (hit) return base + __ffsll(static_cast<long long>(hit)) - 1;
-      return last_pos;
+    for (int k = 0; k < K; ++k) {
+      const int y = min(base + 64 * k + lane, hi - 1);
+      tv[k] = tr[y];
+      dv[k] = dr[y];
     }
-    run += step;
+#pragma unroll
+    for (int k = 0; k < K; ++k) w[k] = base + 64 * k + lane < ce ? R.w(tv[k], dv[k], tbl) : 0.0;
+  };
+  double run = 0.0;
+  for (int base = cb; base < ce; base += 64 * K) {
+    double w[K];
+    block_w(base, w);
+    double ls = 0.0;
+#pragma unroll
+    for (int k = 0; k < K; ++k) ls += w[k];
+    run += wave_sum(ls);
   }
-  return last_pos;
+  if (lane == 0) sh[wave] = run;
+  __syncthreads();
+  int fw = -1, last_w = -1;
+  double pre = 0.0, fpre = 0.0, last_pre = 0.0;
+  for (int w = 0; w < kWaves; ++w) {
+    const double cw = sh[w];
+    if (cw > 0.0) {
+      last_w = w;
+      last_pre = pre;
+    }
+    if (fw < 0 && pre <= thr && thr < pre + cw) {
+      fw = w;
+      fpre = pre;
+    }
+    pre += cw;
+  }
+  const bool past_end = fw < 0;  // rounding put thr past the end
+  if (past_end) {
+    fw = last_w;
+    fpre = last_pre;
+  }
+  __syncthreads();
+  if (wave == fw) {
+    const double local = thr - fpre;
+    double acc = 0.0;
+    int found = -1, last_pos = -1;
+    for (int base = cb; base < ce && found < 0; base += 64 * K) {
+      double w[K];
+      block_w(base, w);
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const unsigned long long posmask = __ballot(w[k] > 0.0);
+        if (posmask) last_pos = base + 64 * k + 63 - __clzll(posmask);
+        double incl = w[k];
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const double o = __shfl_up(incl, off, kWave);
+          if (lane >= off) incl += o;
+        }
+        const unsigned long long hit = __ballot(!past_end && acc + incl > local && w[k] > 0.0);
+        if (found < 0 && hit) found = base + 64 * k + __ffsll(static_cast<long long>(hit)) - 1;
+        acc += __shfl(incl, 63, kWave);
+      }
+    }
+    if (found < 0) found = last_pos;
+    if (lane == 0) *s_y = found < 0 ? lo : found;
+  }
+  if (fw < 0 && threadIdx.x == 0) *s_y = lo;
+  __syncthreads();
+}
+
+// Next child of v after row `after` (children in ascending row = draw
+// order), found by wave 0 with a ballot; -1 when none. Broadcast via LDS.
+__device__ int next_child(const int* par, int N, int v, int after, int* s_c) {
+  if (threadIdx.x < kWave) {
+    int found = -1;
+    for (int base = after + 1; base < N && found < 0; base += kWave) {
+      const int i = base + threadIdx.x;
+      const unsigned long long m = __ballot(i < N && par[i] == v);
+      if (m) found = base + __ffsll(static_cast<long long>(m)) - 1;
+    }
+    if (threadIdx.x == 0) *s_c = found;
+  }
+  __syncthreads();
+  const int c = *s_c;
+  __syncthreads();
+  return c;
 }
 
 __global__ __launch_bounds__(kThreads) void sample_kernel(SampleParams p) {
+  __shared__ double tbl[64];
   __shared__ double sh[2 * kWaves];
-  __shared__ double sh_chunk[kWaves];
+  __shared__ double s_slice[kMaxTeam];
   __shared__ float shv[kWaves];
   __shared__ int shi[kWaves];
-  __shared__ int s_children[kMaxChildren];
-  __shared__ int s_nchild;
+  __shared__ int s_int;
 
-  const int r = blockIdx.x / p.W;
-  const int member = blockIdx.x - r * p.W;
+  // Team placement: block b runs on XCD b % 8; the W members of a team are
+  // consecutive slots of one XCD.
+  const int xcd = blockIdx.x & 7;
+  const int slot = blockIdx.x >> 3;
+  const int r = (slot / p.W) * 8 + xcd;
+  const int member = slot - (slot / p.W) * p.W;
+  if (r >= p.B) return;  // padding block: belongs to no team
+
+  for (int j = threadIdx.x; j < 64; j += kThreads) tbl[j] = exp2(double(j) / 64.0);
+
   Team tm;
   tm.ctr = p.team_ctr + r;
   tm.target = 0;
@@ -355,13 +406,14 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleParams p) {
   const int N = p.node_indptr[r + 1] - nbeg;
   const int V = p.V;
   const float T = p.temperature[r];
-  const bool shape_ok = N > 0 && N <= p.max_nodes && N <= kMaxChildren;
-  if (!shape_ok) {
+  if (N <= 0 || N > p.max_nodes) {
     if (N != 0 && threadIdx.x == 0 && member == 0) raise_status(p.status, TV_DEV_SHAPE);
     return;  // uniform for the whole team: nobody waits on anybody
   }
   const int* par = p.parent + nbeg;
   const int* tok = p.tokens + nbeg;
+  const bool vec4 = (V & 3) == 0;
+  __syncthreads();  // table ready
 
   if (!(T >= 0.f) || (T > 0.f && p.d == nullptr)) {
     if (member == 0) {
@@ -377,8 +429,38 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleParams p) {
   if (T == 0.f) {
     // Greedy exact match: argmax of every row, then the match flags.
     for (int i = member; i < N; i += p.W) {
-      const int y = block_argmax(p.t + size_t(nbeg + i) * V, V, p.status, shv, shi);
-      if (threadIdx.x == 0) p.next_token[nbeg + i] = y;
+      const float* row = p.t + size_t(nbeg + i) * V;
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+      bool bad = false;
+      sweep<false>(row, row, 0, V, vec4, [&](float t, float, int y, bool ok) {
+        bad |= ok && !isfinite(t);
+        const bool take = ok && t > bv;  // ascending y per thread: ties keep the first
+        bv = take ? t : bv;
+        bi = take ? y : bi;
+      });
+      if (bad) raise_status(p.status, TV_DEV_LOGITS);
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        const float v2 = __shfl_xor(bv, off, kWave);
+        const int i2 = __shfl_xor(bi, off, kWave);
+        am_combine(bv, bi, v2, i2);
+      }
+      const int wave = threadIdx.x / kWave;
+      if ((threadIdx.x & 63) == 0) {
+        shv[wave] = bv;
+        shi[wave] = bi;
+      }
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        float v = -INFINITY;
+        int idx = 0x7fffffff;
+        for (int w = 0; w < kWaves; ++w) am_combine(v, idx, shv[w], shi[w]);
+        // device-coherent store: other members read it after the barrier
+        __hip_atomic_store(p.next_token + nbeg + i, idx == 0x7fffffff ? 0 : idx, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();
     }
     team_sync(tm);
     for (int i = member * kThreads + threadIdx.x; i < N; i += p.W * kThreads) {
@@ -390,7 +472,9 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleParams p) {
         if (pi < 0 || pi >= i) {
           raise_status(p.status, TV_DEV_TREE);
         } else {
-          f = (tok[i] == p.next_token[nbeg + pi]) ? 1 : 0;
+          const int ntp = __hip_atomic_load(p.next_token + nbeg + pi, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+          f = (tok[i] == ntp) ? 1 : 0;
         }
       }
       p.flag[nbeg + i] = f;
@@ -411,66 +495,87 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleParams p) {
   slice = (slice + 3) / 4 * 4;
   const int lo = min(V, member * slice);
   const int hi = min(V, lo + slice);
-  const bool vec4 = (V & 3) == 0;
-  const int wv = threadIdx.x / kWave;
-  const int cb = wave_chunk_begin(lo, hi, wv);
-  const int ce = wave_chunk_begin(lo, hi, wv + 1);
 
   int v = 0;
   for (int depth_guard = 0; depth_guard <= N; ++depth_guard) {
     const float* trow = p.t + size_t(nbeg + v) * V;
     const float* drow = p.d + size_t(nbeg + v) * V;
-    // Stats pass: (max, sum exp) of t/T and d/T over the team's slices.
+    // Stats pass: (max, sum exp) of t/T and d/T over the member's slice.
+    // Each thread keeps running maxima; one sweep step raises them first
+    // (rescaling the sums once), then adds the step's terms.
     double mt = -INFINITY, st = 0.0, md = -INFINITY, sd = 0.0;
     bool bad = false;
-    slice_stats(trow, lo, hi, invT, vec4, mt, st, bad);
-    slice_stats(drow, lo, hi, invT, vec4, md, sd, bad);
+    {
+      double xt[4 * kUnroll], xd[4 * kUnroll];
+      int cnt = 0;
+      double smt = -INFINITY, smd = -INFINITY;
+      auto flush = [&]() {
+        const double nmt = fmax(mt, smt), nmd = fmax(md, smd);
+        st *= exp_nonpos(mt - nmt, tbl);  // 0 while mt is -inf (st is 0 then)
+        sd *= exp_nonpos(md - nmd, tbl);
+        mt = nmt;
+        md = nmd;
+#pragma unroll
+        for (int k = 0; k < 4 * kUnroll; ++k) {
+          st += exp_nonpos(xt[k] - mt, tbl);
+          sd += exp_nonpos(xd[k] - md, tbl);
+        }
+        smt = smd = -INFINITY;
+        cnt = 0;
+      };
+      sweep<true>(trow, drow, lo, hi, vec4, [&](float t, float d, int, bool ok) {
+        bad |= ok && (!isfinite(t) || !isfinite(d));
+        const double a = ok ? double(t) * invT : -INFINITY;
+        const double b = ok ? double(d) * invT : -INFINITY;
+        xt[cnt] = a;
+        xd[cnt] = b;
+        smt = fmax(smt, a);
+        smd = fmax(smd, b);
+        if (++cnt == 4 * kUnroll) flush();
+      });
+      if (cnt) {
+        for (int k = cnt; k < 4 * kUnroll; ++k) xt[k] = xd[k] = -INFINITY;
+        flush();
+      }
+      if (mt == -INFINITY) st = sd = 0.0;
+    }
     if (bad) raise_status(p.status, TV_DEV_LOGITS);
-    block_ms(mt, st, sh);
-    block_ms(md, sd, sh);
+    block_ms(mt, st, sh, tbl);
+    block_ms(md, sd, sh, tbl);
     if (threadIdx.x == 0) {
-      double* slot = member_slot(tm, member);
-      slot[0] = mt;
-      slot[1] = st;
-      slot[2] = md;
-      slot[3] = sd;
+      double* ms = member_slot(tm, member);
+      put_partial(ms, 0, mt);
+      put_partial(ms, 1, st);
+      put_partial(ms, 2, md);
+      put_partial(ms, 3, sd);
     }
     team_sync(tm);
     double Mt = -INFINITY, Zt = 0.0, Md = -INFINITY, Zd = 0.0;
     for (int w = 0; w < p.W; ++w) {
-      const double* slot = member_slot(tm, w);
-      ms_combine(Mt, Zt, slot[0], slot[1]);
-      ms_combine(Md, Zd, slot[2], slot[3]);
+      const double* ms = member_slot(tm, w);
+      ms_combine(Mt, Zt, get_partial(ms, 0), get_partial(ms, 1), tbl);
+      ms_combine(Md, Zd, get_partial(ms, 2), get_partial(ms, 3), tbl);
+    }
+    // Slice sums of p (for a draw at a leaf): s_w exp(m_w - Mt) / Zt.
+    if (threadIdx.x < p.W) {
+      const double* ms = member_slot(tm, threadIdx.x);
+      const double m0 = get_partial(ms, 0), s0 = get_partial(ms, 1);
+      s_slice[threadIdx.x] = m0 == -INFINITY ? 0.0 : s0 * exp_nonpos(m0 - Mt, tbl) / Zt;
     }
     tm.phase++;
-
-    // Children of v in draw order.
-    if (threadIdx.x < kWave) {
-      int cnt = 0;
-      for (int base = v + 1; base < N; base += kWave) {
-        const int i = base + threadIdx.x;
-        const bool is_child = i < N && par[i] == v;
-        const unsigned long long m = __ballot(is_child);
-        if (is_child) s_children[cnt + __popcll(m & ((1ull << threadIdx.x) - 1ull))] = i;
-        cnt += __popcll(m);
-      }
-      if (threadIdx.x == 0) s_nchild = cnt;
-    }
     __syncthreads();
-    const int nchild = s_nchild;
 
-    Resid R{trow, drow, invT, Mt, 1.0 / Zt, Md, 1.0 / Zd, 0.0};
+    Resid R{invT, Mt, 1.0 / Zt, Md, 1.0 / Zd, 0.0};
     double B = 1.0, S = 1.0;
     int accepted = -1;
-    for (int j = 0; j < nchild; ++j) {
-      const int c = s_children[j];
+    for (int c = next_child(par, N, v, v, &s_int); c >= 0; c = next_child(par, N, v, c, &s_int)) {
       int x = tok[c];
       if (x < 0 || x >= V) {
         if (threadIdx.x == 0 && member == 0) raise_status(p.status, TV_DEV_SHAPE);
         x = 0;
       }
-      const double px = R.p(x);
-      const double qx = R.q(x);
+      const double px = R.p(trow[x], tbl);
+      const double qx = R.q(drow[x], tbl);
       double pj = px - R.a * qx;
       pj = (pj > 0.0 ? pj : 0.0) / B;
       const double qj = qx / S;
@@ -484,18 +589,24 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleParams p) {
       // Rejected: one residual pass at a' = a + B/S.
       Resid Rn = R;
       Rn.a = R.a + B / S;
-      double part = slice_resid_sum(Rn, lo, hi, vec4);
+      double part = 0.0;
+      sweep<true>(trow, drow, lo, hi, vec4, [&](float t, float d, int, bool ok) {
+        const double w = Rn.w(t, d, tbl);
+        part += ok ? w : 0.0;
+      });
       part = block_sum(part, sh);
-      if (threadIdx.x == 0) member_slot(tm, member)[0] = part;
+      if (threadIdx.x == 0) put_partial(member_slot(tm, member), 0, part);
       team_sync(tm);
       double F = 0.0;
-      for (int w = 0; w < p.W; ++w) F += member_slot(tm, w)[0];
-      tm.phase++;
+      for (int w = 0; w < p.W; ++w) F += get_partial(member_slot(tm, w), 0);
       if (F > 0.0) {
         R.a = Rn.a;
         B = F;
+        if (threadIdx.x < p.W) s_slice[threadIdx.x] = get_partial(member_slot(tm, threadIdx.x), 0);
       }
+      tm.phase++;
       S -= qx;
+      __syncthreads();
     }
     if (accepted >= 0) {
       v = accepted;
@@ -503,70 +614,32 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleParams p) {
     }
 
     // Stop at v: inverse-CDF draw from the residual (p itself when a == 0).
-    const double wsum = wave_chunk_sum(R, cb, ce);
-    if ((threadIdx.x & 63) == 0) sh_chunk[wv] = wsum;
-    __syncthreads();
-    double mine = 0.0;
-    for (int w = 0; w < kWaves; ++w) mine += sh_chunk[w];
-    if (threadIdx.x == 0) member_slot(tm, member)[0] = mine;
-    team_sync(tm);
-    double total = 0.0;
-    int finder = -1;
-    double base_w = 0.0;
+    // The slice sums of the last pass locate the slice; its owner scans it.
     const double u = double(p.uniforms[2 * size_t(nbeg + v) + 1]);
-    {
-      double run = 0.0;
-      for (int w = 0; w < p.W; ++w) run += member_slot(tm, w)[0];
-      total = run;
-      const double thr = u * total;
-      double pre = 0.0;
-      int last_pos = -1;
-      double last_pre = 0.0;
-      for (int w = 0; w < p.W; ++w) {
-        const double sw = member_slot(tm, w)[0];
-        if (sw > 0.0) {
-          last_pos = w;
-          last_pre = pre;
-        }
-        if (finder < 0 && pre <= thr && thr < pre + sw) {
-          finder = w;
-          base_w = pre;
-        }
-        pre += sw;
+    double total = 0.0;
+    for (int w = 0; w < p.W; ++w) total += s_slice[w];
+    const double thr = u * total;
+    int finder = -1, last_w = -1;
+    double pre = 0.0, base_w = 0.0, last_pre = 0.0;
+    for (int w = 0; w < p.W; ++w) {
+      const double sw = s_slice[w];
+      if (sw > 0.0) {
+        last_w = w;
+        last_pre = pre;
       }
-      if (finder < 0) {
-        finder = last_pos;
-        base_w = last_pre;
+      if (finder < 0 && pre <= thr && thr < pre + sw) {
+        finder = w;
+        base_w = pre;
       }
+      pre += sw;
     }
-    tm.phase++;
+    if (finder < 0) {
+      finder = last_w;
+      base_w = last_pre;
+    }
     if (finder == member) {
-      const double local = u * total - base_w;
-      int fw = -1;
-      double pre = 0.0, fpre = 0.0;
-      int last_w = -1;
-      double last_pre = 0.0;
-      for (int w = 0; w < kWaves; ++w) {
-        const double cw = sh_chunk[w];
-        if (cw > 0.0) {
-          last_w = w;
-          last_pre = pre;
-        }
-        if (fw < 0 && pre <= local && local < pre + cw) {
-          fw = w;
-          fpre = pre;
-        }
-        pre += cw;
-      }
-      if (fw < 0) {
-        fw = last_w;
-        fpre = last_pre;
-      }
-      if (wv == fw) {
-        int y = wave_chunk_search(R, cb, ce, local - fpre);
-        if (y < 0) y = 0;
-        if ((threadIdx.x & 63) == 0) p.next_token[nbeg + v] = y;
-      }
+      slice_search(trow, drow, lo, hi, R, thr - base_w, tbl, sh, &s_int);
+      if (threadIdx.x == 0) p.next_token[nbeg + v] = s_int;
     }
     break;
   }
@@ -576,8 +649,7 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleParams p) {
 }  // namespace
 
 bool plan_sample(const tv_sample_desc& d, SamplePlan* out) {
-  if (d.batch < 1 || d.vocab < 1 || d.max_nodes < 1 || d.max_nodes > kMaxChildren ||
-      d.max_depth < 0)
+  if (d.batch < 1 || d.vocab < 1 || d.max_nodes < 1 || d.max_nodes > 65536 || d.max_depth < 0)
     return false;
   SamplePlan pl{};
   pl.threads = kThreads;
@@ -586,8 +658,7 @@ bool plan_sample(const tv_sample_desc& d, SamplePlan* out) {
   pl.off_team_ctr = off;
   off = align256(off + size_t(d.batch) * sizeof(uint32_t));
   pl.off_part = off;
-  // Up to 16 members per team, two parities.
-  off = align256(off + size_t(d.batch) * 2 * 16 * pl.part_stride * sizeof(double));
+  off = align256(off + size_t(d.batch) * 2 * kMaxTeam * pl.part_stride * sizeof(double));
   pl.total_bytes = off;
   *out = pl;
   return true;
@@ -614,12 +685,14 @@ hipError_t launch_sample(const tv_sample_desc& d, const SamplePlan& pl, const Sa
     g_coop_blocks_per_cu = per;
     g_num_cus = prop.multiProcessorCount;
   }
-  // Team size: roughly one workgroup per CU across the batch, at most 16.
+  // Team size: about two workgroups per CU across the batch, at most 8
+  // (a team lives on one XCD), and the padded grid must be resident.
   const long resident = long(g_coop_blocks_per_cu) * g_num_cus;
-  int W = int(g_num_cus / d.batch);
-  if (W > 16) W = 16;
+  int W = int(2L * g_num_cus / d.batch);
+  if (W > kMaxTeam) W = kMaxTeam;
   if (W < 1) W = 1;
-  while (W > 1 && long(W) * d.batch > resident) --W;
+  auto grid_for = [&](int w) { return long((d.batch + 7) / 8) * 8 * w; };
+  while (W > 1 && grid_for(W) > resident) --W;
   SampleParams p{};
   p.t = a.target;
   p.d = a.draft;
@@ -639,7 +712,7 @@ hipError_t launch_sample(const tv_sample_desc& d, const SamplePlan& pl, const Sa
   p.W = W;
   p.max_nodes = d.max_nodes;
   p.part_stride = pl.part_stride;
-  const dim3 grid(unsigned(d.batch * W)), block(kThreads);
+  const dim3 grid(unsigned(grid_for(W))), block(kThreads);
   if (W == 1) {
     hipLaunchKernelGGL(sample_kernel, grid, block, 0, stream, p);
     return hipGetLastError();
