@@ -27,7 +27,7 @@ import numpy as np  # noqa: E402
 
 METRIC = "tree-verify nodes/s per layer + achieved HBM GB/s (% of MI355X peak), 1 GPU"
 HBM_PEAK_GBS = 8000.0
-PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "attn_mfma_highload_counters.md")
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "tree_verify_attn_highload_counters.md")
 ATTN_SOURCE = os.path.join(ROOT, "tree_verification_verify_amd", "csrc", "tree_attn.hip")
 
 
@@ -250,7 +250,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic,
-                     "kernel": "attn_stream_kernel<128> (tree_verify_attn)",
+                     "kernel": "tree_verify_attn (attn_stream_kernel<128> + attn_merge_kernel<128>)",
                      "algorithmic_bytes": abytes, "algorithmic_flops": aflops,
                      "kernel_ms": attn_ms,
                      "tflops": aflops / (attn_ms * 1e-3) / 1e12},
