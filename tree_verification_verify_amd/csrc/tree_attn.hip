@@ -301,7 +301,8 @@ __global__ __launch_bounds__(256, 2) void attn_stream_kernel(AttnParams p) {
   constexpr int KK = D / 32;          // 32-wide k-steps of the QK product
   constexpr int DT = D / 16;          // 16-wide d tiles of the PV product
   constexpr int KS = D + 8;           // LDS row stride of K (bf16 elements)
-  constexpr int VS = kStage + 8;      // LDS row stride of V^T (bf16 elements)
+  constexpr int VS = kStage + 4;      // LDS row stride of V^T: 34 words, so the 8-byte operand
+                                      // reads of 16 (32) lanes hit distinct banks with 32 (64) banks
   constexpr int PCH = 2 * D;          // 16-byte chunks per (page, head) block
   constexpr int CPT = 4 * PCH / 256;  // chunks per thread per stage (K, and V)
   constexpr int DB = D / 8;           // 16-byte chunks per K row
@@ -316,7 +317,7 @@ __global__ __launch_bounds__(256, 2) void attn_stream_kernel(AttnParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int l16 = lane & 15;
   const int lg = lane >> 4;
   const int lw = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
@@ -451,7 +452,9 @@ __global__ __launch_bounds__(256, 2) void attn_stream_kernel(AttnParams p) {
           vv = keep_first(vv, tail - (pg * kPage + (o & 1) * 8));
         }
         *reinterpret_cast<uint4*>(&k_lds[buf][(pg * kPage + kip) * KS + (o - kip * DB) * 8]) = kv;
-        *reinterpret_cast<uint4*>(&v_lds[buf][(o >> 1) * VS + pg * kPage + (o & 1) * 8]) = vv;
+        uint2* vdst = reinterpret_cast<uint2*>(&v_lds[buf][(o >> 1) * VS + pg * kPage + (o & 1) * 8]);
+        vdst[0] = make_uint2(vv.x, vv.y);  // rows are 8-byte aligned only
+        vdst[1] = make_uint2(vv.z, vv.w);
       }
     };
 

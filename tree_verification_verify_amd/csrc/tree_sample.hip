@@ -41,8 +41,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kMaxTeam = 8;              // members per team (one XCD holds a team)
-constexpr int kUnroll = 4;               // float4 loads per row per sweep step
+constexpr int kMaxTeam = 16;             // members per team (one XCD holds a team)
+constexpr int kUnroll = 4;               // float4 loads per row per step of a two-row sweep
 constexpr uint32_t kSpinLimit = 1u << 25;
 
 struct SampleParams {
@@ -113,6 +113,16 @@ __device__ inline double get_partial(const double* slot, int k) {
   return __hip_atomic_load(const_cast<double*>(slot) + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// All K partials of every member for the current phase, loaded in parallel
+// (one device-coherent load per thread) into LDS s_part[w * K + k].
+__device__ void gather_partials(Team& tm, int K, double* s_part) {
+  for (int i = threadIdx.x; i < tm.W * K; i += blockDim.x) {
+    const int w = i / K;
+    s_part[i] = get_partial(tm.part + (size_t(tm.phase & 1) * tm.W + w) * tm.stride, i - w * K);
+  }
+  __syncthreads();
+}
+
 // All members have published their partial for the current phase.
 __device__ void team_sync(Team& tm) {
   __syncthreads();
@@ -165,34 +175,23 @@ __device__ inline double block_sum(double v, double* sh) {
   return tot;
 }
 
-// (max, sum of exp(x - max)) pairs.
-__device__ inline void ms_combine(double& m, double& s, double m2, double s2, const double* tbl) {
-  if (m2 > m) {
-    s = s * exp_nonpos(m - m2, tbl) + s2;
-    m = m2;
-  } else if (m2 != -INFINITY) {
-    s += s2 * exp_nonpos(m2 - m, tbl);
-  }
-}
-
+// Block-wide (max, sum of exp(x - max)) of per-thread pairs: the maximum is
+// reduced first (shuffles only), then every sum is rescaled to it with one
+// exp and the sums are added in a fixed order.
 __device__ inline void block_ms(double& m, double& s, double* sh, const double* tbl) {
+  double M = m;
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const double m2 = shfl_xor_d(m, off), s2 = shfl_xor_d(s, off);
-    ms_combine(m, s, m2, s2, tbl);
-  }
-  m = __shfl(m, 0, kWave);
-  s = __shfl(s, 0, kWave);
+  for (int off = 32; off > 0; off >>= 1) M = fmax(M, shfl_xor_d(M, off));
   const int wave = threadIdx.x / kWave;
-  if ((threadIdx.x & 63) == 0) {
-    sh[2 * wave] = m;
-    sh[2 * wave + 1] = s;
-  }
+  if ((threadIdx.x & 63) == 0) sh[wave] = M;
   __syncthreads();
-  m = -INFINITY;
-  s = 0.0;
-  for (int w = 0; w < kWaves; ++w) ms_combine(m, s, sh[2 * w], sh[2 * w + 1], tbl);
+  M = sh[0];
+  for (int w = 1; w < kWaves; ++w) M = fmax(M, sh[w]);
   __syncthreads();
+  double v = (M == -INFINITY || m == -INFINITY) ? 0.0 : s * exp_nonpos(m - M, tbl);
+  v = block_sum(v, sh);
+  m = M;
+  s = v;
 }
 
 // argmax with the lowest index on ties.
@@ -211,6 +210,7 @@ __device__ inline void am_combine(float& v, int& i, float v2, int i2) {
 // the vectorised form (rows are 16-byte aligned when V % 4 == 0).
 template <bool TWO, class F>
 __device__ inline void sweep(const float* tr, const float* dr, int lo, int hi, bool vec4, F&& f) {
+  constexpr int kUnroll = TWO ? 4 : 8;  // 8 independent 16-byte loads per thread either way
   if (vec4) {
     const float4* t4 = reinterpret_cast<const float4*>(tr + lo);
     const float4* d4 = reinterpret_cast<const float4*>(dr + lo);
@@ -248,6 +248,77 @@ __device__ inline void sweep(const float* tr, const float* dr, int lo, int hi, b
         const int y = base + u * kThreads;
         f(tv[u], TWO ? dv[u] : 0.f, y, y < hi);
       }
+    }
+  }
+}
+
+// Per-thread (max, sum of exp(x/T - max)) of both rows over [lo, hi): every
+// step loads 4 float4 per row, raises the running maxima once from the
+// step's own maxima (one rescale), then adds the step's terms. Tail
+// elements are masked to -inf, so nothing branches per element.
+__device__ inline void slice_stats(const float* tr, const float* dr, int lo, int hi, bool vec4,
+                                   double invT, const double* tbl, double& mt, double& st,
+                                   double& md, double& sd, bool& bad) {
+  constexpr int U = 4;
+  auto step = [&](float (&a)[4 * U], float (&b)[4 * U]) {
+    float smt = -INFINITY, smd = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 4 * U; ++k) {
+      smt = fmaxf(smt, a[k]);
+      smd = fmaxf(smd, b[k]);
+    }
+    const double nmt = fmax(mt, double(smt) * invT), nmd = fmax(md, double(smd) * invT);
+    st = mt == -INFINITY ? 0.0 : st * exp_nonpos(mt - nmt, tbl);
+    sd = md == -INFINITY ? 0.0 : sd * exp_nonpos(md - nmd, tbl);
+    mt = nmt;
+    md = nmd;
+#pragma unroll
+    for (int k = 0; k < 4 * U; ++k) {
+      st += exp_nonpos(fma(double(a[k]), invT, -mt), tbl);
+      sd += exp_nonpos(fma(double(b[k]), invT, -md), tbl);
+    }
+  };
+  if (vec4) {
+    const float4* t4 = reinterpret_cast<const float4*>(tr + lo);
+    const float4* d4 = reinterpret_cast<const float4*>(dr + lo);
+    const int n4 = (hi - lo) >> 2;
+    for (int base = threadIdx.x; base < n4; base += U * kThreads) {
+      float4 tv[U], dv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = min(base + u * kThreads, n4 - 1);
+        tv[u] = t4[i];
+        dv[u] = d4[i];
+      }
+      float a[4 * U], b[4 * U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool ok = base + u * kThreads < n4;
+        const float ta[4] = {tv[u].x, tv[u].y, tv[u].z, tv[u].w};
+        const float da[4] = {dv[u].x, dv[u].y, dv[u].z, dv[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bad |= ok && (!isfinite(ta[e]) || !isfinite(da[e]));
+          a[4 * u + e] = ok ? ta[e] : -INFINITY;
+          b[4 * u + e] = ok ? da[e] : -INFINITY;
+        }
+      }
+      step(a, b);
+    }
+  } else {
+    for (int base = lo + threadIdx.x; base < hi; base += 4 * U * kThreads) {
+      float a[4 * U], b[4 * U];
+#pragma unroll
+      for (int k = 0; k < 4 * U; ++k) {
+        const int y = base + k * kThreads;
+        const int yc = min(y, hi - 1);
+        const float t = tr[yc], d = dr[yc];
+        const bool ok = y < hi;
+        bad |= ok && (!isfinite(t) || !isfinite(d));
+        a[k] = ok ? t : -INFINITY;
+        b[k] = ok ? d : -INFINITY;
+      }
+      step(a, b);
     }
   }
 }
@@ -378,6 +449,7 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleParams p) {
   __shared__ double tbl[64];
   __shared__ double sh[2 * kWaves];
   __shared__ double s_slice[kMaxTeam];
+  __shared__ double s_part[4 * kMaxTeam];
   __shared__ float shv[kWaves];
   __shared__ int shi[kWaves];
   __shared__ int s_int;
@@ -501,44 +573,9 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleParams p) {
     const float* trow = p.t + size_t(nbeg + v) * V;
     const float* drow = p.d + size_t(nbeg + v) * V;
     // Stats pass: (max, sum exp) of t/T and d/T over the member's slice.
-    // Each thread keeps running maxima; one sweep step raises them first
-    // (rescaling the sums once), then adds the step's terms.
     double mt = -INFINITY, st = 0.0, md = -INFINITY, sd = 0.0;
     bool bad = false;
-    {
-      double xt[4 * kUnroll], xd[4 * kUnroll];
-      int cnt = 0;
-      double smt = -INFINITY, smd = -INFINITY;
-      auto flush = [&]() {
-        const double nmt = fmax(mt, smt), nmd = fmax(md, smd);
-        st *= exp_nonpos(mt - nmt, tbl);  // 0 while mt is -inf (st is 0 then)
-        sd *= exp_nonpos(md - nmd, tbl);
-        mt = nmt;
-        md = nmd;
-#pragma unroll
-        for (int k = 0; k < 4 * kUnroll; ++k) {
-          st += exp_nonpos(xt[k] - mt, tbl);
-          sd += exp_nonpos(xd[k] - md, tbl);
-        }
-        smt = smd = -INFINITY;
-        cnt = 0;
-      };
-      sweep<true>(trow, drow, lo, hi, vec4, [&](float t, float d, int, bool ok) {
-        bad |= ok && (!isfinite(t) || !isfinite(d));
-        const double a = ok ? double(t) * invT : -INFINITY;
-        const double b = ok ? double(d) * invT : -INFINITY;
-        xt[cnt] = a;
-        xd[cnt] = b;
-        smt = fmax(smt, a);
-        smd = fmax(smd, b);
-        if (++cnt == 4 * kUnroll) flush();
-      });
-      if (cnt) {
-        for (int k = cnt; k < 4 * kUnroll; ++k) xt[k] = xd[k] = -INFINITY;
-        flush();
-      }
-      if (mt == -INFINITY) st = sd = 0.0;
-    }
+    slice_stats(trow, drow, lo, hi, vec4, invT, tbl, mt, st, md, sd, bad);
     if (bad) raise_status(p.status, TV_DEV_LOGITS);
     block_ms(mt, st, sh, tbl);
     block_ms(md, sd, sh, tbl);
@@ -550,16 +587,19 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleParams p) {
       put_partial(ms, 3, sd);
     }
     team_sync(tm);
+    gather_partials(tm, 4, s_part);
     double Mt = -INFINITY, Zt = 0.0, Md = -INFINITY, Zd = 0.0;
     for (int w = 0; w < p.W; ++w) {
-      const double* ms = member_slot(tm, w);
-      ms_combine(Mt, Zt, get_partial(ms, 0), get_partial(ms, 1), tbl);
-      ms_combine(Md, Zd, get_partial(ms, 2), get_partial(ms, 3), tbl);
+      Mt = fmax(Mt, s_part[4 * w]);
+      Md = fmax(Md, s_part[4 * w + 2]);
+    }
+    for (int w = 0; w < p.W; ++w) {  // fixed member order
+      if (s_part[4 * w] != -INFINITY) Zt += s_part[4 * w + 1] * exp_nonpos(s_part[4 * w] - Mt, tbl);
+      if (s_part[4 * w + 2] != -INFINITY) Zd += s_part[4 * w + 3] * exp_nonpos(s_part[4 * w + 2] - Md, tbl);
     }
     // Slice sums of p (for a draw at a leaf): s_w exp(m_w - Mt) / Zt.
     if (threadIdx.x < p.W) {
-      const double* ms = member_slot(tm, threadIdx.x);
-      const double m0 = get_partial(ms, 0), s0 = get_partial(ms, 1);
+      const double m0 = s_part[4 * threadIdx.x], s0 = s_part[4 * threadIdx.x + 1];
       s_slice[threadIdx.x] = m0 == -INFINITY ? 0.0 : s0 * exp_nonpos(m0 - Mt, tbl) / Zt;
     }
     tm.phase++;
@@ -597,12 +637,13 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleParams p) {
       part = block_sum(part, sh);
       if (threadIdx.x == 0) put_partial(member_slot(tm, member), 0, part);
       team_sync(tm);
+      gather_partials(tm, 1, s_part);
       double F = 0.0;
-      for (int w = 0; w < p.W; ++w) F += get_partial(member_slot(tm, w), 0);
+      for (int w = 0; w < p.W; ++w) F += s_part[w];
       if (F > 0.0) {
         R.a = Rn.a;
         B = F;
-        if (threadIdx.x < p.W) s_slice[threadIdx.x] = get_partial(member_slot(tm, threadIdx.x), 0);
+        if (threadIdx.x < p.W) s_slice[threadIdx.x] = s_part[threadIdx.x];
       }
       tm.phase++;
       S -= qx;
@@ -685,10 +726,10 @@ hipError_t launch_sample(const tv_sample_desc& d, const SamplePlan& pl, const Sa
     g_coop_blocks_per_cu = per;
     g_num_cus = prop.multiProcessorCount;
   }
-  // Team size: about two workgroups per CU across the batch, at most 8
-  // (a team lives on one XCD), and the padded grid must be resident.
+  // Team size: as many workgroups per request as stay resident (the
+  // launch is cooperative), at most kMaxTeam; a team lives on one XCD.
   const long resident = long(g_coop_blocks_per_cu) * g_num_cus;
-  int W = int(2L * g_num_cus / d.batch);
+  int W = int(resident / ((d.batch + 7) / 8 * 8));
   if (W > kMaxTeam) W = kMaxTeam;
   if (W < 1) W = 1;
   auto grid_for = [&](int w) { return long((d.batch + 7) / 8) * 8 * w; };
