@@ -16,6 +16,10 @@ LIB_NAME = "libtreeverify.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["tree_attn.hip", "tree_sample.hip", "tree_path.hip", "api.cpp"]
 ARCH = "gfx950"
+# Per-source extra flags. The attention kernels are scheduled for ILP (LDS
+# operand loads batched ahead of their MFMAs); their occupancy is fixed by
+# LDS, not registers.
+EXTRA_FLAGS = {"tree_attn.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 
 
 def hipcc():
@@ -42,7 +46,7 @@ def build(verbose=False):
 
     def compile_one(src):
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
-        cmd = [cc] + common_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc] + common_flags() + EXTRA_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".cpp"):
             cmd[1:1] = ["-x", "hip"]
         res = subprocess.run(cmd, capture_output=True, text=True)

@@ -31,6 +31,8 @@
 //    reaches the tree's own keys, and consulted only in those tiles.
 // fp32 path (small validation shapes): a VALU kernel, one workgroup per
 // (request, kv head, row block, key split), with the same partial format.
+#include <type_traits>
+
 #include "tv_device.hpp"
 #include "tv_internal.hpp"
 
@@ -41,8 +43,9 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kRowsPB = 128;     // rows per row block (bf16 path)
 constexpr int kStage = 64;       // keys per stage / tile (bf16 path)
-constexpr int kMaxWG = 512;      // persistent workgroups: 2 per CU on 256 CUs
+constexpr int kMaxWG = 256;      // persistent workgroups: one per CU on 256 CUs
 constexpr int kMinTilesPerWG = 2;
+constexpr size_t kLdsBytes = 160 * 1024;  // LDS per workgroup (gfx950)
 
 struct AttnParams {
   const void* q;
@@ -111,9 +114,28 @@ __device__ inline uint4 keep_first(uint4 v, int n) {
 // ---------------------------------------------------------------------------
 // Stream-K bookkeeping of the bf16 path.
 
-// Tiles of request r (all kv heads and row blocks); 0 for an empty or
+// Work is measured in cost units. A 64-key tile costs kCostSmall units when
+// its row block has at most four 16-row tiles and kCostBig when it has more
+// (one row tile per wave, twice the MFMA and softmax work of a split wave),
+// and each (request, kv head, row block) pair adds kCostPair units for the
+// set-up and hand-off of a segment. Shares are equal in units, so a
+// workgroup that crosses many short pairs, or streams many wide row blocks,
+// gets fewer tiles.
+constexpr int kCostSmall = 8;
+constexpr int kCostBig = 11;
+constexpr int kCostPair = 40;
+
+__device__ inline int tile_cost(int rows) { return rows > 64 ? kCostBig : kCostSmall; }
+
+// Units of one kv head of a request with R rows and nt tiles per pair.
+__device__ inline int head_units(int R, int nt) {
+  const int full = R / kRowsPB, rem = R - full * kRowsPB;
+  return full * (kCostPair + nt * kCostBig) + (rem > 0 ? kCostPair + nt * tile_cost(rem) : 0);
+}
+
+// Units of request r (all kv heads and row blocks); 0 for an empty or
 // rejected request (rejections are reported once, by `report`).
-__device__ inline int request_tiles(const AttnParams& p, int r, bool report) {
+__device__ inline int request_units(const AttnParams& p, int r, bool report) {
   const int nbeg = p.node_indptr[r];
   const int N = p.node_indptr[r + 1] - nbeg;
   const int P = p.prefix_len[r];
@@ -128,15 +150,34 @@ __device__ inline int request_tiles(const AttnParams& p, int r, bool report) {
     if (report) raise_status(p.status, TV_DEV_PAGES);
     return 0;
   }
-  return p.Hkv * ceil_div(N * p.G, kRowsPB) * ceil_div(L, kStage);
+  return p.Hkv * head_units(N * p.G, ceil_div(L, kStage));
 }
 
-// Share [a_w, b_w) of the T tiles given to logical workgroup w of n = 2^lg.
+// The pair of request r (first unit `base`, R rows, nt tiles per pair) that
+// holds unit x: kv head g, row block rb, first tile unit t0 (after the
+// pair's header), units per tile c.
+struct PairAt {
+  int g, rb, t0, c;
+};
+__device__ inline PairAt pair_at(int base, int x, int R, int nt) {
+  const int per_g = head_units(R, nt);
+  PairAt q;
+  q.g = (x - base) / per_g;
+  const int rem = x - base - q.g * per_g;
+  const int full = R / kRowsPB;
+  const int fu = kCostPair + nt * kCostBig;  // units of a full row block
+  q.rb = min(rem / fu, full);
+  q.t0 = base + q.g * per_g + q.rb * fu + kCostPair;
+  q.c = q.rb < full ? kCostBig : tile_cost(R - full * kRowsPB);
+  return q;
+}
+
+// Share [a_w, b_w) of the T units given to logical workgroup w of n = 2^lg.
 __device__ inline int share_begin(int T, int w, int lg) {
   return int((uint64_t(T) * uint32_t(w)) >> lg);
 }
 
-// Logical workgroup whose share contains tile x (x < T): the largest w with
+// Logical workgroup whose share contains unit x (x < T): the largest w with
 // share_begin(w) <= x.
 __device__ inline int share_of(int T, int x, int lg) {
   const int n = 1 << lg;
@@ -147,23 +188,31 @@ __device__ inline int share_of(int T, int x, int lg) {
   return w;
 }
 
-// Partial slot of logical workgroup w for a pair starting at tile ps: a
-// share holds at most two cut pairs, the one it starts inside (slot 2w) and
-// the one it ends inside (slot 2w+1).
-__device__ inline size_t cut_slot(int T, int w, int lg, int ps) {
-  return ps < share_begin(T, w, lg) ? size_t(2 * w) : size_t(2 * w + 1);
+// Tiles [lo, hi) of a pair (first tile unit t0, c units per tile, nt tiles)
+// whose first unit lies in the share [sa, sb): a tile belongs to the share
+// holding its first unit.
+__device__ inline int tiles_before(int x, int t0, int c, int nt) {
+  return x <= t0 ? 0 : min(nt, (x - t0 + c - 1) / c);
 }
 
-// Block-wide tile offsets of every request: off[r] = first tile of request
+// Partial slot of logical workgroup w for its part of a cut pair: a share
+// holds at most two cut pairs, one continued from earlier shares (its part
+// starts past tile 0; slot 2w) and one continued by later shares (slot 2w+1).
+__device__ inline size_t cut_slot(int w, int lo) {
+  return lo > 0 ? size_t(2 * w) : size_t(2 * w + 1);
+}
+
+// Block-wide unit offsets of every request: off[r] = first unit of request
 // r in the flat (request, kv head, row block, tile) order, off[B] = T.
-// Rejected requests (reported once when `report`) contribute no tiles.
-__device__ inline int scan_tiles(const AttnParams& p, int* off, int* s_scan, bool report) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int per = ceil_div(p.B, 256);
+// Rejected requests (reported once when `report`) contribute no units.
+// s_scan holds one int per wave of the block.
+__device__ inline int scan_units(const AttnParams& p, int* off, int* s_scan, bool report) {
+  const int nt = blockDim.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = ceil_div(p.B, nt);
   const int r0 = min(p.B, tid * per), r1 = min(p.B, r0 + per);
   int mine = 0;
   for (int r = r0; r < r1; ++r) {
-    const int t = request_tiles(p, r, report);
+    const int t = request_units(p, r, report);
     off[r] = t;
     mine += t;
   }
@@ -176,8 +225,7 @@ __device__ inline int scan_tiles(const AttnParams& p, int* off, int* s_scan, boo
   if (lane == 63) s_scan[wave] = inc;
   __syncthreads();
   int base = 0, total = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < (nt >> 6); ++w) {
     base += (w < wave) ? s_scan[w] : 0;
     total += s_scan[w];
   }
@@ -203,9 +251,10 @@ __device__ inline int request_of(const int* off, int B, int x) {
   return lo;
 }
 
-// Merge kernel: workgroup w merges the cut pair whose first inner share
-// boundary is a_w (a_{w-1} <= ps < a_w < pe), combining the partials of
-// every share that holds part of it, in share order (deterministic).
+// Merge kernel: workgroup w merges the cut pair whose first tile lies in
+// share w-1 and which has a tile in share w (a_{w-1} <= t0 < a_w <= the
+// first unit of its last tile), combining the partials of every share that
+// holds part of it, in share order (deterministic).
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   constexpr int D4 = D / 4;
@@ -216,7 +265,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   extern __shared__ int off[];  // [B + 1]
   const int w = blockIdx.x;
   if (w == 0) return;
-  const int T = scan_tiles(p, off, s_scan, false);
+  const int T = scan_units(p, off, s_scan, false);
   const int aw = share_begin(T, w, p.lg_nwg);
   if (aw >= T) return;
   const int r = request_of(off, p.B, aw);
@@ -224,27 +273,33 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   const int N = p.node_indptr[r + 1] - nbeg;
   const int L = p.prefix_len[r] + N;
   const int R = N * p.G;
-  const int nrb = ceil_div(R, kRowsPB);
   const int nt = ceil_div(L, kStage);
-  const int pir = (aw - off[r]) / nt;
-  const int ps = off[r] + pir * nt, pe = ps + nt;
-  if (!(ps < aw && share_begin(T, w - 1, p.lg_nwg) <= ps)) return;
-  const int g = pir / nrb;
-  const int row0 = (pir - g * nrb) * kRowsPB;
+  const PairAt q = pair_at(off[r], aw, R, nt);
+  const int t_last = q.t0 + (nt - 1) * q.c;  // first unit of the pair's last tile
+  if (!(share_begin(T, w - 1, p.lg_nwg) <= q.t0 && q.t0 < aw && aw <= t_last)) return;
+  const int g = q.g;
+  const int row0 = q.rb * kRowsPB;
   const int rows_here = min(kRowsPB, R - row0);
-  const int w0 = share_of(T, ps, p.lg_nwg), w1 = share_of(T, pe - 1, p.lg_nwg);
+  const int w0 = w - 1, w1 = share_of(T, t_last, p.lg_nwg);
+  // Share v holds tiles [lo_v, hi_v) of the pair; shares without any are skipped.
+  auto part = [&](int v, int& lo) {
+    lo = tiles_before(share_begin(T, v, p.lg_nwg), q.t0, q.c, nt);
+    return tiles_before(share_begin(T, v + 1, p.lg_nwg), q.t0, q.c, nt) > lo;
+  };
 
   for (int row = threadIdx.x; row < rows_here; row += blockDim.x) {
     float M = -INFINITY;
     for (int v = w0; v <= w1; ++v) {
-      if (share_begin(T, v + 1, p.lg_nwg) == share_begin(T, v, p.lg_nwg)) continue;
-      M = fmaxf(M, p.part_ml[(cut_slot(T, v, p.lg_nwg, ps) * kRowsPB + row) * 2]);
+      int lo;
+      if (!part(v, lo)) continue;
+      M = fmaxf(M, p.part_ml[(cut_slot(v, lo) * kRowsPB + row) * 2]);
     }
     float Ls = 0.f;
     if (M != -INFINITY) {
       for (int v = w0; v <= w1; ++v) {
-        if (share_begin(T, v + 1, p.lg_nwg) == share_begin(T, v, p.lg_nwg)) continue;
-        const float* ml = p.part_ml + (cut_slot(T, v, p.lg_nwg, ps) * kRowsPB + row) * 2;
+        int lo;
+        if (!part(v, lo)) continue;
+        const float* ml = p.part_ml + (cut_slot(v, lo) * kRowsPB + row) * 2;
         Ls += ml[1] * exp2f(ml[0] - M);
       }
     }
@@ -256,8 +311,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
 #pragma unroll
   for (int k = 0; k < IPT; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int v = w0; v <= w1; ++v) {
-    if (share_begin(T, v + 1, p.lg_nwg) == share_begin(T, v, p.lg_nwg)) continue;
-    const size_t slot = cut_slot(T, v, p.lg_nwg, ps);
+    int lo;
+    if (!part(v, lo)) continue;
+    const size_t slot = cut_slot(v, lo);
     float4 o[IPT];
     float m[IPT];
 #pragma unroll
@@ -295,25 +351,103 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA kernel: 256 threads = 4 waves x 32 rows; persistent over tiles.
+// bf16 MFMA kernel: one workgroup of 8 waves per CU, persistent over tiles.
+
+constexpr int kWavesS = 8;                // waves per workgroup
+constexpr int kThreadsS = 64 * kWavesS;   // threads per workgroup
+
+// LDS layout of a stage slot, unpadded, swizzled at 16-byte granularity:
+//  * K [64 keys][D]: row r keeps its chunk c at c ^ swz_k(r);
+//  * V^T page-major [4 pages][D][16 keys]: the two 8-key halves h of row d
+//    sit at 16-byte unit 2d + (h ^ swz_v(d)) of the page block.
+// The 16 lanes that read together in an MFMA operand load (K: rows differing
+// in bits 0, 1, 3 and 4; V^T: 16 consecutive rows, one half each) then hit
+// 16 distinct 16-byte bank groups (and 8 distinct ones per 8 lanes).
 template <int D>
-__global__ __launch_bounds__(256, 2) void attn_stream_kernel(AttnParams p) {
+__device__ inline int swz_k(int r) {
+  return D == 128 ? ((r & 3) | ((r >> 1) & 12)) : ((r & 3) | ((r >> 1) & 4));
+}
+__device__ inline int swz_v(int d) { return ((d >> 2) ^ (d >> 3)) & 1; }
+
+// NaN-propagating max (gfx950 v_maximum3_f32; no operand canonicalisation).
+__device__ inline float fmax_(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// Row max over a lane's group of four lanes (lanes l, l^16, l^32, l^48),
+// with gfx950's cross-row swaps (no LDS round trip).
+__device__ inline float max_across_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmax_(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmax_(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Wait until at most N vector-memory operations of this wave are pending
+// (s_waitcnt vmcnt(N); the other counters are left alone).
+template <int N>
+__device__ inline void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane i of the
+// wave writes lds_base + 16*i (lds_base must be wave-uniform).
+__device__ inline void load_lds16(const void* src, void* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+#endif
+}
+
+// Workgroup barrier without a memory fence: the waits that make the stage
+// data visible are explicit. The empty asm statements keep the compiler from
+// moving memory operations across it.
+__device__ inline void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int I, int N, class F>
+__device__ __attribute__((always_inline)) inline void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// Stage ring: NS slots of 64 keys, each K [64][D] then V^T [D][64] (bf16).
+// Loads go straight from HBM to LDS (global_load_lds_dwordx4), NS-1 stages
+// ahead of the one being computed; each slot is its own LDS object so the
+// compiler knows which pending loads a read depends on.
+// page_idx is p.page_indices again, declared __restrict__ so the per-stage
+// page-id loads can go through the scalar cache.
+template <int D, int NS>
+__global__ __launch_bounds__(kThreadsS, 1) void attn_stream_kernel(AttnParams p,
+                                                                   const int32_t* __restrict__ page_idx) {
   constexpr int KK = D / 32;          // 32-wide k-steps of the QK product
   constexpr int DT = D / 16;          // 16-wide d tiles of the PV product
-  constexpr int KS = D + 8;           // LDS row stride of K (bf16 elements)
-  constexpr int VS = kStage + 4;      // LDS row stride of V^T: 34 words, so the 8-byte operand
-                                      // reads of 16 (32) lanes hit distinct banks with 32 (64) banks
-  constexpr int PCH = 2 * D;          // 16-byte chunks per (page, head) block
-  constexpr int CPT = 4 * PCH / 256;  // chunks per thread per stage (K, and V)
-  constexpr int DB = D / 8;           // 16-byte chunks per K row
+  constexpr int NI = D / 32;          // 1 KB loads per wave per stage (K and V^T)
+  constexpr int KI = NI / 2;          // of which K
+  constexpr int KROWS = 512 / D;      // K rows per 1 KB load
+  constexpr int SLOT = 2 * kStage * D;
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kStage * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][D * VS];
-  __shared__ int s_scan[4];
+  __shared__ __attribute__((aligned(16))) uint16_t s0[SLOT];
+  __shared__ __attribute__((aligned(16))) uint16_t s1[SLOT];
+  __shared__ __attribute__((aligned(16))) uint16_t s2[NS > 2 ? SLOT : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t s3[NS > 3 ? SLOT : 8];
+  __shared__ float s_xol[4 * 16 * 2];
+  __shared__ int s_scan[kWavesS];
   extern __shared__ int dyn_lds[];
   int* off = dyn_lds;                                                 // [B + 1]
   int* par = dyn_lds + p.B + 1;                                       // [max_nodes]
   uint32_t* anc = reinterpret_cast<uint32_t*>(par + p.max_nodes);     // [nn][words]
+
+  auto slot = [&](auto j_c) __attribute__((always_inline)) -> uint16_t* {
+    constexpr int J = decltype(j_c)::value % NS;
+    if constexpr (J == 0) return s0;
+    else if constexpr (J == 1) return s1;
+    else if constexpr (J == 2) return s2;
+    else return s3;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -322,339 +456,330 @@ __global__ __launch_bounds__(256, 2) void attn_stream_kernel(AttnParams p) {
   const int lg = lane >> 4;
   const int lw = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
 
-  const int T = scan_tiles(p, off, s_scan, lw == 0);
+  const int T = scan_units(p, off, s_scan, lw == 0);
   const int a = share_begin(T, lw, p.lg_nwg);
   const int b = share_begin(T, lw + 1, p.lg_nwg);
   if (a >= b) return;
 
-  int r = request_of(off, p.B, a);  // request holding tile a
+  int r = request_of(off, p.B, a);  // request holding unit a
 
   const uint16_t* qb = static_cast<const uint16_t*>(p.q);
   const uint16_t* kp = static_cast<const uint16_t*>(p.k_pages);
   const uint16_t* vp = static_cast<const uint16_t*>(p.v_pages);
   const size_t head_block = size_t(kPage) * D;  // elements per (page, head)
 
-  int c = a;
+  // Operand addresses (elements) inside one slot. In the QK product block h
+  // of 32-key half kt2 feeds lane row l16 with stage key kt2*32 + 4h + krow,
+  // krow = 8*(l16/4) + l16%4, so the S^T accumulator of lane group lg holds
+  // keys kt2*32 + 8lg + 4h + e (e < 4): eight consecutive keys, which are
+  // exactly the keys the PV operand of lane group lg takes from one 16-byte
+  // V^T chunk.
+  const int krow = 8 * (l16 >> 2) + (l16 & 3);
+  int kaddr[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) kaddr[kk] = krow * D + (((kk * 4 + lg) ^ swz_k<D>(krow)) * 8);
+  // V^T operand of lane group lg in half kt2: keys 8lg..8lg+7 of the half,
+  // i.e. page 2*kt2 + lg/2, 8-key half lg&1, row d = 16*dt + l16 (the
+  // swizzle depends on d's bits 2 and 3 only, so on l16).
+  const int vaddr = kStage * D + (lg >> 1) * (D * kPage) + 16 * l16 + 8 * ((lg & 1) ^ swz_v(l16));
+
+  // Stage loads of this wave, each 1 KB and inside one (page, head) block:
+  // K rows 8*wave .. 8*wave+7 (page wave/2 of the stage), and V^T rows
+  // 32*(q % (D/32)) .. +31 of page q / (D/32), q = KI*wave + j. Lane offsets
+  // inside a block are fixed; only the page ids change.
+  constexpr int VPI = D / 32;  // 1 KB loads per V^T page block
+  int k_off[KI], v_off[KI];
+#pragma unroll
+  for (int j = 0; j < KI; ++j) {
+    const int kr = 8 * wave + j * KROWS + lane / (D / 8);
+    k_off[j] = (kr & 15) * D + (((lane % (D / 8)) ^ swz_k<D>(kr)) * 8);
+    const int q = KI * wave + j;
+    const int d = 32 * (q % VPI) + (lane >> 1);
+    v_off[j] = d * kPage + 8 * ((lane & 1) ^ swz_v(d));
+  }
+
+  int c = a;  // unit cursor
   while (c < b) {
     while (off[r + 1] <= c) ++r;
+    r = __builtin_amdgcn_readfirstlane(r);
     const int nbeg = p.node_indptr[r];
     const int N = p.node_indptr[r + 1] - nbeg;
     const int P = p.prefix_len[r];
     const int L = P + N;
     const int R = N * p.G;
-    const int nrb = ceil_div(R, kRowsPB);
     const int nt = ceil_div(L, kStage);
-    const int local = c - off[r];
-    const int pir = local / nt;
-    const int g = pir / nrb;
-    const int rb = pir - g * nrb;
-    const int ps = off[r] + pir * nt;  // pair's first tile
-    const int pe = ps + nt;            // pair's end tile
-    const int seg_end = min(b, pe);
-    const int tlo = c - ps, thi = seg_end - ps;
-    const bool whole = ps >= a && pe <= b;
-    const int row0 = rb * kRowsPB;
+    const PairAt q = pair_at(__builtin_amdgcn_readfirstlane(off[r]), c, R, nt);
+    c = q.t0 + nt * q.c;  // next pair
+    // This share's tiles of the pair.
+    const int tlo = tiles_before(a, q.t0, q.c, nt);
+    const int thi = tiles_before(b, q.t0, q.c, nt);
+    if (tlo >= thi) continue;
+    const int g = q.g;
+    const bool whole = tlo == 0 && thi == nt;
+    const int row0 = q.rb * kRowsPB;
     const int rows_here = min(kRowsPB, R - row0);
     const int pbase = p.page_indptr[r];
+    const int pend = p.page_indptr[r + 1] - 1;  // last listed page (>= pbase)
     const int words = ceil_div(N, 32);
     const int first_node = row0 / p.G;
     const int nn_blk = (row0 + rows_here - 1) / p.G - first_node + 1;
-    c = seg_end;
 
-    __syncthreads();  // LDS of the previous segment is no longer read
-    if (thi * kStage > P) build_anc(p, nbeg, N, first_node, nn_blk, words, anc, par);
+    stage_barrier();  // every wave is done with the LDS of the previous segment
 
     // Wave roles. Row tile t holds block rows 16t..16t+15. With five or
-    // more row tiles each wave takes two (rtA, rtB) and every key; with
-    // three or four, one each; with one or two row tiles the waves also
-    // split the 64 keys of a stage into 32-key halves (hmask), and the two
-    // halves of a row tile are merged through LDS at the end of the segment.
+    // more row tiles each wave takes one and every key of a stage (NH = 2
+    // halves); with four or fewer, waves w and w+4 take row tile w and the
+    // 32-key halves 0 and 1 of each stage (NH = 1), merged through LDS at
+    // the end of the segment.
     const int nrt = ceil_div(rows_here, 16);
-    int rtA, rtB, hmask;
-    if (nrt >= 5) {
-      rtA = 2 * wave < nrt ? 2 * wave : -1;
-      rtB = 2 * wave + 1 < nrt ? 2 * wave + 1 : -1;
-      hmask = 3;
-    } else if (nrt >= 3) {
-      rtA = wave < nrt ? wave : -1;
-      rtB = -1;
-      hmask = 3;
-    } else if (nrt == 2) {
-      rtA = wave & 1;
-      rtB = -1;
-      hmask = 1 << (wave >> 1);
+    const bool ksplit = nrt <= 4;
+    const int rt0 = ksplit ? (wave & 3) : wave;
+    const int rt = rt0 < nrt ? rt0 : -1;
+    const int half = ksplit ? (wave >> 2) : 0;
+    bool active = rt >= 0;
+    const int row = rt * 16 + l16;  // block-local row of this lane
+
+    bf16x8 qf[KK];
+    if (active && row < rows_here) {
+      const uint16_t* src = qb + qo_offset(p, nbeg, g, row0 + row, D) + lg * 8;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(src + kk * 32);
     } else {
-      rtA = wave < 2 ? 0 : -1;
-      rtB = -1;
-      hmask = 1 << (wave & 1);
-    }
-    const bool ksplit = nrt <= 2;
-    bool active = rtA >= 0;
-    const bool two = rtB >= 0;
-    const int rowA = rtA * 16 + l16;  // block-local rows of this lane
-    const int rowB = rtB * 16 + l16;
-
-    bf16x8 qf[2][KK];
 #pragma unroll
-    for (int w2 = 0; w2 < 2; ++w2) {
-      const int row = w2 == 0 ? rowA : rowB;
-      const bool ok = (w2 == 0 ? rtA >= 0 : two) && row < rows_here;
-      if (ok) {
-        const uint16_t* src = qb + qo_offset(p, nbeg, g, row0 + row, D) + lg * 8;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) qf[w2][kk] = *reinterpret_cast<const bf16x8*>(src + kk * 32);
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) qf[w2][kk] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      }
+      for (int kk = 0; kk < KK; ++kk) qf[kk] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
 
-    // Stage loads: thread chunk j covers 16 bytes of page (j*256+tid)/PCH of
-    // the stage, at the same offset in its K and its V^T block. Loads never
-    // branch: a page past the sequence is read from page 0 and, like slots
-    // past the sequence in the last page, zeroed when it is committed to LDS.
-    const int pend = p.page_indptr[r + 1] - 1;  // last listed page (>= pbase)
-    uint4 kreg[CPT], vreg[CPT];
-    int ids[4];         // raw page ids of the next stage to issue (unchecked)
+    // Every load of a wave lies in page wave/2 of its stage (K rows 8*wave..
+    // 8*wave+7, and V^T blocks KI*wave .. KI*wave+KI-1 of D/32 per page), so
+    // a wave needs one page id per stage, a scalar. A page past the sequence
+    // is read from page 0; its slots, like slots past the sequence in the
+    // last page, are zeroed in LDS before use. Ids outside the pool are
+    // reported and also replaced by page 0.
+    const int wpg = wave >> 1;
     bool bad_page = false;
-    auto page_ids = [&](int tile) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        ids[j] = p.page_indices[min(pbase + ((tile * kStage + j * kPage) >> 4), pend)];
+    auto load_id = [&](int tile) __attribute__((always_inline)) -> int {
+      const int x = page_idx[min(pbase + tile * 4 + wpg, pend)];
+      const bool live = tile < thi && tile * kStage + wpg * kPage < L;
+      const bool in_pool = unsigned(x) < unsigned(p.num_pages);
+      bad_page |= live && !in_pool;
+      return (live && in_pool) ? x : 0;
     };
-    auto issue = [&](int tile) {
+    // Each load is a scalar block address plus the lane's fixed offset.
+    // Stages past the segment are issued as dummies (every lane reads the
+    // same 16 bytes of page 0, and the slot is never read), so every step
+    // waits for the same number of loads.
+    auto issue = [&](uint16_t* sb, int id, bool live) __attribute__((always_inline)) {
+      const size_t blk = (size_t(id) * p.Hkv + g) * head_block;
 #pragma unroll
-      for (int j = 0; j < CPT; ++j) {
-        const int cidx = tid + 256 * j;
-        const int pg = cidx / PCH;
-        const int o = cidx - pg * PCH;
-        int id = pg == 0 ? ids[0] : pg == 1 ? ids[1] : pg == 2 ? ids[2] : ids[3];
-        const bool live = tile * kStage + pg * kPage < L;
-        const bool in_pool = unsigned(id) < unsigned(p.num_pages);
-        bad_page |= live && !in_pool;
-        id = (live && in_pool) ? id : 0;
-        const size_t blk = (size_t(id) * p.Hkv + g) * head_block + size_t(o) * 8;
-        kreg[j] = *reinterpret_cast<const uint4*>(kp + blk);
-        vreg[j] = *reinterpret_cast<const uint4*>(vp + blk);
+      for (int j = 0; j < KI; ++j)
+        load_lds16(kp + blk + (live ? k_off[j] : 0), sb + (8 * wave + j * KROWS) * D);
+#pragma unroll
+      for (int j = 0; j < KI; ++j) {
+        const int q = KI * wave + j;
+        load_lds16(vp + blk + (live ? v_off[j] : 0), sb + kStage * D + wpg * (D * kPage) + (q % VPI) * 512);
       }
     };
-    auto commit = [&](int buf, int tile) {
-      const int tail = L - tile * kStage;  // keys of this tile inside the sequence
-#pragma unroll
-      for (int j = 0; j < CPT; ++j) {
-        const int cidx = tid + 256 * j;
-        const int pg = cidx / PCH;
-        const int o = cidx - pg * PCH;
-        const int kip = o / DB;
-        uint4 kv = kreg[j], vv = vreg[j];
-        if (tail < kStage) {
-          kv = pg * kPage + kip < tail ? kv : make_uint4(0, 0, 0, 0);
-          vv = keep_first(vv, tail - (pg * kPage + (o & 1) * 8));
+    // Zero V^T keys >= tail of a slot (the sequence ends inside the stage).
+    auto zero_tail = [&](uint16_t* sb, int tail) __attribute__((always_inline)) {
+      for (int i = tid; i < D * 8; i += kThreadsS) {
+        const int d = i >> 3, lc = i & 7;  // key chunk lc: page lc/2, half lc&1
+        if (lc * 8 + 8 > tail) {
+          uint4* ptr = reinterpret_cast<uint4*>(sb + kStage * D + (lc >> 1) * (D * kPage) + 16 * d +
+                                                8 * ((lc & 1) ^ swz_v(d)));
+          *ptr = keep_first(*ptr, tail - lc * 8);
         }
-        *reinterpret_cast<uint4*>(&k_lds[buf][(pg * kPage + kip) * KS + (o - kip * DB) * 8]) = kv;
-        uint2* vdst = reinterpret_cast<uint2*>(&v_lds[buf][(o >> 1) * VS + pg * kPage + (o & 1) * 8]);
-        vdst[0] = make_uint2(vv.x, vv.y);  // rows are 8-byte aligned only
-        vdst[1] = make_uint2(vv.z, vv.w);
       }
     };
 
-    // Online softmax state per row (w2 = 0: rtA, 1: rtB). Scores stay raw
-    // dot products; the exponent is exp2(c*s - off) with c = scale*log2(e)
-    // and off = c*m_ref. The reference m_ref is raised only when a new raw
-    // max exceeds it by more than kLazy/c (then acc and l are rescaled), so
-    // p <= 2^kLazy and most tiles skip the rescale.
+    // Online softmax state of the lane's row. Scores stay raw dot products;
+    // the exponent is exp2(c*s - off) with c = scale*log2(e) and off =
+    // c*m_ref. The reference m_ref is raised only when a new raw max exceeds
+    // it by more than kLazy/c (then acc and l are rescaled), so p <= 2^kLazy
+    // and most tiles skip the rescale. Whether any row must raise is decided
+    // from each lane's own eight scores (the row max passes the threshold iff
+    // one of its lanes' maxima does), so the cross-lane row max is formed
+    // only on the tiles that raise.
     constexpr float kLazy = 8.f;
-    const float c = p.scale_log2;
-    float m_ref[2] = {-INFINITY, -INFINITY};
-    float off_[2] = {0.f, 0.f};
-    float l_run[2] = {0.f, 0.f};
-    f32x4 acc[DT][2];
+    const float cs = p.scale_log2;
+    float m_ref = -INFINITY, off_ = 0.f, l_run = 0.f;
+    f32x4 acc[DT];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      acc[dt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-      acc[dt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    page_ids(tlo);
-    issue(tlo);
-    if (tlo + 1 < thi) page_ids(tlo + 1);
-    commit(0, tlo);
-    if (tlo + 1 < thi) {
-      issue(tlo + 1);
-      if (tlo + 2 < thi) page_ids(tlo + 2);
-    }
-    __syncthreads();
-    int buf = 0;
-    for (int tile = tlo; tile < thi; ++tile) {
+    // One stage of a row tile: NH = 2 computes both 32-key halves, NH = 1
+    // the wave's own half.
+    auto compute = [&](const uint16_t* sb, int tile, auto nh_c) __attribute__((always_inline)) {
+      constexpr int NH = decltype(nh_c)::value;
       const int t0 = tile * kStage;
-      if (active) {
 #pragma unroll
-        for (int kt2 = 0; kt2 < 2; ++kt2) {
-          if (!((hmask >> kt2) & 1)) continue;
-          f32x4 s[2][2];  // [16-key half][w2]
+      for (int hh = 0; hh < NH; ++hh) {
+        const int kt2 = NH == 2 ? hh : half;
+        f32x4 s[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          s[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) {
+            const bf16x8 ka = *reinterpret_cast<const bf16x8*>(sb + (kt2 * 32 + 4 * h) * D + kaddr[kk]);
+            s[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[kk], s[h], 0, 0, 0);
+          }
+        }
+        const int k0 = t0 + kt2 * 32;
+        if (k0 + 32 > P) {
+          // Tree or tail keys: prefix keys stay visible; tree key P+j needs
+          // bit j of the row's ancestor bitset; keys >= L are hidden. The
+          // 64-bit window of bitset words starting at wa covers every j the
+          // lane tests (tree indices below 0 read as ones).
+          const int jlo = k0 - P;
+          const int wa = jlo >= 0 ? (jlo >> 5) : -1;
+          const int jb = jlo - 32 * wa;
+          const int nl = min((row0 + row) / p.G - first_node, nn_blk - 1);
+          const uint32_t* arow = anc + nl * words;
+          const uint32_t lo_w = arow[min(max(wa, 0), words - 1)];
+          const uint32_t hi_w = arow[min(wa + 1, words - 1)];
+          const uint32_t lo = wa < 0 ? ~0u : (wa < words ? lo_w : 0u);
+          const uint32_t hi = wa + 1 < words ? hi_w : 0u;
+          const uint64_t win = uint64_t(lo) | (uint64_t(hi) << 32);
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            s[h][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-            s[h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const uint16_t* krow = &k_lds[buf][((2 * kt2 + h) * 16 + l16) * KS + lg * 8];
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-              const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + kk * 32);
-              s[h][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[0][kk], s[h][0], 0, 0, 0);
-              if (two)
-                s[h][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[1][kk], s[h][1], 0, 0, 0);
+            for (int e = 0; e < 4; ++e) {
+              const int dk = lg * 8 + h * 4 + e;
+              const bool vis = (k0 + dk < L) & (row < rows_here) & (((win >> (jb + dk)) & 1u) != 0);
+              s[h][e] = vis ? s[h][e] : -INFINITY;
             }
-          }
-          const int k0 = t0 + kt2 * 32;
-          if (k0 + 32 > P) {
-            // Tree or tail keys: prefix keys stay visible; tree key P+j needs
-            // bit j of the row's ancestor bitset; keys >= L are hidden. The
-            // 64-bit window of bitset words starting at wa covers every j the
-            // lane tests (tree indices below 0 read as ones).
-            const int jlo = k0 - P;
-            const int wa = jlo >= 0 ? (jlo >> 5) : -1;
-            const int jb = jlo - 32 * wa;
-#pragma unroll
-            for (int w2 = 0; w2 < 2; ++w2) {
-              if (w2 == 1 && !two) continue;
-              const int row = w2 == 0 ? rowA : rowB;
-              const int nl = min((row0 + row) / p.G - first_node, nn_blk - 1);
-              const uint32_t* arow = anc + nl * words;
-              const uint32_t lo_w = arow[min(max(wa, 0), words - 1)];
-              const uint32_t hi_w = arow[min(wa + 1, words - 1)];
-              const uint32_t lo = wa < 0 ? ~0u : (wa < words ? lo_w : 0u);
-              const uint32_t hi = wa + 1 < words ? hi_w : 0u;
-              const uint64_t win = uint64_t(lo) | (uint64_t(hi) << 32);
-#pragma unroll
-              for (int h = 0; h < 2; ++h) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  const int dk = h * 16 + lg * 4 + e;
-                  const bool vis = (k0 + dk < L) & (row < rows_here) &
-                                   (((win >> (jb + dk)) & 1u) != 0);
-                  s[h][w2][e] = vis ? s[h][w2][e] : -INFINITY;
-                }
-              }
-            }
-          }
-          bf16x8 pb[2];
-#pragma unroll
-          for (int w2 = 0; w2 < 2; ++w2) {
-            if (w2 == 1 && !two) continue;
-            float mt = fmaxf(fmaxf(fmaxf(s[0][w2][0], s[0][w2][1]), fmaxf(s[0][w2][2], s[0][w2][3])),
-                             fmaxf(fmaxf(s[1][w2][0], s[1][w2][1]), fmaxf(s[1][w2][2], s[1][w2][3])));
-            mt = fmaxf(mt, shfl_xor(mt, 16));
-            mt = fmaxf(mt, shfl_xor(mt, 32));
-            // Raise the reference when the row max passed it by > kLazy/c.
-            const bool raise = mt > m_ref[w2] && (m_ref[w2] == -INFINITY || c * (mt - m_ref[w2]) > kLazy);
-            if (__builtin_amdgcn_ballot_w64(raise)) {
-              const float m_new = raise ? mt : m_ref[w2];
-              const float off_new = m_new == -INFINITY ? 0.f : c * m_new;
-              const float alpha = m_ref[w2] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(off_[w2] - off_new);
-              m_ref[w2] = m_new;
-              off_[w2] = off_new;
-              l_run[w2] *= alpha;
-#pragma unroll
-              for (int dt = 0; dt < DT; ++dt) acc[dt][w2] *= alpha;
-            }
-            float ls = 0.f;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float pv = __builtin_amdgcn_exp2f(fmaf(s[h][w2][e], c, -off_[w2]));
-                ls += pv;
-                pb[w2][4 * h + e] = static_cast<__bf16>(pv);
-              }
-            }
-            l_run[w2] += ls;
-          }
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const uint16_t* vrow = &v_lds[buf][(dt * 16 + l16) * VS + kt2 * 32 + lg * 4];
-            const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-            const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
-            const uint4 w4 = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            const bf16x8 va = __builtin_bit_cast(bf16x8, w4);
-            acc[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[0], acc[dt][0], 0, 0, 0);
-            if (two)
-              acc[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[1], acc[dt][1], 0, 0, 0);
           }
         }
-      }
-      if (tile + 1 < thi) {
-        commit(buf ^ 1, tile + 1);
-        if (tile + 2 < thi) {
-          issue(tile + 2);
-          if (tile + 3 < thi) page_ids(tile + 3);
+        const float mloc = fmax_(fmax_(fmax_(s[0][0], s[0][1]), fmax_(s[0][2], s[0][3])),
+                                 fmax_(fmax_(s[1][0], s[1][1]), fmax_(s[1][2], s[1][3])));
+        const bool need = (mloc > m_ref) & ((m_ref == -INFINITY) | (cs * (mloc - m_ref) > kLazy));
+        if (__builtin_amdgcn_ballot_w64(need)) {
+          const float mt = max_across_groups(mloc);
+          const bool raise = (mt > m_ref) & ((m_ref == -INFINITY) | (cs * (mt - m_ref) > kLazy));
+          const float m_new = raise ? mt : m_ref;
+          const float off_new = m_new == -INFINITY ? 0.f : cs * m_new;
+          const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(off_ - off_new);
+          m_ref = m_new;
+          off_ = off_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+        }
+        bf16x8 pb;
+        float ls = 0.f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float pv = __builtin_amdgcn_exp2f(fmaf(s[h][e], cs, -off_));
+            ls += pv;
+            pb[4 * h + e] = static_cast<__bf16>(pv);
+          }
+        }
+        l_run += ls;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const bf16x8 va = *reinterpret_cast<const bf16x8*>(sb + kt2 * (2 * D * kPage) + dt * 256 + vaddr);
+          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, acc[dt], 0, 0, 0);
         }
       }
+    };
+
+    // Prologue: stages tlo .. tlo+NS-2 in flight.
+    static_for<0, NS - 1>([&](auto j_c) __attribute__((always_inline)) {
+      constexpr int J = decltype(j_c)::value;
+      issue(slot(j_c), load_id(tlo + J), tlo + J < thi);
+    });
+    int idn = load_id(tlo + NS - 1);  // page id of the next stage to issue
+
+    // The ancestor bitsets are built while the first stages load.
+    if (thi * kStage > P) {
+      build_anc(p, nbeg, N, first_node, nn_blk, words, anc, par);
       __syncthreads();
-      buf ^= 1;
     }
+
+    // Step i (stage i in slot J = (i - tlo) % NS): wait for this wave's
+    // loads of stage i (NS-2 later stages stay pending), barrier (every
+    // wave's loads landed; every wave is done with the slot of stage i-1),
+    // issue stage i+NS-1 into that slot, compute stage i.
+    auto step = [&](int i, auto j_c, auto nh_c) __attribute__((always_inline)) {
+      constexpr int J = decltype(j_c)::value;
+      wait_vm<(NS - 2) * NI>();
+      stage_barrier();
+      issue(slot(std::integral_constant<int, J + NS - 1>{}), idn, i + NS - 1 < thi);
+      if (i == nt - 1 && (L & (kStage - 1)) != 0) {
+        zero_tail(slot(j_c), L - i * kStage);
+        __syncthreads();
+      }
+      if (active) compute(slot(j_c), i, nh_c);
+      idn = load_id(i + NS);
+    };
+    // Unrolled NS times so every slot is a compile-time object; the last
+    // thi - i < NS stages run straight-line.
+    auto run = [&](auto nh_c) __attribute__((always_inline)) {
+      int i = tlo;
+      for (; i + NS <= thi; i += NS)
+        static_for<0, NS>([&](auto j_c) __attribute__((always_inline)) {
+          step(i + decltype(j_c)::value, j_c, nh_c);
+        });
+      static_for<0, NS - 1>([&](auto j_c) __attribute__((always_inline)) {
+        if (i + decltype(j_c)::value < thi) step(i + decltype(j_c)::value, j_c, nh_c);
+      });
+    };
+    if (ksplit)
+      run(std::integral_constant<int, 1>{});
+    else
+      run(std::integral_constant<int, 2>{});
+    wait_vm<0>();  // the dummy stages have landed before the slots are reused
     if (bad_page) raise_status(p.status, TV_DEV_PAGES);
 
     // Row sums: the four lane groups of a row hold disjoint key subsets.
-#pragma unroll
-    for (int w2 = 0; w2 < 2; ++w2) {
-      float l = l_run[w2];
-      l += shfl_xor(l, 16);
-      l += shfl_xor(l, 32);
-      l_run[w2] = l;
-    }
+    l_run += shfl_xor(l_run, 16);
+    l_run += shfl_xor(l_run, 32);
 
-    // Key-split waves: the second-half wave of a row tile hands (off, l, acc)
-    // to the first-half wave through LDS (the stage buffers are free now).
+    // Key-split waves: the half-1 wave of a row tile hands (off, l, acc) to
+    // the half-0 wave through LDS (slot 0; every stage load has landed).
     if (ksplit) {
-      float* xacc = reinterpret_cast<float*>(&k_lds[0][0]);  // [2 row tiles][16][D]
-      float* xol = xacc + 2 * 16 * D;                        // [2][16][2]
-      if (active && hmask == 2) {
-        float* dst = xacc + (rtA * 16 + l16) * D + lg * 4;
+      __syncthreads();
+      float* xacc = reinterpret_cast<float*>(s0);  // [4 row tiles][16][D]
+      if (active && half == 1) {
+        float* dst = xacc + (rt * 16 + l16) * D + lg * 4;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          *reinterpret_cast<f32x4*>(dst + dt * 16) = acc[dt][0];
+        for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(dst + dt * 16) = acc[dt];
         if (lg == 0) {
-          xol[(rtA * 16 + l16) * 2] = off_[0] + (m_ref[0] == -INFINITY ? -INFINITY : 0.f);
-          xol[(rtA * 16 + l16) * 2 + 1] = l_run[0];
+          s_xol[(rt * 16 + l16) * 2] = off_ + (m_ref == -INFINITY ? -INFINITY : 0.f);
+          s_xol[(rt * 16 + l16) * 2 + 1] = l_run;
         }
       }
       __syncthreads();
-      if (active && hmask == 1) {
-        const float* src = xacc + (rtA * 16 + l16) * D + lg * 4;
-        const float o2 = xol[(rtA * 16 + l16) * 2];
-        const float l2 = xol[(rtA * 16 + l16) * 2 + 1];
-        const float o1 = m_ref[0] == -INFINITY ? -INFINITY : off_[0];
+      if (active && half == 0) {
+        const float* src = xacc + (rt * 16 + l16) * D + lg * 4;
+        const float o2 = s_xol[(rt * 16 + l16) * 2];
+        const float l2 = s_xol[(rt * 16 + l16) * 2 + 1];
+        const float o1 = m_ref == -INFINITY ? -INFINITY : off_;
         const float om = fmaxf(o1, o2);
         const float a1 = o1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(o1 - om);
         const float a2 = o2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(o2 - om);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-          acc[dt][0] = acc[dt][0] * a1 + *reinterpret_cast<const f32x4*>(src + dt * 16) * a2;
-        l_run[0] = l_run[0] * a1 + l2 * a2;
-        off_[0] = om == -INFINITY ? 0.f : om;
-        m_ref[0] = om;  // only its -inf-ness is used below
+          acc[dt] = acc[dt] * a1 + *reinterpret_cast<const f32x4*>(src + dt * 16) * a2;
+        l_run = l_run * a1 + l2 * a2;
+        off_ = om == -INFINITY ? 0.f : om;
+        m_ref = om;  // only its -inf-ness is used below
       }
-      active = active && hmask == 1;
+      active = active && half == 0;
     }
 
     if (whole) {
-      if (active) {
+      if (active && row < rows_here) {
+        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+        uint16_t* dst = static_cast<uint16_t*>(p.out) + qo_offset(p, nbeg, g, row0 + row, D) + lg * 4;
 #pragma unroll
-        for (int w2 = 0; w2 < 2; ++w2) {
-          if (w2 == 1 && !two) continue;
-          const int row = w2 == 0 ? rowA : rowB;
-          if (row < rows_here) {
-            const float inv = l_run[w2] > 0.f ? 1.f / l_run[w2] : 0.f;
-            uint16_t* dst =
-                static_cast<uint16_t*>(p.out) + qo_offset(p, nbeg, g, row0 + row, D) + lg * 4;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-              uint2 pk;
-              pk.x = pack_bf16x2(acc[dt][w2][0] * inv, acc[dt][w2][1] * inv);
-              pk.y = pack_bf16x2(acc[dt][w2][2] * inv, acc[dt][w2][3] * inv);
-              *reinterpret_cast<uint2*>(dst + dt * 16) = pk;
-            }
-          }
+        for (int dt = 0; dt < DT; ++dt) {
+          uint2 pk;
+          pk.x = pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv);
+          pk.y = pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv);
+          *reinterpret_cast<uint2*>(dst + dt * 16) = pk;
         }
       }
       continue;
@@ -662,23 +787,15 @@ __global__ __launch_bounds__(256, 2) void attn_stream_kernel(AttnParams p) {
 
     // Cut pair: publish (offset, l, acc) of this share's part of it; the
     // offset is in log2 units (-inf when no key was visible).
-    const size_t slot = cut_slot(T, lw, p.lg_nwg, ps);
-    if (active) {
+    const size_t slot_id = cut_slot(lw, tlo);
+    if (active && row < rows_here) {
+      const size_t base = slot_id * kRowsPB + row;
+      float* dst = p.part_o + base * D + lg * 4;
 #pragma unroll
-      for (int w2 = 0; w2 < 2; ++w2) {
-        if (w2 == 1 && !two) continue;
-        const int row = w2 == 0 ? rowA : rowB;
-        if (row < rows_here) {
-          const size_t base = slot * kRowsPB + row;
-          float* dst = p.part_o + base * D + lg * 4;
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-            *reinterpret_cast<f32x4*>(dst + dt * 16) = acc[dt][w2];
-          if (lg == 0) {
-            p.part_ml[base * 2] = m_ref[w2] == -INFINITY ? -INFINITY : off_[w2];
-            p.part_ml[base * 2 + 1] = l_run[w2];
-          }
-        }
+      for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(dst + dt * 16) = acc[dt];
+      if (lg == 0) {
+        p.part_ml[base * 2] = m_ref == -INFINITY ? -INFINITY : off_;
+        p.part_ml[base * 2 + 1] = l_run;
       }
     }
   }
@@ -933,7 +1050,7 @@ bool plan_attn(const tv_attn_desc& d, AttnPlan* out) {
   if (pl.mfma) {
     if (d.batch > 4096) return false;  // tile offsets live in LDS
     const long long tiles = pairs * ((d.max_kv_len + kStage - 1) / kStage);
-    if (tiles > 0x7fffffffLL) return false;
+    if (tiles * kCostBig + pairs * kCostPair > 0x7fffffffLL) return false;  // units fit an int
     // A power of two (>= 8, the XCD count) so share bounds are shifts.
     long long want = (tiles + kMinTilesPerWG - 1) / kMinTilesPerWG;
     if (want > kMaxWG) want = kMaxWG;
@@ -950,6 +1067,12 @@ bool plan_attn(const tv_attn_desc& d, AttnPlan* out) {
     const int nn_max = kRowsPB / pl.group + 2;
     pl.dyn_lds = size_t(d.batch + 1 + d.max_nodes) * sizeof(int) +
                  size_t(nn_max) * pl.words * sizeof(uint32_t);
+    // Stage ring depth: four 64-key slots when they fit next to the
+    // dynamic arrays in the 160 KB of LDS, else two.
+    const size_t slot_bytes = size_t(2) * kStage * d.head_dim * sizeof(uint16_t);
+    const size_t fixed = 4 * 16 * 2 * sizeof(float) + kWavesS * sizeof(int);
+    pl.ns = (4 * slot_bytes + fixed + pl.dyn_lds <= kLdsBytes) ? 4 : 2;
+    if (2 * slot_bytes + fixed + pl.dyn_lds > kLdsBytes) return false;
   } else {
     const long long target_items = 1024;
     long long chunk = ((long long)d.max_kv_len * pairs + target_items - 1) / target_items;
@@ -1013,11 +1136,18 @@ hipError_t launch_attn(const tv_attn_desc& d, const AttnPlan& pl, const AttnArgs
     // Streaming pass (whole pairs written, cut pairs left as partials), then
     // the merge of the cut pairs; the kernel boundary orders the two.
     const size_t merge_lds = size_t(d.batch + 1) * sizeof(int);
+    const dim3 sblock(kThreadsS);
     if (d.head_dim == 128) {
-      hipLaunchKernelGGL(attn_stream_kernel<128>, grid, block, lds, stream, p);
+      if (pl.ns == 4)
+        attn_stream_kernel<128, 4><<<grid, sblock, lds, stream>>>(p, a.page_indices);
+      else
+        attn_stream_kernel<128, 2><<<grid, sblock, lds, stream>>>(p, a.page_indices);
       hipLaunchKernelGGL(attn_merge_kernel<128>, grid, block, merge_lds, stream, p);
     } else {
-      hipLaunchKernelGGL(attn_stream_kernel<64>, grid, block, lds, stream, p);
+      if (pl.ns == 4)
+        attn_stream_kernel<64, 4><<<grid, sblock, lds, stream>>>(p, a.page_indices);
+      else
+        attn_stream_kernel<64, 2><<<grid, sblock, lds, stream>>>(p, a.page_indices);
       hipLaunchKernelGGL(attn_merge_kernel<64>, grid, block, merge_lds, stream, p);
     }
   } else {

@@ -24,6 +24,7 @@ struct AttnPlan {
   // the 64-key tiles of all (request, kv head, row block) pairs
   int nwg;            // workgroups (a power of two >= 8)
   int lg_nwg;         // log2(nwg)
+  int ns;             // stage ring slots (4, or 2 when LDS is short)
   size_t slots;       // partial-result slots
   size_t grid;        // launch size (multiple of 8: XCD-aware remap)
   size_t dyn_lds;     // dynamic LDS bytes per workgroup
