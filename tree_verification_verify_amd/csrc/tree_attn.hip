@@ -122,8 +122,8 @@ __device__ inline uint4 keep_first(uint4 v, int n) {
 // workgroup that crosses many short pairs, or streams many wide row blocks,
 // gets fewer tiles.
 constexpr int kCostSmall = 8;
-constexpr int kCostBig = 11;
-constexpr int kCostPair = 40;
+constexpr int kCostBig = 10;
+constexpr int kCostPair = 64;
 
 __device__ inline int tile_cost(int rows) { return rows > 64 ? kCostBig : kCostSmall; }
 
@@ -390,18 +390,21 @@ __device__ inline void wait_vm() {
 }
 
 // 16 bytes per lane from global memory straight into LDS: lane i of the
-// wave writes lds_base + 16*i (lds_base must be wave-uniform).
+// wave writes lds_base + 16*i (lds_base must be wave-uniform). Written as
+// inline asm so the compiler keeps no account of these loads: every wait
+// for them is explicit (wait_vm before a stage barrier), and the compiler
+// adds no conservative full waits of its own in front of LDS reads.
 __device__ inline void load_lds16(const void* src, void* lds_base) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
-#endif
+  const uint32_t base = uint32_t(reinterpret_cast<uintptr_t>(lds_base));
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(base) : "memory");
 }
 
-// Workgroup barrier without a memory fence: the waits that make the stage
-// data visible are explicit. The empty asm statements keep the compiler from
-// moving memory operations across it.
+// Workgroup barrier without a memory fence (no wait for pending global
+// loads or stores); this wave's LDS operations complete first. The empty
+// asm statements keep the compiler from moving memory operations across it.
 __device__ inline void stage_barrier() {
   asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -418,11 +421,15 @@ __device__ __attribute__((always_inline)) inline void static_for(F&& f) {
 // Loads go straight from HBM to LDS (global_load_lds_dwordx4), NS-1 stages
 // ahead of the one being computed; each slot is its own LDS object so the
 // compiler knows which pending loads a read depends on.
-// page_idx is p.page_indices again, declared __restrict__ so the per-stage
-// page-id loads can go through the scalar cache.
+// page_idx, node_ip, prefix and page_ip alias p.page_indices,
+// p.node_indptr, p.prefix_len and p.page_indptr, declared __restrict__ so
+// their (wave-uniform) loads go through the scalar cache.
 template <int D, int NS>
 __global__ __launch_bounds__(kThreadsS, 1) void attn_stream_kernel(AttnParams p,
-                                                                   const int32_t* __restrict__ page_idx) {
+                                                                   const int32_t* __restrict__ page_idx,
+                                                                   const int32_t* __restrict__ node_ip,
+                                                                   const int32_t* __restrict__ prefix,
+                                                                   const int32_t* __restrict__ page_ip) {
   constexpr int KK = D / 32;          // 32-wide k-steps of the QK product
   constexpr int DT = D / 16;          // 16-wide d tiles of the PV product
   constexpr int NI = D / 32;          // 1 KB loads per wave per stage (K and V^T)
@@ -502,9 +509,9 @@ __global__ __launch_bounds__(kThreadsS, 1) void attn_stream_kernel(AttnParams p,
   while (c < b) {
     while (off[r + 1] <= c) ++r;
     r = __builtin_amdgcn_readfirstlane(r);
-    const int nbeg = p.node_indptr[r];
-    const int N = p.node_indptr[r + 1] - nbeg;
-    const int P = p.prefix_len[r];
+    const int nbeg = node_ip[r];
+    const int N = node_ip[r + 1] - nbeg;
+    const int P = prefix[r];
     const int L = P + N;
     const int R = N * p.G;
     const int nt = ceil_div(L, kStage);
@@ -518,8 +525,8 @@ __global__ __launch_bounds__(kThreadsS, 1) void attn_stream_kernel(AttnParams p,
     const bool whole = tlo == 0 && thi == nt;
     const int row0 = q.rb * kRowsPB;
     const int rows_here = min(kRowsPB, R - row0);
-    const int pbase = p.page_indptr[r];
-    const int pend = p.page_indptr[r + 1] - 1;  // last listed page (>= pbase)
+    const int pbase = page_ip[r];
+    const int pend = page_ip[r + 1] - 1;  // last listed page (>= pbase)
     const int words = ceil_div(N, 32);
     const int first_node = row0 / p.G;
     const int nn_blk = (row0 + rows_here - 1) / p.G - first_node + 1;
@@ -552,9 +559,9 @@ __global__ __launch_bounds__(kThreadsS, 1) void attn_stream_kernel(AttnParams p,
     // Every load of a wave lies in page wave/2 of its stage (K rows 8*wave..
     // 8*wave+7, and V^T blocks KI*wave .. KI*wave+KI-1 of D/32 per page), so
     // a wave needs one page id per stage, a scalar. A page past the sequence
-    // is read from page 0; its slots, like slots past the sequence in the
-    // last page, are zeroed in LDS before use. Ids outside the pool are
-    // reported and also replaced by page 0.
+    // is read from page 0; its keys, like slots past the sequence in the
+    // last page, are masked and their V rows zeroed in registers. Ids outside
+    // the pool are reported and also replaced by page 0.
     const int wpg = wave >> 1;
     bool bad_page = false;
     auto load_id = [&](int tile) __attribute__((always_inline)) -> int {
@@ -577,17 +584,6 @@ __global__ __launch_bounds__(kThreadsS, 1) void attn_stream_kernel(AttnParams p,
       for (int j = 0; j < KI; ++j) {
         const int q = KI * wave + j;
         load_lds16(vp + blk + (live ? v_off[j] : 0), sb + kStage * D + wpg * (D * kPage) + (q % VPI) * 512);
-      }
-    };
-    // Zero V^T keys >= tail of a slot (the sequence ends inside the stage).
-    auto zero_tail = [&](uint16_t* sb, int tail) __attribute__((always_inline)) {
-      for (int i = tid; i < D * 8; i += kThreadsS) {
-        const int d = i >> 3, lc = i & 7;  // key chunk lc: page lc/2, half lc&1
-        if (lc * 8 + 8 > tail) {
-          uint4* ptr = reinterpret_cast<uint4*>(sb + kStage * D + (lc >> 1) * (D * kPage) + 16 * d +
-                                                8 * ((lc & 1) ^ swz_v(d)));
-          *ptr = keep_first(*ptr, tail - lc * 8);
-        }
       }
     };
 
@@ -677,10 +673,23 @@ __global__ __launch_bounds__(kThreadsS, 1) void attn_stream_kernel(AttnParams p,
           }
         }
         l_run += ls;
+        if (k0 + 32 <= L) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const bf16x8 va = *reinterpret_cast<const bf16x8*>(sb + kt2 * (2 * D * kPage) + dt * 256 + vaddr);
-          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, acc[dt], 0, 0, 0);
+          for (int dt = 0; dt < DT; ++dt) {
+            const bf16x8 va = *reinterpret_cast<const bf16x8*>(sb + kt2 * (2 * D * kPage) + dt * 256 + vaddr);
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, acc[dt], 0, 0, 0);
+          }
+        } else {
+          // The sequence ends inside this half: V rows of keys >= L may hold
+          // anything (unused slots, page 0), so they are zeroed before the
+          // PV product (p is 0 there, but 0 * NaN is not).
+          const int keep = L - (k0 + 8 * lg);
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const uint4 raw = *reinterpret_cast<const uint4*>(sb + kt2 * (2 * D * kPage) + dt * 256 + vaddr);
+            const bf16x8 va = __builtin_bit_cast(bf16x8, keep_first(raw, keep));
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, acc[dt], 0, 0, 0);
+          }
         }
       }
     };
@@ -697,6 +706,9 @@ __global__ __launch_bounds__(kThreadsS, 1) void attn_stream_kernel(AttnParams p,
       build_anc(p, nbeg, N, first_node, nn_blk, words, anc, par);
       __syncthreads();
     }
+    // Q and the first stages have landed (the first step would wait for the
+    // first stage anyway; Q is then settled for the whole segment).
+    wait_vm<0>();
 
     // Step i (stage i in slot J = (i - tlo) % NS): wait for this wave's
     // loads of stage i (NS-2 later stages stay pending), barrier (every
@@ -707,10 +719,6 @@ __global__ __launch_bounds__(kThreadsS, 1) void attn_stream_kernel(AttnParams p,
       wait_vm<(NS - 2) * NI>();
       stage_barrier();
       issue(slot(std::integral_constant<int, J + NS - 1>{}), idn, i + NS - 1 < thi);
-      if (i == nt - 1 && (L & (kStage - 1)) != 0) {
-        zero_tail(slot(j_c), L - i * kStage);
-        __syncthreads();
-      }
       if (active) compute(slot(j_c), i, nh_c);
       idn = load_id(i + NS);
     };
@@ -1139,15 +1147,15 @@ hipError_t launch_attn(const tv_attn_desc& d, const AttnPlan& pl, const AttnArgs
     const dim3 sblock(kThreadsS);
     if (d.head_dim == 128) {
       if (pl.ns == 4)
-        attn_stream_kernel<128, 4><<<grid, sblock, lds, stream>>>(p, a.page_indices);
+        attn_stream_kernel<128, 4><<<grid, sblock, lds, stream>>>(p, a.page_indices, a.node_indptr, a.prefix_len, a.page_indptr);
       else
-        attn_stream_kernel<128, 2><<<grid, sblock, lds, stream>>>(p, a.page_indices);
+        attn_stream_kernel<128, 2><<<grid, sblock, lds, stream>>>(p, a.page_indices, a.node_indptr, a.prefix_len, a.page_indptr);
       hipLaunchKernelGGL(attn_merge_kernel<128>, grid, block, merge_lds, stream, p);
     } else {
       if (pl.ns == 4)
-        attn_stream_kernel<64, 4><<<grid, sblock, lds, stream>>>(p, a.page_indices);
+        attn_stream_kernel<64, 4><<<grid, sblock, lds, stream>>>(p, a.page_indices, a.node_indptr, a.prefix_len, a.page_indptr);
       else
-        attn_stream_kernel<64, 2><<<grid, sblock, lds, stream>>>(p, a.page_indices);
+        attn_stream_kernel<64, 2><<<grid, sblock, lds, stream>>>(p, a.page_indices, a.node_indptr, a.prefix_len, a.page_indptr);
       hipLaunchKernelGGL(attn_merge_kernel<64>, grid, block, merge_lds, stream, p);
     }
   } else {
