@@ -10,25 +10,25 @@
 //    (request r, kv head g), so one K/V tile staged in LDS serves every node
 //    of the block and all G = Hq/Hkv heads that share the kv head.
 //  * Work is the flat list of 64-key tiles of every (r, g, row block) pair.
-//    A fixed grid of persistent workgroups splits that list into equal
-//    contiguous shares (stream-K), so uneven prefixes balance exactly. A
-//    pair wholly inside one share is finished in registers and written out;
-//    a pair cut by share boundaries leaves fp32 partials (offset, l, acc),
-//    which a second, small kernel merges in share order (deterministic; the
-//    kernel boundary makes the partials visible, so the streaming kernel
-//    needs no fences, counters or waiting). Shares are laid out XCD by XCD,
-//    so the row blocks of one kv head run on one XCD and share its L2.
-//  * 4 waves x 32 rows. S^T = K Q^T and O^T += V^T P^T on
+//    A fixed grid of persistent workgroups (one of 8 waves per CU) splits
+//    that list into contiguous shares of equal cost (stream-K, with tiles of
+//    wide row blocks and each pair's set-up weighted), so uneven prefixes
+//    balance. A pair wholly inside one share is finished in registers and
+//    written out; a pair cut by share boundaries leaves fp32 partials
+//    (offset, l, acc), which a second, small kernel merges in share order
+//    (deterministic; the kernel boundary makes the partials visible, so the
+//    streaming kernel needs no fences, counters or waiting). Shares are laid
+//    out XCD by XCD, so the row blocks of one kv head share an XCD's L2.
+//  * One 16-row tile per wave. S^T = K Q^T and O^T += V^T P^T on
 //    v_mfma_f32_16x16x32_bf16; both keep a row on lane%16, so the online
-//    softmax rescale is lane-local and P never leaves registers (the PV key
-//    order is permuted to match the S^T accumulator layout).
-//  * V pages are stored transposed ([D][16] per page and head), so every
-//    16-byte global load lands in LDS unchanged and each MFMA operand is two
-//    8-byte LDS reads; K tiles are stored as loaded ([key][D], padded rows).
-//  * Loads of the next 64-key stage are issued before the MFMA work on the
-//    current one (register staging, LDS double buffer).
-//  * The ancestor mask is a per-node bitset built in LDS when a segment
-//    reaches the tree's own keys, and consulted only in those tiles.
+//    softmax rescale is lane-local and P never leaves registers.
+//  * V pages are stored transposed ([D][16] per page and head). K and V^T
+//    stages go from HBM straight into a ring of LDS slots (1 KB per wave
+//    load instruction), three stages ahead of the one being computed; the
+//    slots are XOR-swizzled so operand reads are free of bank conflicts, and
+//    the QK operand rows are permuted so each PV operand is one 16-byte read.
+//  * The ancestor mask is a per-node bitset built in LDS while a segment's
+//    first stages load, and consulted only in tiles reaching the tree keys.
 // fp32 path (small validation shapes): a VALU kernel, one workgroup per
 // (request, kv head, row block, key split), with the same partial format.
 #include <type_traits>
