@@ -603,10 +603,75 @@ __global__ __launch_bounds__(kThreadsS, 1) void attn_stream_kernel(AttnParams p,
     for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // One stage of a row tile: NH = 2 computes both 32-key halves, NH = 1
-    // the wave's own half.
+    // the wave's own half. Stages of prefix keys only (all but the last one
+    // or two of a pair) take a single straight-line path for all halves: one
+    // raise decision for the stage, no mask, no tail.
+    auto compute_plain = [&](const uint16_t* sb, auto nh_c) __attribute__((always_inline)) {
+      constexpr int NH = decltype(nh_c)::value;
+      f32x4 s[NH][2];
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh) {
+        const int kt2 = NH == 2 ? hh : half;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          s[hh][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) {
+            const bf16x8 ka = *reinterpret_cast<const bf16x8*>(sb + (kt2 * 32 + 4 * h) * D + kaddr[kk]);
+            s[hh][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[kk], s[hh][h], 0, 0, 0);
+          }
+        }
+      }
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh)
+        mloc = fmax_(mloc, fmax_(fmax_(fmax_(s[hh][0][0], s[hh][0][1]), fmax_(s[hh][0][2], s[hh][0][3])),
+                                 fmax_(fmax_(s[hh][1][0], s[hh][1][1]), fmax_(s[hh][1][2], s[hh][1][3]))));
+      const bool need = (mloc > m_ref) & ((m_ref == -INFINITY) | (cs * (mloc - m_ref) > kLazy));
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float mt = max_across_groups(mloc);
+        const bool raise = (mt > m_ref) & ((m_ref == -INFINITY) | (cs * (mt - m_ref) > kLazy));
+        const float m_new = raise ? mt : m_ref;
+        const float off_new = m_new == -INFINITY ? 0.f : cs * m_new;
+        const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(off_ - off_new);
+        m_ref = m_new;
+        off_ = off_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+      }
+      bf16x8 pb[NH];
+      float ls = 0.f;
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float pv = __builtin_amdgcn_exp2f(fmaf(s[hh][h][e], cs, -off_));
+            ls += pv;
+            pb[hh][4 * h + e] = static_cast<__bf16>(pv);
+          }
+        }
+      }
+      l_run += ls;
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh) {
+        const int kt2 = NH == 2 ? hh : half;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const bf16x8 va = *reinterpret_cast<const bf16x8*>(sb + kt2 * (2 * D * kPage) + dt * 256 + vaddr);
+          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[hh], acc[dt], 0, 0, 0);
+        }
+      }
+    };
     auto compute = [&](const uint16_t* sb, int tile, auto nh_c) __attribute__((always_inline)) {
       constexpr int NH = decltype(nh_c)::value;
       const int t0 = tile * kStage;
+      if (t0 + kStage <= P) {
+        compute_plain(sb, nh_c);
+        return;
+      }
 #pragma unroll
       for (int hh = 0; hh < NH; ++hh) {
         const int kt2 = NH == 2 ? hh : half;
