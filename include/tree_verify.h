@@ -18,8 +18,13 @@
  *     errors are returned before anything is launched.
  *   - Calls are stream-ordered and re-entrant; concurrent streams need
  *     distinct workspaces. A workspace must be zero-filled once
- *     (tv_workspace_init) before its first use; calls leave its
- *     synchronisation counters at zero when they complete.
+ *     (tv_workspace_init) before its first use and then belongs to one
+ *     entry point: calls keep synchronisation state in it between calls.
+ *     A tree_spec_sample workspace keeps that state per request at fixed
+ *     offsets, so it serves any later call whose batch fits the size it
+ *     was sized for. A tree_verify_attn workspace is laid out by its
+ *     descriptor: before reusing it with another descriptor, zero-fill it
+ *     again.
  *   - Anomalies found on the device (bad parent, page id out of range, too
  *     few pages, NaN/Inf logits, two accepted siblings, a stalled team
  *     barrier) set bits of a status word at the start of the workspace; they

@@ -23,14 +23,19 @@ def run_attention(inp, repeat=1, sm_scale=0.0):
     return (res if repeat > 1 else res[0]), st, bits
 
 
-def run_sampler(inp, max_depth=None, prefix_lens=None):
+def run_sampler(inp, max_depth=None, prefix_lens=None, ws=None):
+    """ws: a workspace to reuse (sized for at least this batch); a fresh
+    zero-filled one when None."""
     import torch
     import tree_verification_verify_amd as tv
     from workloads.device import sampler_tensors
     t = sampler_tensors(inp)
     md = max_depth if max_depth is not None else inp.max_nodes
     desc = tv.sample_desc(inp.batch, inp.vocab, inp.max_nodes, md)
-    ws = tv.alloc_workspace(tv.sample_workspace_size(desc))
+    if ws is None:
+        ws = tv.alloc_workspace(tv.sample_workspace_size(desc))
+    else:
+        assert ws.numel() >= tv.sample_workspace_size(desc)
     T = int(inp.node_indptr[-1])
     flag = torch.full((T,), -7, dtype=torch.int8, device="cuda")
     nt = torch.full((T,), -7, dtype=torch.int32, device="cuda")

@@ -177,3 +177,53 @@ def test_monte_carlo_tv_on_gpu():
     tvs = [0.5 * np.abs(rng.multinomial(n, p) / n - p).sum() for _ in range(300)]
     assert tv_walk <= np.percentile(tvs, 99), (tv_walk, np.percentile(tvs, 99))
     _compare(inp, got)
+
+
+def _subset(inp, idx):
+    """Requests idx of a batch, in that order (repeats allowed)."""
+    from workloads.inputs import SamplerInputs
+    rows, ind = [], [0]
+    for r in idx:
+        a, b = int(inp.node_indptr[r]), int(inp.node_indptr[r + 1])
+        rows.append(np.arange(a, b))
+        ind.append(ind[-1] + b - a)
+    rr = np.concatenate(rows)
+    return SamplerInputs(vocab=inp.vocab, target_logits=inp.target_logits[rr],
+                         draft_logits=None if inp.draft_logits is None else inp.draft_logits[rr],
+                         tokens=inp.tokens[rr], node_indptr=np.asarray(ind, np.int32),
+                         parent=inp.parent[rr], temperature=inp.temperature[list(idx)],
+                         uniforms=inp.uniforms[rr])
+
+
+def test_workspace_reused_across_calls():
+    """One workspace, calls of different batch sizes (so different team
+    sizes and request-to-slot maps) back to back: the team exchange must
+    never take a word left by an earlier call for a current one."""
+    import tree_verification_verify_amd as tv
+    cfg = make_config("highload", attention=False)
+    big = cfg.sampler
+    rng = np.random.default_rng(5)
+    trees = [random_tree(rng, int(rng.integers(2, 20)), depth_cap=5) for _ in range(200)]
+    many = make_sampler_inputs(rng, rng, rng, trees, 2048, rng.choice([0.5, 1.0], size=200))
+    desc = tv.sample_desc(200, big.vocab, big.max_nodes, 8)
+    ws = tv.alloc_workspace(tv.sample_workspace_size(desc))
+    for inp in [big, _subset(big, [46, 19, 3]), many, big, big, _subset(big, list(range(63, -1, -1)))]:
+        _compare(inp, _run(inp, max_depth=8, ws=ws))
+
+
+def test_streamed_slices():
+    """A vocabulary whose per-member slice exceeds the resident capacity
+    (the streamed passes), with 4-aligned rows."""
+    rng = np.random.default_rng(9)
+    trees = [random_tree(rng, n, depth_cap=4) for n in (9, 14, 5)]
+    inp = make_sampler_inputs(rng, rng, rng, trees, 262144, [1.0, 0.5, 1.0], noise=1.0)
+    _compare(inp, _run(inp, max_depth=4))
+
+
+def test_more_children_than_listed():
+    """A root with 150 children: the per-visit child list holds 64, the rest
+    are found by scanning; independent logits force long rejection runs."""
+    rng = np.random.default_rng(12)
+    inp = make_sampler_inputs(rng, rng, rng, [star_tree(151), star_tree(90)], 4096, [1.0, 2.0],
+                              mode="independent")
+    _compare(inp, _run(inp, max_depth=1))

@@ -8,26 +8,38 @@
 // at the stop node (TreeSpark §3.2 step 3).
 //
 // Design (gfx950):
-//  * One team of W workgroups per request, all on one XCD (so team traffic
-//    stays in that XCD's L2); the team splits the vocabulary into W slices,
-//    so every vocab-wide reduction is W-way parallel. Members publish
-//    partials and meet at a device-scope counter (bounded spin; the launch
-//    is cooperative when W > 1, so every member is resident). Partials are
-//    combined by every member in the same fixed order, so all members take
-//    bit-identical decisions without a broadcast.
+//  * One team of W workgroups per request, all on one XCD; the team splits
+//    the vocabulary into W slices, so every vocab-wide reduction is W-way
+//    parallel. Every member combines the gathered partials in the same fixed
+//    order, so all members take bit-identical decisions without a broadcast.
+//  * The walk is a chain of dependent vocabulary passes (one per visited
+//    node, one per rejected sibling), so its speed is the latency of one
+//    pass. A member keeps its slice of the visited node's two logit rows in
+//    registers and LDS (up to kResCh chunks of 1024 logits per row): the
+//    slice is loaded with every load in flight at once, and the residual
+//    passes after rejections reuse it without touching memory. Larger
+//    slices stream.
+//  * Team exchange: each member publishes 64-bit words holding a 32-bit
+//    payload and a 32-bit tag, and readers poll the words themselves until
+//    the tag is the expected one: one memory round trip per exchange, no
+//    counter. Tags come from a per-request sequence kept in the workspace
+//    that only grows, and each request owns a fixed slot region, so a word
+//    left by an earlier call never carries a live tag.
+//  * The children of the visited node, their tokens' logits and their
+//    uniforms are fetched at the start of the visit, beside the slice loads.
 //  * No residual vector is stored. After rejecting siblings x_1..x_j the
 //    residual is max(p - a q, 0) / B with scalars a_{j+1} = a_j + B_j / S_j,
 //    B_{j+1} = sum_y max(p(y) - a_{j+1} q(y), 0), S_j = 1 - sum_{i<j} q(x_i)
 //    (a rejected token's residual is already 0, so removing it from the
-//    proposal is implicit). Each rejection costs one vocab-wide pass over
-//    the two logit rows. The per-slice sums of that pass (or of p, at a leaf)
-//    locate the slice of the correction/bonus draw, so the draw rescans one
-//    slice only.
-//  * Arithmetic is fp64 (logits widened exactly). exp uses Tang's table
-//    method (2^(j/64) table in LDS, degree-5 polynomial, ~1 ulp), about half
-//    the instructions of the library routine. Decisions therefore agree with
-//    an fp64 reference except within ~1e-12 of a threshold.
-//  * Sweeps keep 8 independent 16-byte loads per thread in flight.
+//    proposal is implicit). The per-slice sums of the last pass (or of p, at
+//    a leaf) locate the slice of the correction/bonus draw, so the draw
+//    rescans one slice only.
+//  * Arithmetic is fp64 (logits widened exactly). Vocabulary sums use a
+//    table exp (2^(j/1024) in LDS, cubic polynomial, the power of two set by
+//    ldexp) on an argument formed by one fma from the fp32 logit; single
+//    values that decide (p(x), q(x), rescale factors) use a 64-entry table
+//    with a degree-5 polynomial (~1 ulp). Decisions therefore agree with an
+//    fp64 reference except within ~1e-12 of a threshold.
 //  * T = 0 requests: the team splits the rows; argmax (lowest index on ties)
 //    of every row, then the exact-match flags; no draft logits are read.
 #include <math.h>
@@ -42,7 +54,17 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxTeam = 16;             // members per team (one XCD holds a team)
-constexpr int kUnroll = 4;               // float4 loads per row per step of a two-row sweep
+constexpr int kResCh = 10;               // resident chunks (1024 logits) per row per member
+constexpr int kLdsCh = 2;                // of which the last kLdsCh live in LDS
+constexpr int kRegCh = kResCh - kLdsCh;  // and the rest in registers
+constexpr int kParLds = 1024;            // parents and tokens staged in LDS up to this many rows
+constexpr int kKids = 64;                // children listed (and prefetched) per visit
+constexpr int kSlotWords = 8;            // 64-bit words per (member, parity) exchange slot
+// Per-request workspace block at a fixed stride (so a workspace serves any
+// batch up to the one it was sized for): greedy barrier counter (byte 0),
+// exchange tag sequence (byte 4), exchange slots from byte 256.
+constexpr size_t kReqSlotsOff = 256;
+constexpr size_t kReqBytes = kReqSlotsOff + size_t(kMaxTeam) * 2 * kSlotWords * sizeof(uint64_t);
 constexpr uint32_t kSpinLimit = 1u << 25;
 
 struct SampleParams {
@@ -56,15 +78,14 @@ struct SampleParams {
   int8_t* flag;
   int32_t* next_token;
   uint32_t* status;
-  uint32_t* team_ctr;
-  double* part;
-  int B, V, W, max_nodes, part_stride;
+  char* req;  // per-request blocks of kReqBytes
+  int B, V, W, max_nodes;
 };
 
 // ---------------------------------------------------------------------------
-// exp(a) for a <= 0 in fp64: a = (64 k + j) ln2/64 + r, |r| <= ln2/128,
-// e^a = 2^k * 2^(j/64) * P(r) with P the degree-5 Taylor polynomial
-// (remainder below 2^-53 on that interval). tbl[j] = 2^(j/64).
+// exp(a) for a <= 0 in fp64, for single values: a = (64 k + j) ln2/64 + r,
+// |r| <= ln2/128, e^a = 2^k * 2^(j/64) * P(r) with P the degree-5 Taylor
+// polynomial (remainder below 2^-53 on that interval). tbl[j] = 2^(j/64).
 constexpr double kInvLn2x64 = 92.33248261689366;
 constexpr double kLn2by64Hi = 0.01083042469326756;  // low mantissa bits zero: n*hi exact
 constexpr double kLn2by64Lo = 2.9815858269852933e-12;
@@ -82,86 +103,241 @@ __device__ inline double exp_nonpos(double a, const double* tbl) {
   return ldexp(tbl[ni & 63] * p, ni >> 6);
 }
 
+// exp for vocabulary sums, taking z = x * 1024/ln2 (x <= 0): z = 1024 k + j
+// + f with |f| <= 1/2 (rounding by the 1.5 * 2^52 shift, whose low word is
+// then the integer), e^x = 2^k * 2^(j/1024) * e^(f ln2/1024), the last
+// factor a cubic (truncation below 6e-16 for |f ln2/1024| <= 3.4e-4).
+// z below -1100 * 1024 (e^x < 2^-1100, and -inf) gives exactly 0.
+// tbl[j] = 2^(j/1024).
+constexpr double kZScale = 1024.0 / 0.69314718055994530942;
+constexpr double kZC1 = 0.69314718055994530942 / 1024.0;
+constexpr double kZC2 = kZC1 * kZC1 / 2.0;
+constexpr double kZC3 = kZC1 * kZC1 * kZC1 / 6.0;
+constexpr double kShift52 = 6755399441055744.0;  // 1.5 * 2^52
+
+__device__ inline double exp_z(double z, const double* tbl) {
+  z = fmax(z, -1100.0 * 1024.0);
+  const double nd = z + kShift52;
+  const int n = __double2loint(nd);
+  const double f = z - (nd - kShift52);
+  double q = fma(f, kZC3, kZC2);
+  q = fma(q, f, kZC1);
+  q *= f;
+  const double tj = tbl[n & 1023];
+  return ldexp(fma(tj, q, tj), n >> 10);
+}
+
+// Empty volatile asm on a value: the value is taken to be produced (or
+// consumed) at that point in program order. Used to fence units of exp work
+// so the compiler keeps one float4 in flight at a time (the resident slice
+// already occupies most of the register budget) and does not keep widened
+// copies of the slice alive between passes.
+__device__ inline float4 opaque(float4 x) {
+  asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w));
+  return x;
+}
+__device__ inline double opaque(double x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// exp_z of the four lanes of x at z = x * A + b, summed in lane order; the
+// four table reads are issued together so their LDS latency overlaps.
+__device__ inline double exp4_sum(float4 x, double A, double b, const double* tbl) {
+  x = opaque(x);
+  const float xs[4] = {x.x, x.y, x.z, x.w};
+  double f[4], tj[4];
+  int n[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const double z = fmax(fma(double(xs[e]), A, b), -1100.0 * 1024.0);
+    const double nd = z + kShift52;
+    n[e] = __double2loint(nd);
+    f[e] = z - (nd - kShift52);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) tj[e] = tbl[n[e] & 1023];
+  double s = 0.0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    double q = fma(f[e], kZC3, kZC2);
+    q = fma(q, f[e], kZC1);
+    q *= f[e];
+    s += ldexp(fma(tj[e], q, tj[e]), n[e] >> 10);
+  }
+  return opaque(s);
+}
+
 // ---------------------------------------------------------------------------
-// Team synchronisation.
+// Team exchange (T > 0): tagged 64-bit words.
 
 struct Team {
-  uint32_t* ctr;
-  uint32_t target;
+  uint64_t* slots;  // this request's region: [member][2 parities][kSlotWords]
+  uint32_t seq;     // tag base of this call (the request's sequence at entry)
+  int phase;        // exchanges completed so far
   int W;
   int member;
-  int phase;
-  double* part;   // this team's partial area: [2 parities][W][part_stride]
-  int stride;
   uint32_t* status;
 };
 
-__device__ inline double* member_slot(Team& tm, int member) {
-  return tm.part + (size_t(tm.phase & 1) * tm.W + member) * tm.stride;
-}
-
-// Partials travel through device-coherent (agent-scope) atomic stores and
-// loads, which bypass the non-coherent caches; so the barrier needs no L2
-// write-back or invalidate, only ordering: a member's partial stores
-// complete before its counter increment (release at workgroup scope is a
-// wait for them), and no partial is read before the counter says all
-// members have arrived.
-__device__ inline void put_partial(double* slot, int k, double v) {
-  __hip_atomic_store(slot + k, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline double get_partial(const double* slot, int k) {
-  return __hip_atomic_load(const_cast<double*>(slot) + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// All K partials of every member for the current phase, loaded in parallel
-// (one device-coherent load per thread) into LDS s_part[w * K + k].
-__device__ void gather_partials(Team& tm, int K, double* s_part) {
-  for (int i = threadIdx.x; i < tm.W * K; i += blockDim.x) {
-    const int w = i / K;
-    s_part[i] = get_partial(tm.part + (size_t(tm.phase & 1) * tm.W + w) * tm.stride, i - w * K);
+// Word k of this member's payload for the next exchange. Stored
+// device-coherent (agent scope): readers on other CUs poll it.
+__device__ inline void ll_put(Team& tm, int k, uint32_t payload, uint32_t* s_words) {
+  if (tm.W == 1) {
+    s_words[k] = payload;
+    return;
   }
-  __syncthreads();
+  const uint32_t tag = tm.seq + uint32_t(tm.phase) + 1u;
+  uint64_t* a = tm.slots + (size_t(tm.member) * 2 + ((tm.phase + 1) & 1)) * kSlotWords + k;
+  __hip_atomic_store(a, (uint64_t(tag) << 32) | payload, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// All members have published their partial for the current phase.
-__device__ void team_sync(Team& tm) {
-  __syncthreads();
+// Words 0..K-1 of every member for the next exchange into s_words[w * K + k]
+// (one polling thread per word; bounded spin). A member two exchanges ahead
+// cannot overwrite a slot still being read: it must first have read this
+// member's next words, which are published only after this gather.
+__device__ void ll_gather(Team& tm, int K, uint32_t* s_words) {
   if (tm.W > 1) {
-    tm.target += uint32_t(tm.W);
-    if (threadIdx.x == 0) {
-      __hip_atomic_fetch_add(tm.ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint32_t tag = tm.seq + uint32_t(tm.phase) + 1u;
+    const int par = (tm.phase + 1) & 1;
+    for (int i = threadIdx.x; i < tm.W * K; i += blockDim.x) {
+      const int w = i / K;
+      const uint64_t* a = tm.slots + (size_t(w) * 2 + par) * kSlotWords + (i - w * K);
+      uint64_t x = __hip_atomic_load(const_cast<uint64_t*>(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       uint32_t spins = 0;
-      while (__hip_atomic_load(tm.ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < tm.target) {
-        __builtin_amdgcn_s_sleep(1);
+      while (uint32_t(x >> 32) != tag) {
         if (++spins > kSpinLimit) {
           raise_status(tm.status, TV_DEV_TIMEOUT);
           break;
         }
+        __builtin_amdgcn_s_sleep(1);
+        x = __hip_atomic_load(const_cast<uint64_t*>(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      s_words[i] = uint32_t(x);
+    }
+  }
+  __syncthreads();
+  tm.phase++;
+}
+
+__device__ inline double words_to_double(uint32_t lo, uint32_t hi) {
+  return __hiloint2double(int(hi), int(lo));
+}
+
+// A value every lane holds identically, moved to scalar registers.
+__device__ inline double uniform_d(double x) {
+  return __hiloint2double(__builtin_amdgcn_readfirstlane(__double2hiint(x)),
+                          __builtin_amdgcn_readfirstlane(__double2loint(x)));
+}
+__device__ inline float uniform_f(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
+// ---------------------------------------------------------------------------
+// Greedy team barrier (T = 0): a device-scope counter, reset by the last
+// member to leave.
+
+struct Barrier {
+  uint32_t* ctr;
+  uint32_t target;
+  int W;
+  uint32_t* status;
+};
+
+__device__ void barrier_sync(Barrier& b) {
+  __syncthreads();
+  if (b.W > 1) {
+    b.target += uint32_t(b.W);
+    if (threadIdx.x == 0) {
+      __hip_atomic_fetch_add(b.ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      uint32_t spins = 0;
+      while (__hip_atomic_load(b.ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < b.target) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > kSpinLimit) {
+          raise_status(b.status, TV_DEV_TIMEOUT);
+          break;
+        }
+      }
     }
     __syncthreads();
   }
 }
 
-// Leave the counter at zero: the last member to leave resets it. No member
-// waits after this point, so the reset cannot strand anyone.
-__device__ void team_exit(Team& tm) {
+// No member waits after this point, so the reset cannot strand anyone.
+__device__ void barrier_exit(Barrier& b) {
   __syncthreads();
-  if (tm.W > 1 && threadIdx.x == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(tm.ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == tm.target + uint32_t(tm.W) - 1u)
-      __hip_atomic_store(tm.ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (b.W > 1 && threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(b.ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == b.target + uint32_t(b.W) - 1u)
+      __hip_atomic_store(b.ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Block reductions (fixed order: wave shuffles, then waves in index order).
 
+// Lane exchanges by ds_swizzle xor patterns (within 32 lanes; the pattern
+// is an immediate, so no lane-address registers stay live), the two halves
+// joined through readlane (the result is wave-uniform).
+template <int M>
+__device__ inline int swz_i(int x) {
+  return __builtin_amdgcn_ds_swizzle(x, 0x1F | (M << 10));
+}
+template <int M>
+__device__ inline float swz(float x) {
+  return __int_as_float(swz_i<M>(__float_as_int(x)));
+}
+template <int M>
+__device__ inline double swz(double x) {
+  return __hiloint2double(swz_i<M>(__double2hiint(x)), swz_i<M>(__double2loint(x)));
+}
+__device__ inline double lane_d(double x, int l) {
+  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(x), l),
+                          __builtin_amdgcn_readlane(__double2loint(x), l));
+}
+__device__ inline float lane_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+// Row (16-lane) reductions by DPP moves, which are VALU operations: xor 1
+// and xor 2 by quad permutes, then the half-row and row mirrors. Every
+// step combines two values that all lanes of the group then share
+// (addition and max are commutative), so every lane of a row ends with the
+// same result, in an order fixed by the lane layout alone.
+template <int CTRL>
+__device__ inline float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ inline double dpp_d(double v) {
+  return __hiloint2double(__builtin_amdgcn_mov_dpp(__double2hiint(v), CTRL, 0xF, 0xF, false),
+                          __builtin_amdgcn_mov_dpp(__double2loint(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+__device__ inline double row_sum(double v) {
+  v += dpp_d<kDppXor1>(v);
+  v += dpp_d<kDppXor2>(v);
+  v += dpp_d<kDppHalfMirror>(v);
+  v += dpp_d<kDppMirror>(v);
+  return v;
+}
+__device__ inline float row_max(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppMirror>(v));
+  return v;
+}
+
+// Wave-wide, wave-uniform results: the four rows joined in row order.
 __device__ inline double wave_sum(double v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += shfl_xor_d(v, off);
-  return __shfl(v, 0, kWave);
+  v = row_sum(v);
+  return (lane_d(v, 0) + lane_d(v, 16)) + (lane_d(v, 32) + lane_d(v, 48));
+}
+__device__ inline float wave_max(float v) {
+  v = row_max(v);
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
 __device__ inline double block_sum(double v, double* sh) {
@@ -175,23 +351,41 @@ __device__ inline double block_sum(double v, double* sh) {
   return tot;
 }
 
-// Block-wide (max, sum of exp(x - max)) of per-thread pairs: the maximum is
-// reduced first (shuffles only), then every sum is rescaled to it with one
-// exp and the sums are added in a fixed order.
-__device__ inline void block_ms(double& m, double& s, double* sh, const double* tbl) {
-  double M = m;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmax(M, shfl_xor_d(M, off));
+// Block-wide maxima (fp32 logits) and sums of exp(x/T - max/T) of both rows:
+// the maxima first, then every thread's sums rescaled to them with one exp
+// and added in a fixed order.
+__device__ inline void block_ms2(float& mt, double& st, float& md, double& sd, double invT,
+                                 double* sh, float* shf, const double* tbl) {
+  float Mt = wave_max(mt), Md = wave_max(md);
   const int wave = threadIdx.x / kWave;
-  if ((threadIdx.x & 63) == 0) sh[wave] = M;
+  if ((threadIdx.x & 63) == 0) {
+    shf[wave] = Mt;
+    shf[kWaves + wave] = Md;
+  }
   __syncthreads();
-  M = sh[0];
-  for (int w = 1; w < kWaves; ++w) M = fmax(M, sh[w]);
+  Mt = shf[0];
+  Md = shf[kWaves];
+  for (int w = 1; w < kWaves; ++w) {
+    Mt = fmaxf(Mt, shf[w]);
+    Md = fmaxf(Md, shf[kWaves + w]);
+  }
+  double vt = mt == -INFINITY ? 0.0 : st * exp_nonpos((double(mt) - double(Mt)) * invT, tbl);
+  double vd = md == -INFINITY ? 0.0 : sd * exp_nonpos((double(md) - double(Md)) * invT, tbl);
+  vt = wave_sum(vt);
+  vd = wave_sum(vd);
+  if ((threadIdx.x & 63) == 0) {
+    sh[wave] = vt;
+    sh[kWaves + wave] = vd;
+  }
   __syncthreads();
-  double v = (M == -INFINITY || m == -INFINITY) ? 0.0 : s * exp_nonpos(m - M, tbl);
-  v = block_sum(v, sh);
-  m = M;
-  s = v;
+  st = 0.0;
+  sd = 0.0;
+  for (int w = 0; w < kWaves; ++w) {
+    st += sh[w];
+    sd += sh[kWaves + w];
+  }
+  mt = Mt;
+  md = Md;
 }
 
 // argmax with the lowest index on ties.
@@ -202,15 +396,15 @@ __device__ inline void am_combine(float& v, int& i, float v2, int i2) {
 }
 
 // ---------------------------------------------------------------------------
-// Vocabulary sweeps over [lo, hi) of one or two rows. Each step issues
-// kUnroll 16-byte loads per row per thread before using any of them; then
+// Streaming vocabulary sweeps over [lo, hi) of one or two rows. Each step
+// issues 8 independent loads per thread before using any of them; then
 // f(t, d, y, valid) sees every element once (d = 0 when only one row is
 // read). Indices past hi are clamped to a valid address and passed with
 // valid = false, so the loop body never branches. lo is a multiple of 4 in
 // the vectorised form (rows are 16-byte aligned when V % 4 == 0).
 template <bool TWO, class F>
 __device__ inline void sweep(const float* tr, const float* dr, int lo, int hi, bool vec4, F&& f) {
-  constexpr int kUnroll = TWO ? 4 : 8;  // 8 independent 16-byte loads per thread either way
+  constexpr int kUnroll = TWO ? 4 : 8;
   if (vec4) {
     const float4* t4 = reinterpret_cast<const float4*>(tr + lo);
     const float4* d4 = reinterpret_cast<const float4*>(dr + lo);
@@ -252,77 +446,6 @@ __device__ inline void sweep(const float* tr, const float* dr, int lo, int hi, b
   }
 }
 
-// Per-thread (max, sum of exp(x/T - max)) of both rows over [lo, hi): every
-// step loads 4 float4 per row, raises the running maxima once from the
-// step's own maxima (one rescale), then adds the step's terms. Tail
-// elements are masked to -inf, so nothing branches per element.
-__device__ inline void slice_stats(const float* tr, const float* dr, int lo, int hi, bool vec4,
-                                   double invT, const double* tbl, double& mt, double& st,
-                                   double& md, double& sd, bool& bad) {
-  constexpr int U = 4;
-  auto step = [&](float (&a)[4 * U], float (&b)[4 * U]) {
-    float smt = -INFINITY, smd = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < 4 * U; ++k) {
-      smt = fmaxf(smt, a[k]);
-      smd = fmaxf(smd, b[k]);
-    }
-    const double nmt = fmax(mt, double(smt) * invT), nmd = fmax(md, double(smd) * invT);
-    st = mt == -INFINITY ? 0.0 : st * exp_nonpos(mt - nmt, tbl);
-    sd = md == -INFINITY ? 0.0 : sd * exp_nonpos(md - nmd, tbl);
-    mt = nmt;
-    md = nmd;
-#pragma unroll
-    for (int k = 0; k < 4 * U; ++k) {
-      st += exp_nonpos(fma(double(a[k]), invT, -mt), tbl);
-      sd += exp_nonpos(fma(double(b[k]), invT, -md), tbl);
-    }
-  };
-  if (vec4) {
-    const float4* t4 = reinterpret_cast<const float4*>(tr + lo);
-    const float4* d4 = reinterpret_cast<const float4*>(dr + lo);
-    const int n4 = (hi - lo) >> 2;
-    for (int base = threadIdx.x; base < n4; base += U * kThreads) {
-      float4 tv[U], dv[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = min(base + u * kThreads, n4 - 1);
-        tv[u] = t4[i];
-        dv[u] = d4[i];
-      }
-      float a[4 * U], b[4 * U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const bool ok = base + u * kThreads < n4;
-        const float ta[4] = {tv[u].x, tv[u].y, tv[u].z, tv[u].w};
-        const float da[4] = {dv[u].x, dv[u].y, dv[u].z, dv[u].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          bad |= ok && (!isfinite(ta[e]) || !isfinite(da[e]));
-          a[4 * u + e] = ok ? ta[e] : -INFINITY;
-          b[4 * u + e] = ok ? da[e] : -INFINITY;
-        }
-      }
-      step(a, b);
-    }
-  } else {
-    for (int base = lo + threadIdx.x; base < hi; base += 4 * U * kThreads) {
-      float a[4 * U], b[4 * U];
-#pragma unroll
-      for (int k = 0; k < 4 * U; ++k) {
-        const int y = base + k * kThreads;
-        const int yc = min(y, hi - 1);
-        const float t = tr[yc], d = dr[yc];
-        const bool ok = y < hi;
-        bad |= ok && (!isfinite(t) || !isfinite(d));
-        a[k] = ok ? t : -INFINITY;
-        b[k] = ok ? d : -INFINITY;
-      }
-      step(a, b);
-    }
-  }
-}
-
 // Residual weight max(p(y) - a q(y), 0) with p(y) = exp(t/T - Mt)/Zt and
 // q(y) = exp(d/T - Md)/Zd (plain p(y) when a == 0; the draft row is then
 // not needed).
@@ -346,7 +469,7 @@ struct Resid {
 // (8 loads per lane in flight); the quarter holding thr is then scanned
 // block by block with an in-order prefix over the block's tokens. Falls
 // back to the last token with positive weight. Result in *s_y.
-__device__ void slice_search(const float* tr, const float* dr, int lo, int hi, const Resid& R,
+__device__ __attribute__((noinline)) void slice_search(const float* tr, const float* dr, int lo, int hi, const Resid& R,
                              double thr, const double* tbl, double* sh, int* s_y) {
   constexpr int K = 8;
   const int lane = threadIdx.x & 63;
@@ -427,9 +550,28 @@ __device__ void slice_search(const float* tr, const float* dr, int lo, int hi, c
   __syncthreads();
 }
 
+// Parent and token arrays of one request: staged in LDS when they fit,
+// else read from global memory (each access names its memory, so neither
+// goes through generic addressing).
+struct Parents {
+  const int* g;
+  const int* s;
+  const int* gtok;
+  const int* stok;
+  bool lds;
+  __device__ inline int operator[](int i) const {
+    if (lds) return s[i];
+    return g[i];
+  }
+  __device__ inline int tok(int i) const {
+    if (lds) return stok[i];
+    return gtok[i];
+  }
+};
+
 // Next child of v after row `after` (children in ascending row = draw
 // order), found by wave 0 with a ballot; -1 when none. Broadcast via LDS.
-__device__ int next_child(const int* par, int N, int v, int after, int* s_c) {
+__device__ int next_child(const Parents& par, int N, int v, int after, int* s_c) {
   if (threadIdx.x < kWave) {
     int found = -1;
     for (int base = after + 1; base < N && found < 0; base += kWave) {
@@ -440,19 +582,397 @@ __device__ int next_child(const int* par, int N, int v, int after, int* s_c) {
     if (threadIdx.x == 0) *s_c = found;
   }
   __syncthreads();
-  const int c = *s_c;
+  const int c = __builtin_amdgcn_readfirstlane(*s_c);
   __syncthreads();
   return c;
 }
 
-__global__ __launch_bounds__(kThreads) void sample_kernel(SampleParams p) {
+// ---------------------------------------------------------------------------
+// The T > 0 walk.
+
+struct WalkLds {
+  double* tbl;        // 2^(j/64)
+  double* tbl1k;      // 2^(j/1024)
+  double* sh;         // [2 * kWaves]
+  float* shf;         // [2 * kWaves]
+  double* s_slice;    // [kMaxTeam] slice sums of the last pass
+  uint32_t* s_words;  // [kMaxTeam * 6] gathered exchange words
+  int* s_kid;         // [kKids]
+  float* s_kt;        // [kKids] target logit of the child token
+  float* s_kd;        // [kKids] draft logit of the child token
+  float* s_ku;        // [kKids] acceptance uniform of the child
+  int* s_nk;          // children of the visited node (kKids + 1: more follow)
+  int* s_int;
+  float4* s_res;      // [2 rows][kLdsCh][kThreads] LDS-resident chunks
+};
+
+// 16-byte load of lane offset voff (bytes) from [base, base + bytes) through
+// a raw buffer resource: reads at or past the end return 0 without touching
+// memory (gfx9 resource word 3).
+__device__ inline float4 load4_bounded(const float* base, int bytes, int voff) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, bytes, 0x00020000);
+  const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
+// The same into LDS (each lane's 16 bytes at lds + 16 * lane; lds is the
+// wave's base). Completion is counted by vmcnt like any load.
+__device__ inline void load4_bounded_lds(const float* base, int bytes, int voff, float4* lds) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, bytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+
+// The compiler does not order LDS reads after buffer-to-LDS loads: wait for
+// every outstanding load, as a memory barrier.
+__device__ inline void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Member's part of the visited node's rows when resident: nch chunks of
+// kThreads float4 (1024 logits) of both rows, chunk u < kRegCh in t[u],
+// d[u], the rest in LDS. Only the row's last chunk can be partial; its
+// missing elements read as -inf, whose exp term is exactly 0 (z is -inf,
+// or NaN when the thread's maximum is -inf too, and the clamp in exp_z
+// maps both to its floor).
+template <bool RES>
+struct Slice {
+  float4 t[RES ? kRegCh : 1], d[RES ? kRegCh : 1];
+};
+
+
+template <bool RES>
+__device__ __attribute__((always_inline)) inline void walk(
+    const SampleParams& p, Team& tm, int nbeg, int N, const Parents& par,
+    double invT, int lo, int hi, int nch, bool vec4, const WalkLds& L) {
+  const int V = p.V;
+  const int member = tm.member;
+  const int lane = threadIdx.x & 63;
+  const double A = invT * kZScale;  // z = (t/T - M/T) * 1024/ln2 = fma(t, A, -M * A)
+  Slice<RES> S;
+  // Flags: member 0 alone writes them (initial values here, accepted nodes
+  // later, in program order). next_token is written once per node at the
+  // end (the stop node by the member that draws it, the rest by member 0).
+  if (member == 0)
+    for (int i = threadIdx.x; i < N; i += kThreads) p.flag[nbeg + i] = i == 0 ? 1 : 0;
+
+  // Chunk u of the resident slice (RES only), past-the-slice lanes of the
+  // row's last chunk as -inf. With chk, the loaded values (0 past the
+  // slice) also go into the non-finite check: t * 0 is 0 for finite t.
+  const int n4m = (hi - lo) >> 2;
+  auto chunk = [&](int u, float4& a, float4& b, float* chk) __attribute__((always_inline)) {
+    if constexpr (RES) {
+      if (u < kRegCh) {
+        a = S.t[u];
+        b = S.d[u];
+      } else {
+        if (u == kRegCh) wait_loads();
+        a = L.s_res[(u - kRegCh) * kThreads + threadIdx.x];
+        b = L.s_res[(kLdsCh + u - kRegCh) * kThreads + threadIdx.x];
+      }
+      if (chk) {
+        float c = *chk;
+        c = fmaf(a.x, 0.f, fmaf(a.y, 0.f, fmaf(a.z, 0.f, fmaf(a.w, 0.f, c))));
+        c = fmaf(b.x, 0.f, fmaf(b.y, 0.f, fmaf(b.z, 0.f, fmaf(b.w, 0.f, c))));
+        *chk = c;
+      }
+      if ((u + 1) * kThreads > n4m && int(threadIdx.x) + u * kThreads >= n4m) {
+        a = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        b = a;
+      }
+    }
+  };
+
+  int v = 0;
+  for (int depth_guard = 0; depth_guard <= N; ++depth_guard) {
+    const float* trow = p.t + size_t(nbeg + v) * V;
+    const float* drow = p.d + size_t(nbeg + v) * V;
+
+    // Children of v (ascending rows, the first kKids) and their values, by
+    // wave 0, after its slice loads are issued (they are needed only once
+    // the stats exchange is done).
+    float kt = 0.f, kd = 0.f, ku = 0.f;
+    int nk = 0;
+    auto kids = [&]() __attribute__((always_inline)) {
+      if (threadIdx.x < kWave) {
+        int cnt = 0;
+        for (int base = v + 1; base < N && cnt <= kKids; base += kWave) {
+          const int i = base + lane;
+          const bool is = i < N && par[i] == v;
+          const unsigned long long m = __ballot(is);
+          const int pos = cnt + int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
+          if (is && pos < kKids) L.s_kid[pos] = i;
+          cnt += __popcll(m);
+        }
+        nk = min(cnt, kKids + 1);
+        if (lane < min(cnt, kKids)) {
+          const int c = L.s_kid[lane];  // written above by this wave
+          int x = par.tok(c);
+          if (x < 0 || x >= V) {
+            raise_status(p.status, TV_DEV_SHAPE);
+            x = 0;
+          }
+          kt = trow[x];
+          kd = drow[x];
+          ku = p.uniforms[2 * size_t(nbeg + c)];
+        }
+      }
+    };
+
+    // Stats pass: per-thread (max, sum exp) of t/T and d/T over the slice.
+    float mt = -INFINITY, md = -INFINITY;
+    double st = 0.0, sd = 0.0;
+    bool bad = false;
+    if constexpr (RES) {
+      // Every load of the slice in flight at once, chunk u through its own
+      // bounded resource (reads past the slice return 0; they are masked or
+      // skipped).
+      const int voff = int(threadIdx.x) * 16;
+      const int wbase = int(threadIdx.x) & ~(kWave - 1);
+#pragma unroll
+      for (int u = 0; u < kResCh; ++u) {
+        const int nb = max(0, 4 * (hi - lo) - u * 16 * kThreads);
+        if (u < kRegCh) {
+          S.t[u] = load4_bounded(trow + lo + u * 4 * kThreads, nb, voff);
+          S.d[u] = load4_bounded(drow + lo + u * 4 * kThreads, nb, voff);
+        } else {
+          load4_bounded_lds(trow + lo + u * 4 * kThreads, nb, voff, L.s_res + (u - kRegCh) * kThreads + wbase);
+          load4_bounded_lds(drow + lo + u * 4 * kThreads, nb, voff,
+                            L.s_res + (kLdsCh + u - kRegCh) * kThreads + wbase);
+        }
+      }
+      kids();
+      float chk = 0.f;
+      // Three groups: running maxima raised once per group (one rescale).
+      auto group = [&](int u0, int u1) __attribute__((always_inline)) {
+        float gt = -INFINITY, gd = -INFINITY;
+#pragma unroll
+        for (int u = u0; u < u1; ++u) {
+          if (u < nch) {
+            float4 a, b;
+            chunk(u, a, b, &chk);
+            gt = fmaxf(fmaxf(gt, fmaxf(a.x, a.y)), fmaxf(a.z, a.w));
+            gd = fmaxf(fmaxf(gd, fmaxf(b.x, b.y)), fmaxf(b.z, b.w));
+          }
+        }
+        const float nt = fmaxf(mt, gt), nd = fmaxf(md, gd);
+        st = mt == -INFINITY ? 0.0 : st * exp_nonpos((double(mt) - double(nt)) * invT, L.tbl);
+        sd = md == -INFINITY ? 0.0 : sd * exp_nonpos((double(md) - double(nd)) * invT, L.tbl);
+        mt = nt;
+        md = nd;
+        const double bt = -double(nt) * A, bd = -double(nd) * A;
+#pragma unroll
+        for (int u = u0; u < u1; ++u) {
+          if (u < nch) {
+            float4 a, b;
+            chunk(u, a, b, nullptr);
+            st += exp4_sum(a, A, bt, L.tbl1k);
+            sd += exp4_sum(b, A, bd, L.tbl1k);
+          }
+        }
+      };
+      group(0, kRegCh / 2);
+      group(kRegCh / 2, kRegCh);
+      group(kRegCh, kResCh);
+      bad = !(chk == 0.f);
+    } else {
+      kids();
+      // Streamed: the running maxima rise element by element.
+      sweep<true>(trow, drow, lo, hi, vec4, [&](float t, float d, int, bool ok) {
+        bad |= ok && (!isfinite(t) || !isfinite(d));
+        if (!ok) return;
+        if (t > mt) {
+          st = mt == -INFINITY ? 0.0 : st * exp_nonpos((double(mt) - double(t)) * invT, L.tbl);
+          mt = t;
+        }
+        if (d > md) {
+          sd = md == -INFINITY ? 0.0 : sd * exp_nonpos((double(md) - double(d)) * invT, L.tbl);
+          md = d;
+        }
+        st += exp_z(fma(double(t), A, -double(mt) * A), L.tbl1k);
+        sd += exp_z(fma(double(d), A, -double(md) * A), L.tbl1k);
+      });
+    }
+    if (bad) raise_status(p.status, TV_DEV_LOGITS);
+    if (threadIdx.x < kWave) {
+      L.s_kt[lane] = kt;
+      L.s_kd[lane] = kd;
+      L.s_ku[lane] = ku;
+      if (lane == 0) *L.s_nk = nk;
+    }
+    block_ms2(mt, st, md, sd, invT, L.sh, L.shf, L.tbl);
+    if (threadIdx.x < 6) {
+      const uint32_t k = threadIdx.x;
+      const double dv = k < 3 ? st : sd;
+      const float fv = k < 3 ? mt : md;
+      const uint32_t j = k % 3;
+      const uint32_t wv = j == 0 ? __float_as_uint(fv)
+                                 : (j == 1 ? uint32_t(__double2loint(dv)) : uint32_t(__double2hiint(dv)));
+      ll_put(tm, int(k), wv, L.s_words);
+    }
+    ll_gather(tm, 6, L.s_words);
+    const int nkk = __builtin_amdgcn_readfirstlane(*L.s_nk);
+
+    // Team totals, member w in lane w of the first row of every wave (the
+    // same reduction in every wave and every member): the maxima, then each
+    // member's sums rescaled to them.
+    const bool mem_lane = lane < tm.W;
+    const float mw = mem_lane ? __uint_as_float(L.s_words[6 * lane]) : -INFINITY;
+    const float dw = mem_lane ? __uint_as_float(L.s_words[6 * lane + 3]) : -INFINITY;
+    const float Mt32 = lane_f(row_max(mw), 0), Md32 = lane_f(row_max(dw), 0);
+    const double et = mw == -INFINITY ? 0.0
+                                      : words_to_double(L.s_words[6 * lane + 1], L.s_words[6 * lane + 2]) *
+                                            exp_nonpos((double(mw) - double(Mt32)) * invT, L.tbl);
+    const double ed = dw == -INFINITY ? 0.0
+                                      : words_to_double(L.s_words[6 * lane + 4], L.s_words[6 * lane + 5]) *
+                                            exp_nonpos((double(dw) - double(Md32)) * invT, L.tbl);
+    const double Zt = lane_d(row_sum(et), 0), Zd = lane_d(row_sum(ed), 0);
+    // Slice sums of p (for a draw at a leaf).
+    if (threadIdx.x < tm.W) L.s_slice[threadIdx.x] = et / Zt;
+    const double Mt = double(Mt32) * invT, Md = double(Md32) * invT;
+
+    Resid R{invT, Mt, 1.0 / Zt, Md, 1.0 / Zd, 0.0};
+    double B = 1.0, Sq = 1.0;
+    int accepted = -1;
+    int k = 0;
+    // Every thread takes the same decisions; readfirstlane lets the compiler
+    // see that, so the walk's control flow and row addresses stay scalar.
+    int c = nkk > 0 ? __builtin_amdgcn_readfirstlane(L.s_kid[0]) : -1;
+    while (c >= 0) {
+      float tx, dx, uc;
+      if (k < kKids) {
+        tx = uniform_f(L.s_kt[k]);
+        dx = uniform_f(L.s_kd[k]);
+        uc = uniform_f(L.s_ku[k]);
+      } else {
+        int x = par.tok(c);
+        if (x < 0 || x >= V) {
+          raise_status(p.status, TV_DEV_SHAPE);
+          x = 0;
+        }
+        tx = trow[x];
+        dx = drow[x];
+        uc = p.uniforms[2 * size_t(nbeg + c)];
+      }
+      const double px = R.p(tx, L.tbl);
+      const double qx = R.q(dx, L.tbl);
+      double pj = px - R.a * qx;
+      pj = (pj > 0.0 ? pj : 0.0) / B;
+      const double qj = qx / Sq;
+      const double ratio = qj > 0.0 ? pj / qj : (pj > 0.0 ? INFINITY : 0.0);
+      if (__builtin_amdgcn_readfirstlane(int(double(uc) < ratio))) {
+        accepted = c;
+        if (member == 0 && threadIdx.x == 0) p.flag[nbeg + c] = 1;
+        break;
+      }
+      // Rejected: one residual pass at a' = a + B/S.
+      const double an = R.a + B / Sq;
+      double part = 0.0;
+      if constexpr (RES) {
+        const double bt = -double(Mt32) * A, bd = -double(Md32) * A;
+        const double ca = R.invZt, cb = -an * R.invZd;
+        auto wsum = [&](float t, float d) __attribute__((always_inline)) {
+          const double w = fma(cb, exp_z(fma(double(d), A, bd), L.tbl1k), ca * exp_z(fma(double(t), A, bt), L.tbl1k));
+          return w > 0.0 ? w : 0.0;
+        };
+#pragma unroll
+        for (int u = 0; u < kResCh; ++u) {
+          if (u < nch) {
+            float4 a, b;
+            chunk(u, a, b, nullptr);
+            a = opaque(a);
+            b = opaque(b);
+            part = opaque(part + (wsum(a.x, b.x) + wsum(a.y, b.y)));
+            part = opaque(part + (wsum(a.z, b.z) + wsum(a.w, b.w)));
+          }
+        }
+      } else {
+        Resid Rn = R;
+        Rn.a = an;
+        sweep<true>(trow, drow, lo, hi, vec4, [&](float t, float d, int, bool ok) {
+          const double w = Rn.w(t, d, L.tbl);
+          part += ok ? w : 0.0;
+        });
+      }
+      part = block_sum(part, L.sh);
+      if (threadIdx.x < 2)
+        ll_put(tm, int(threadIdx.x),
+               threadIdx.x == 0 ? uint32_t(__double2loint(part)) : uint32_t(__double2hiint(part)), L.s_words);
+      ll_gather(tm, 2, L.s_words);
+      const double pw = lane < tm.W ? words_to_double(L.s_words[2 * lane], L.s_words[2 * lane + 1]) : 0.0;
+      const double F = lane_d(row_sum(pw), 0);
+      if (F > 0.0) {
+        R.a = an;
+        B = F;
+        if (threadIdx.x < tm.W) L.s_slice[threadIdx.x] = pw;
+      }
+      Sq -= qx;
+      ++k;
+      if (k < min(nkk, kKids))
+        c = __builtin_amdgcn_readfirstlane(L.s_kid[k]);
+      else if (nkk > kKids)
+        c = next_child(par, N, v, c, L.s_int);  // past the listed children
+      else
+        c = -1;
+    }
+    __syncthreads();  // s_slice written; this visit's lists no longer read
+    if (accepted >= 0) {
+      v = __builtin_amdgcn_readfirstlane(accepted);  // uniform: row addresses stay scalar
+      continue;
+    }
+
+    // Stop at v: inverse-CDF draw from the residual (p itself when a == 0).
+    // The slice sums of the last pass locate the slice; its owner scans it.
+    const double u = double(p.uniforms[2 * size_t(nbeg + v) + 1]);
+    double total = 0.0;
+    for (int w = 0; w < tm.W; ++w) total += L.s_slice[w];
+    const double thr = u * total;
+    int finder = -1, last_w = -1;
+    double pre = 0.0, base_w = 0.0, last_pre = 0.0;
+    for (int w = 0; w < tm.W; ++w) {
+      const double sw = L.s_slice[w];
+      if (sw > 0.0) {
+        last_w = w;
+        last_pre = pre;
+      }
+      if (finder < 0 && pre <= thr && thr < pre + sw) {
+        finder = w;
+        base_w = pre;
+      }
+      pre += sw;
+    }
+    if (finder < 0) {
+      finder = last_w;
+      base_w = last_pre;
+    }
+    finder = __builtin_amdgcn_readfirstlane(finder);
+    if (finder == member) {
+      slice_search(trow, drow, lo, hi, R, thr - base_w, L.tbl, L.sh, L.s_int);
+      if (threadIdx.x == 0) p.next_token[nbeg + v] = *L.s_int;
+    } else if (finder < 0 && member == 0 && threadIdx.x == 0) {
+      p.next_token[nbeg + v] = 0;  // no mass in any slice (not reachable with finite logits)
+    }
+    if (member == 0)
+      for (int i = threadIdx.x; i < N; i += kThreads)
+        if (i != v) p.next_token[nbeg + i] = -1;
+    return;
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 4) void sample_kernel(SampleParams p) {
   __shared__ double tbl[64];
+  __shared__ double tbl1k[1024];
   __shared__ double sh[2 * kWaves];
+  __shared__ float shf[2 * kWaves];
   __shared__ double s_slice[kMaxTeam];
-  __shared__ double s_part[4 * kMaxTeam];
+  __shared__ uint32_t s_words[6 * kMaxTeam];
+  __shared__ int s_kid[kKids];
+  __shared__ float s_kt[kKids], s_kd[kKids], s_ku[kKids];
+  __shared__ int s_par[kParLds], s_tok[kParLds];
+  __shared__ float4 s_res[2 * kLdsCh * kThreads];
   __shared__ float shv[kWaves];
   __shared__ int shi[kWaves];
-  __shared__ int s_int;
+  __shared__ int s_nk, s_int;
 
   // Team placement: block b runs on XCD b % 8; the W members of a team are
   // consecutive slots of one XCD.
@@ -463,29 +983,27 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleParams p) {
   if (r >= p.B) return;  // padding block: belongs to no team
 
   for (int j = threadIdx.x; j < 64; j += kThreads) tbl[j] = exp2(double(j) / 64.0);
+  for (int j = threadIdx.x; j < 1024; j += kThreads) tbl1k[j] = exp2(double(j) / 1024.0);
 
-  Team tm;
-  tm.ctr = p.team_ctr + r;
-  tm.target = 0;
-  tm.W = p.W;
-  tm.member = member;
-  tm.phase = 0;
-  tm.part = p.part + size_t(r) * 2 * p.W * p.part_stride;
-  tm.stride = p.part_stride;
-  tm.status = p.status;
-
-  const int nbeg = p.node_indptr[r];
-  const int N = p.node_indptr[r + 1] - nbeg;
+  // Per-request values are wave-uniform: keep them (and the row addresses
+  // derived from them) in scalar registers.
+  const int nbeg = __builtin_amdgcn_readfirstlane(p.node_indptr[r]);
+  const int N = __builtin_amdgcn_readfirstlane(p.node_indptr[r + 1]) - nbeg;
   const int V = p.V;
-  const float T = p.temperature[r];
+  const float T = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(p.temperature[r])));
   if (N <= 0 || N > p.max_nodes) {
     if (N != 0 && threadIdx.x == 0 && member == 0) raise_status(p.status, TV_DEV_SHAPE);
     return;  // uniform for the whole team: nobody waits on anybody
   }
-  const int* par = p.parent + nbeg;
-  const int* tok = p.tokens + nbeg;
+  // Parents in LDS when they fit (child scans then cost no global round trip).
+  const Parents par{p.parent + nbeg, s_par, p.tokens + nbeg, s_tok, N <= kParLds};
+  if (par.lds)
+    for (int i = threadIdx.x; i < N; i += kThreads) {
+      s_par[i] = par.g[i];
+      s_tok[i] = par.gtok[i];
+    }
   const bool vec4 = (V & 3) == 0;
-  __syncthreads();  // table ready
+  __syncthreads();  // tables and parents ready
 
   if (!(T >= 0.f) || (T > 0.f && p.d == nullptr)) {
     if (member == 0) {
@@ -499,6 +1017,7 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleParams p) {
   }
 
   if (T == 0.f) {
+    Barrier bar{reinterpret_cast<uint32_t*>(p.req + size_t(r) * kReqBytes), 0u, p.W, p.status};
     // Greedy exact match: argmax of every row, then the match flags.
     for (int i = member; i < N; i += p.W) {
       const float* row = p.t + size_t(nbeg + i) * V;
@@ -512,12 +1031,12 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleParams p) {
         bi = take ? y : bi;
       });
       if (bad) raise_status(p.status, TV_DEV_LOGITS);
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        const float v2 = __shfl_xor(bv, off, kWave);
-        const int i2 = __shfl_xor(bi, off, kWave);
-        am_combine(bv, bi, v2, i2);
-      }
+      am_combine(bv, bi, swz<1>(bv), swz_i<1>(bi));
+      am_combine(bv, bi, swz<2>(bv), swz_i<2>(bi));
+      am_combine(bv, bi, swz<4>(bv), swz_i<4>(bi));
+      am_combine(bv, bi, swz<8>(bv), swz_i<8>(bi));
+      am_combine(bv, bi, swz<16>(bv), swz_i<16>(bi));
+      am_combine(bv, bi, lane_f(bv, 32), __builtin_amdgcn_readlane(bi, 32));
       const int wave = threadIdx.x / kWave;
       if ((threadIdx.x & 63) == 0) {
         shv[wave] = bv;
@@ -534,7 +1053,7 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleParams p) {
       }
       __syncthreads();
     }
-    team_sync(tm);
+    barrier_sync(bar);
     for (int i = member * kThreads + threadIdx.x; i < N; i += p.W * kThreads) {
       int8_t f = 0;
       if (i == 0) {
@@ -546,145 +1065,52 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleParams p) {
         } else {
           const int ntp = __hip_atomic_load(p.next_token + nbeg + pi, __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT);
-          f = (tok[i] == ntp) ? 1 : 0;
+          f = (par.tok(i) == ntp) ? 1 : 0;
         }
       }
       p.flag[nbeg + i] = f;
     }
-    team_exit(tm);
+    barrier_exit(bar);
     return;
   }
 
-  // Sampled walk (T > 0).
-  if (member == 0) {
-    for (int i = threadIdx.x; i < N; i += kThreads) {
-      p.flag[nbeg + i] = i == 0 ? 1 : 0;
-      p.next_token[nbeg + i] = -1;
-    }
-  }
+  // Sampled walk (T > 0). Member slices in float4 units when V % 4 == 0.
+  Team tm;
+  char* const rq = p.req + size_t(r) * kReqBytes;
+  uint32_t* const seq_word = reinterpret_cast<uint32_t*>(rq + 4);
+  tm.slots = reinterpret_cast<uint64_t*>(rq + kReqSlotsOff);
+  tm.seq = *seq_word;
+  tm.phase = 0;
+  tm.W = p.W;
+  tm.member = member;
+  tm.status = p.status;
   const double invT = 1.0 / double(T);
-  int slice = (V + p.W - 1) / p.W;
-  slice = (slice + 3) / 4 * 4;
-  const int lo = min(V, member * slice);
-  const int hi = min(V, lo + slice);
-
-  int v = 0;
-  for (int depth_guard = 0; depth_guard <= N; ++depth_guard) {
-    const float* trow = p.t + size_t(nbeg + v) * V;
-    const float* drow = p.d + size_t(nbeg + v) * V;
-    // Stats pass: (max, sum exp) of t/T and d/T over the member's slice.
-    double mt = -INFINITY, st = 0.0, md = -INFINITY, sd = 0.0;
-    bool bad = false;
-    slice_stats(trow, drow, lo, hi, vec4, invT, tbl, mt, st, md, sd, bad);
-    if (bad) raise_status(p.status, TV_DEV_LOGITS);
-    block_ms(mt, st, sh, tbl);
-    block_ms(md, sd, sh, tbl);
-    if (threadIdx.x == 0) {
-      double* ms = member_slot(tm, member);
-      put_partial(ms, 0, mt);
-      put_partial(ms, 1, st);
-      put_partial(ms, 2, md);
-      put_partial(ms, 3, sd);
-    }
-    team_sync(tm);
-    gather_partials(tm, 4, s_part);
-    double Mt = -INFINITY, Zt = 0.0, Md = -INFINITY, Zd = 0.0;
-    for (int w = 0; w < p.W; ++w) {
-      Mt = fmax(Mt, s_part[4 * w]);
-      Md = fmax(Md, s_part[4 * w + 2]);
-    }
-    for (int w = 0; w < p.W; ++w) {  // fixed member order
-      if (s_part[4 * w] != -INFINITY) Zt += s_part[4 * w + 1] * exp_nonpos(s_part[4 * w] - Mt, tbl);
-      if (s_part[4 * w + 2] != -INFINITY) Zd += s_part[4 * w + 3] * exp_nonpos(s_part[4 * w + 2] - Md, tbl);
-    }
-    // Slice sums of p (for a draw at a leaf): s_w exp(m_w - Mt) / Zt.
-    if (threadIdx.x < p.W) {
-      const double m0 = s_part[4 * threadIdx.x], s0 = s_part[4 * threadIdx.x + 1];
-      s_slice[threadIdx.x] = m0 == -INFINITY ? 0.0 : s0 * exp_nonpos(m0 - Mt, tbl) / Zt;
-    }
-    tm.phase++;
-    __syncthreads();
-
-    Resid R{invT, Mt, 1.0 / Zt, Md, 1.0 / Zd, 0.0};
-    double B = 1.0, S = 1.0;
-    int accepted = -1;
-    for (int c = next_child(par, N, v, v, &s_int); c >= 0; c = next_child(par, N, v, c, &s_int)) {
-      int x = tok[c];
-      if (x < 0 || x >= V) {
-        if (threadIdx.x == 0 && member == 0) raise_status(p.status, TV_DEV_SHAPE);
-        x = 0;
-      }
-      const double px = R.p(trow[x], tbl);
-      const double qx = R.q(drow[x], tbl);
-      double pj = px - R.a * qx;
-      pj = (pj > 0.0 ? pj : 0.0) / B;
-      const double qj = qx / S;
-      const double ratio = qj > 0.0 ? pj / qj : (pj > 0.0 ? INFINITY : 0.0);
-      const double u = double(p.uniforms[2 * size_t(nbeg + c)]);
-      if (u < ratio) {
-        accepted = c;
-        if (member == 0 && threadIdx.x == 0) p.flag[nbeg + c] = 1;
-        break;
-      }
-      // Rejected: one residual pass at a' = a + B/S.
-      Resid Rn = R;
-      Rn.a = R.a + B / S;
-      double part = 0.0;
-      sweep<true>(trow, drow, lo, hi, vec4, [&](float t, float d, int, bool ok) {
-        const double w = Rn.w(t, d, tbl);
-        part += ok ? w : 0.0;
-      });
-      part = block_sum(part, sh);
-      if (threadIdx.x == 0) put_partial(member_slot(tm, member), 0, part);
-      team_sync(tm);
-      gather_partials(tm, 1, s_part);
-      double F = 0.0;
-      for (int w = 0; w < p.W; ++w) F += s_part[w];
-      if (F > 0.0) {
-        R.a = Rn.a;
-        B = F;
-        if (threadIdx.x < p.W) s_slice[threadIdx.x] = s_part[threadIdx.x];
-      }
-      tm.phase++;
-      S -= qx;
-      __syncthreads();
-    }
-    if (accepted >= 0) {
-      v = accepted;
-      continue;
-    }
-
-    // Stop at v: inverse-CDF draw from the residual (p itself when a == 0).
-    // The slice sums of the last pass locate the slice; its owner scans it.
-    const double u = double(p.uniforms[2 * size_t(nbeg + v) + 1]);
-    double total = 0.0;
-    for (int w = 0; w < p.W; ++w) total += s_slice[w];
-    const double thr = u * total;
-    int finder = -1, last_w = -1;
-    double pre = 0.0, base_w = 0.0, last_pre = 0.0;
-    for (int w = 0; w < p.W; ++w) {
-      const double sw = s_slice[w];
-      if (sw > 0.0) {
-        last_w = w;
-        last_pre = pre;
-      }
-      if (finder < 0 && pre <= thr && thr < pre + sw) {
-        finder = w;
-        base_w = pre;
-      }
-      pre += sw;
-    }
-    if (finder < 0) {
-      finder = last_w;
-      base_w = last_pre;
-    }
-    if (finder == member) {
-      slice_search(trow, drow, lo, hi, R, thr - base_w, tbl, sh, &s_int);
-      if (threadIdx.x == 0) p.next_token[nbeg + v] = s_int;
-    }
-    break;
+  // Vectorised rows are split in chunks of 1024 logits (kThreads float4),
+  // member m taking chunks [m C / W, (m + 1) C / W) of the C in a row, so
+  // only the row's last chunk is ever partial.
+  int lo, hi, nch = 0;
+  const int C = (V + 4 * kThreads - 1) / (4 * kThreads);
+  if (vec4) {
+    const int c0 = member * C / p.W, c1 = (member + 1) * C / p.W;
+    nch = c1 - c0;
+    lo = min(V, 4 * kThreads * c0);
+    hi = min(V, 4 * kThreads * c1);
+  } else {
+    const int slice = (V + p.W - 1) / p.W;
+    lo = min(V, member * slice);
+    hi = min(V, lo + slice);
   }
-  team_exit(tm);
+  WalkLds L{tbl, tbl1k, sh, shf, s_slice, s_words, s_kid, s_kt, s_kd, s_ku, &s_nk, &s_int, s_res};
+  const bool resident = vec4 && (C + p.W - 1) / p.W <= kResCh;  // the same for every member
+  if (resident)
+    walk<true>(p, tm, nbeg, N, par, invT, lo, hi, nch, vec4, L);
+  else
+    walk<false>(p, tm, nbeg, N, par, invT, lo, hi, nch, vec4, L);
+  // The request's sequence moves past every tag this call used. Every
+  // member read the old value before its first publish, and this store
+  // follows member 0's last gather, which saw every member's last publish.
+  if (member == 0 && threadIdx.x == 0 && p.W > 1)
+    __hip_atomic_store(seq_word, tm.seq + uint32_t(tm.phase), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
@@ -694,13 +1120,8 @@ bool plan_sample(const tv_sample_desc& d, SamplePlan* out) {
     return false;
   SamplePlan pl{};
   pl.threads = kThreads;
-  pl.part_stride = 4;
-  size_t off = kHeaderBytes;
-  pl.off_team_ctr = off;
-  off = align256(off + size_t(d.batch) * sizeof(uint32_t));
-  pl.off_part = off;
-  off = align256(off + size_t(d.batch) * 2 * kMaxTeam * pl.part_stride * sizeof(double));
-  pl.total_bytes = off;
+  pl.off_req = kHeaderBytes;
+  pl.total_bytes = kHeaderBytes + size_t(d.batch) * kReqBytes;
   *out = pl;
   return true;
 }
@@ -746,13 +1167,11 @@ hipError_t launch_sample(const tv_sample_desc& d, const SamplePlan& pl, const Sa
   p.next_token = a.next_token;
   char* ws = static_cast<char*>(a.workspace);
   p.status = reinterpret_cast<uint32_t*>(ws);
-  p.team_ctr = reinterpret_cast<uint32_t*>(ws + pl.off_team_ctr);
-  p.part = reinterpret_cast<double*>(ws + pl.off_part);
+  p.req = ws + pl.off_req;
   p.B = d.batch;
   p.V = d.vocab;
   p.W = W;
   p.max_nodes = d.max_nodes;
-  p.part_stride = pl.part_stride;
   const dim3 grid(unsigned(grid_for(W))), block(kThreads);
   if (W == 1) {
     hipLaunchKernelGGL(sample_kernel, grid, block, 0, stream, p);

@@ -33,8 +33,8 @@ struct AttnPlan {
 
 struct SamplePlan {
   int threads;        // threads per workgroup
-  int part_stride;    // doubles per (team, member, parity) partial slot
-  size_t off_team_ctr, off_part, total_bytes;
+  size_t off_req;     // per-request blocks (barrier counter, tag sequence, exchange slots)
+  size_t total_bytes;
 };
 
 bool plan_attn(const tv_attn_desc& d, AttnPlan* out);
