@@ -35,7 +35,7 @@
 //    a leaf) locate the slice of the correction/bonus draw, so the draw
 //    rescans one slice only.
 //  * Arithmetic is fp64 (logits widened exactly). Vocabulary sums use a
-//    table exp (2^(j/1024) in LDS, cubic polynomial, the power of two set by
+//    table exp (2^(j/256) in LDS, quartic polynomial, the power of two set by
 //    ldexp) on an argument formed by one fma from the fp32 logit; single
 //    values that decide (p(x), q(x), rescale factors) use a 64-entry table
 //    with a degree-5 polynomial (~1 ulp). Decisions therefore agree with an
@@ -55,7 +55,7 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxTeam = 16;             // members per team (one XCD holds a team)
 constexpr int kResCh = 10;               // resident chunks (1024 logits) per row per member
-constexpr int kLdsCh = 2;                // of which the last kLdsCh live in LDS
+constexpr int kLdsCh = 3;                // of which the last kLdsCh live in LDS
 constexpr int kRegCh = kResCh - kLdsCh;  // and the rest in registers
 constexpr int kParLds = 1024;            // parents and tokens staged in LDS up to this many rows
 constexpr int kKids = 64;                // children listed (and prefetched) per visit
@@ -103,28 +103,33 @@ __device__ inline double exp_nonpos(double a, const double* tbl) {
   return ldexp(tbl[ni & 63] * p, ni >> 6);
 }
 
-// exp for vocabulary sums, taking z = x * 1024/ln2 (x <= 0): z = 1024 k + j
-// + f with |f| <= 1/2 (rounding by the 1.5 * 2^52 shift, whose low word is
-// then the integer), e^x = 2^k * 2^(j/1024) * e^(f ln2/1024), the last
-// factor a cubic (truncation below 6e-16 for |f ln2/1024| <= 3.4e-4).
-// z below -1100 * 1024 (e^x < 2^-1100, and -inf) gives exactly 0.
-// tbl[j] = 2^(j/1024).
-constexpr double kZScale = 1024.0 / 0.69314718055994530942;
-constexpr double kZC1 = 0.69314718055994530942 / 1024.0;
+// exp for vocabulary sums, taking z = x * 256/ln2 (x <= 0): z = 256 k + j +
+// f with |f| <= 1/2 (rounding by the 1.5 * 2^52 shift, whose low word is
+// then the integer), e^x = 2^k * 2^(j/256) * e^(f ln2/256), the last factor
+// a quartic (truncation below 4e-17 for |f ln2/256| <= 1.4e-3).
+// z below -1100 * 256 (e^x < 2^-1100, and -inf) gives exactly 0.
+// tbl[j] = 2^(j/256).
+constexpr int kZBits = 8;
+constexpr int kZTable = 1 << kZBits;
+constexpr double kZScale = double(kZTable) / 0.69314718055994530942;
+constexpr double kZC1 = 0.69314718055994530942 / double(kZTable);
 constexpr double kZC2 = kZC1 * kZC1 / 2.0;
 constexpr double kZC3 = kZC1 * kZC1 * kZC1 / 6.0;
+constexpr double kZC4 = kZC1 * kZC1 * kZC1 * kZC1 / 24.0;
+constexpr double kZFloor = -1100.0 * kZTable;
 constexpr double kShift52 = 6755399441055744.0;  // 1.5 * 2^52
 
 __device__ inline double exp_z(double z, const double* tbl) {
-  z = fmax(z, -1100.0 * 1024.0);
+  z = fmax(z, kZFloor);
   const double nd = z + kShift52;
   const int n = __double2loint(nd);
   const double f = z - (nd - kShift52);
-  double q = fma(f, kZC3, kZC2);
+  double q = fma(f, kZC4, kZC3);
+  q = fma(q, f, kZC2);
   q = fma(q, f, kZC1);
   q *= f;
-  const double tj = tbl[n & 1023];
-  return ldexp(fma(tj, q, tj), n >> 10);
+  const double tj = tbl[n & (kZTable - 1)];
+  return ldexp(fma(tj, q, tj), n >> kZBits);
 }
 
 // Empty volatile asm on a value: the value is taken to be produced (or
@@ -150,20 +155,21 @@ __device__ inline double exp4_sum(float4 x, double A, double b, const double* tb
   int n[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const double z = fmax(fma(double(xs[e]), A, b), -1100.0 * 1024.0);
+    const double z = fmax(fma(double(xs[e]), A, b), kZFloor);
     const double nd = z + kShift52;
     n[e] = __double2loint(nd);
     f[e] = z - (nd - kShift52);
   }
 #pragma unroll
-  for (int e = 0; e < 4; ++e) tj[e] = tbl[n[e] & 1023];
+  for (int e = 0; e < 4; ++e) tj[e] = tbl[n[e] & (kZTable - 1)];
   double s = 0.0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    double q = fma(f[e], kZC3, kZC2);
+    double q = fma(f[e], kZC4, kZC3);
+    q = fma(q, f[e], kZC2);
     q = fma(q, f[e], kZC1);
     q *= f[e];
-    s += ldexp(fma(tj[e], q, tj[e]), n[e] >> 10);
+    s += ldexp(fma(tj[e], q, tj[e]), n[e] >> kZBits);
   }
   return opaque(s);
 }
@@ -592,7 +598,7 @@ __device__ int next_child(const Parents& par, int N, int v, int after, int* s_c)
 
 struct WalkLds {
   double* tbl;        // 2^(j/64)
-  double* tbl1k;      // 2^(j/1024)
+  double* tblz;       // 2^(j/256)
   double* sh;         // [2 * kWaves]
   float* shf;         // [2 * kWaves]
   double* s_slice;    // [kMaxTeam] slice sums of the last pass
@@ -647,7 +653,7 @@ __device__ __attribute__((always_inline)) inline void walk(
   const int V = p.V;
   const int member = tm.member;
   const int lane = threadIdx.x & 63;
-  const double A = invT * kZScale;  // z = (t/T - M/T) * 1024/ln2 = fma(t, A, -M * A)
+  const double A = invT * kZScale;  // z = (t/T - M/T) * 256/ln2 = fma(t, A, -M * A)
   Slice<RES> S;
   // Flags: member 0 alone writes them (initial values here, accepted nodes
   // later, in program order). next_token is written once per node at the
@@ -766,13 +772,13 @@ __device__ __attribute__((always_inline)) inline void walk(
           if (u < nch) {
             float4 a, b;
             chunk(u, a, b, nullptr);
-            st += exp4_sum(a, A, bt, L.tbl1k);
-            sd += exp4_sum(b, A, bd, L.tbl1k);
+            st += exp4_sum(a, A, bt, L.tblz);
+            sd += exp4_sum(b, A, bd, L.tblz);
           }
         }
       };
-      group(0, kRegCh / 2);
-      group(kRegCh / 2, kRegCh);
+      group(0, (kRegCh + 1) / 2);
+      group((kRegCh + 1) / 2, kRegCh);
       group(kRegCh, kResCh);
       bad = !(chk == 0.f);
     } else {
@@ -789,8 +795,8 @@ __device__ __attribute__((always_inline)) inline void walk(
           sd = md == -INFINITY ? 0.0 : sd * exp_nonpos((double(md) - double(d)) * invT, L.tbl);
           md = d;
         }
-        st += exp_z(fma(double(t), A, -double(mt) * A), L.tbl1k);
-        sd += exp_z(fma(double(d), A, -double(md) * A), L.tbl1k);
+        st += exp_z(fma(double(t), A, -double(mt) * A), L.tblz);
+        sd += exp_z(fma(double(d), A, -double(md) * A), L.tblz);
       });
     }
     if (bad) raise_status(p.status, TV_DEV_LOGITS);
@@ -872,7 +878,7 @@ __device__ __attribute__((always_inline)) inline void walk(
         const double bt = -double(Mt32) * A, bd = -double(Md32) * A;
         const double ca = R.invZt, cb = -an * R.invZd;
         auto wsum = [&](float t, float d) __attribute__((always_inline)) {
-          const double w = fma(cb, exp_z(fma(double(d), A, bd), L.tbl1k), ca * exp_z(fma(double(t), A, bt), L.tbl1k));
+          const double w = fma(cb, exp_z(fma(double(d), A, bd), L.tblz), ca * exp_z(fma(double(t), A, bt), L.tblz));
           return w > 0.0 ? w : 0.0;
         };
 #pragma unroll
@@ -961,7 +967,7 @@ __device__ __attribute__((always_inline)) inline void walk(
 
 __global__ __launch_bounds__(kThreads, 4) void sample_kernel(SampleParams p) {
   __shared__ double tbl[64];
-  __shared__ double tbl1k[1024];
+  __shared__ double tblz[kZTable];
   __shared__ double sh[2 * kWaves];
   __shared__ float shf[2 * kWaves];
   __shared__ double s_slice[kMaxTeam];
@@ -983,7 +989,7 @@ __global__ __launch_bounds__(kThreads, 4) void sample_kernel(SampleParams p) {
   if (r >= p.B) return;  // padding block: belongs to no team
 
   for (int j = threadIdx.x; j < 64; j += kThreads) tbl[j] = exp2(double(j) / 64.0);
-  for (int j = threadIdx.x; j < 1024; j += kThreads) tbl1k[j] = exp2(double(j) / 1024.0);
+  for (int j = threadIdx.x; j < kZTable; j += kThreads) tblz[j] = exp2(double(j) / double(kZTable));
 
   // Per-request values are wave-uniform: keep them (and the row addresses
   // derived from them) in scalar registers.
@@ -1100,7 +1106,7 @@ __global__ __launch_bounds__(kThreads, 4) void sample_kernel(SampleParams p) {
     lo = min(V, member * slice);
     hi = min(V, lo + slice);
   }
-  WalkLds L{tbl, tbl1k, sh, shf, s_slice, s_words, s_kid, s_kt, s_kd, s_ku, &s_nk, &s_int, s_res};
+  WalkLds L{tbl, tblz, sh, shf, s_slice, s_words, s_kid, s_kt, s_kd, s_ku, &s_nk, &s_int, s_res};
   const bool resident = vec4 && (C + p.W - 1) / p.W <= kResCh;  // the same for every member
   if (resident)
     walk<true>(p, tm, nbeg, N, par, invT, lo, hi, nch, vec4, L);
