@@ -227,3 +227,22 @@ def test_more_children_than_listed():
     inp = make_sampler_inputs(rng, rng, rng, [star_tree(151), star_tree(90)], 4096, [1.0, 2.0],
                               mode="independent")
     _compare(inp, _run(inp, max_depth=1))
+
+
+@pytest.mark.parametrize("V", [8192, 8196, 151936])
+def test_greedy_split_rows_and_ties(V):
+    """T = 0 with rows split over team members (trees with fewer rows than the
+    team): equal maxima in different chunks and members resolve to the lowest
+    index, and the last logit of a partial final chunk can win."""
+    rng = np.random.default_rng(V)
+    trees = [chain_tree(1), chain_tree(2), random_tree(rng, 5, depth_cap=3), random_tree(rng, 23, depth_cap=6)]
+    inp = make_sampler_inputs(rng, rng, rng, trees, V, [0.0] * 4)
+    t = inp.target_logits
+    t[0, [100, V // 2 + 3, V - 5]] = 40.0          # ties: lowest index wins
+    t[1, V - 1] = 40.5                              # last logit of the row
+    t[2, [V - 1, V - 2]] = 40.0                     # tie at the row end
+    t[3:, [17, V - 17]] = 40.0
+    got = _run(inp, max_depth=6)
+    assert got["next_token"][0] == 100
+    assert got["next_token"][1] == V - 1
+    _compare(inp, got)

@@ -336,6 +336,11 @@ __device__ inline float row_max(float v) {
   return v;
 }
 
+template <int CTRL>
+__device__ inline int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+
 // Wave-wide, wave-uniform results: the four rows joined in row order.
 __device__ inline double wave_sum(double v) {
   v = row_sum(v);
@@ -394,11 +399,33 @@ __device__ inline void block_ms2(float& mt, double& st, float& md, double& sd, d
   md = Md;
 }
 
-// argmax with the lowest index on ties.
+// argmax with the lowest index on ties (a total order on (value, index),
+// so any combination order gives the same result).
 __device__ inline void am_combine(float& v, int& i, float v2, int i2) {
   const bool take = v2 > v || (v2 == v && i2 < i);
   v = take ? v2 : v;
   i = take ? i2 : i;
+}
+
+// Block-wide argmax of per-thread (v, i); every thread returns it.
+__device__ inline void block_argmax(float& v, int& i, float* shv, int* shi) {
+  am_combine(v, i, dpp_f<kDppXor1>(v), dpp_i<kDppXor1>(i));
+  am_combine(v, i, dpp_f<kDppXor2>(v), dpp_i<kDppXor2>(i));
+  am_combine(v, i, dpp_f<kDppHalfMirror>(v), dpp_i<kDppHalfMirror>(i));
+  am_combine(v, i, dpp_f<kDppMirror>(v), dpp_i<kDppMirror>(i));
+  float bv = lane_f(v, 0);
+  int bi = __builtin_amdgcn_readlane(i, 0);
+  for (int l = 16; l < kWave; l += 16) am_combine(bv, bi, lane_f(v, l), __builtin_amdgcn_readlane(i, l));
+  const int wave = threadIdx.x / kWave;
+  if ((threadIdx.x & 63) == 0) {
+    shv[wave] = bv;
+    shi[wave] = bi;
+  }
+  __syncthreads();
+  v = shv[0];
+  i = shi[0];
+  for (int w = 1; w < kWaves; ++w) am_combine(v, i, shv[w], shi[w]);
+  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
@@ -965,6 +992,145 @@ __device__ __attribute__((always_inline)) inline void walk(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Greedy argmax of every row (T = 0) for 4-aligned rows. The request's
+// N x C units (row, chunk of 1024 logits) are split evenly over the team in
+// row-major order and streamed kGreedyBatch units at a time (one 16-byte
+// load per thread per unit, all of a batch in flight). A row held whole by
+// one member is written directly; a row shared by neighbouring members is
+// finished by the member holding its first unit, from the partial argmaxes
+// every member publishes for its first and last row.
+constexpr int kGreedyBatch = 24;
+
+__device__ __attribute__((always_inline)) inline void greedy_rows(const SampleParams& p, Team& tm, int nbeg,
+                                                                  int N, float* shv, int* shi,
+                                                                  uint32_t* s_words) {
+  const int V = p.V;
+  const int C = (V + 4 * kThreads - 1) / (4 * kThreads);
+  const long long U = (long long)N * C;
+  const int W = tm.W;
+  auto start = [&](int m) { return U * m / W; };
+  const long long g0 = start(tm.member), g1 = start(tm.member + 1);
+  const int row_first = int(g0 / C), row_last = g0 < g1 ? int((g1 - 1) / C) : -1;
+  const bool first_shared = g0 < g1 && g0 % C != 0;
+  const bool last_shared = g0 < g1 && g1 % C != 0;
+  float fv = -INFINITY, lv = -INFINITY;  // member partials of the shared first / last row
+  int fi = 0x7fffffff, li = 0x7fffffff;
+
+  // Four running argmaxes per thread, one per float4 lane (independent
+  // dependency chains); bi[e] holds the chunk offset of the lane's float4,
+  // so the token is bi[e] + e. Merged with lowest-index ties at row end.
+  float bv[4];
+  int bi[4];
+  auto reset = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bv[e] = -INFINITY;
+      bi[e] = 0x7fffffff;
+    }
+  };
+  reset();
+  float chk = 0.f;  // t * 0 is 0 for finite t, NaN otherwise
+  int cur = row_first;
+  auto finish = [&](int row) __attribute__((always_inline)) {
+    float v = bv[0];
+    int i = bi[0];
+#pragma unroll
+    for (int e = 1; e < 4; ++e) am_combine(v, i, bv[e], bi[e] == 0x7fffffff ? bi[e] : bi[e] + e);
+    block_argmax(v, i, shv, shi);
+    const bool is_first = row == row_first && first_shared, is_last = row == row_last && last_shared;
+    if (is_first) {
+      fv = v;
+      fi = i;
+    }
+    if (is_last) {
+      lv = v;
+      li = i;
+    }
+    if (!is_first && !is_last && threadIdx.x == 0)
+      __hip_atomic_store(p.next_token + nbeg + row, i == 0x7fffffff ? 0 : i, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    reset();
+  };
+
+  const int voff = int(threadIdx.x) * 16;
+  const int tail = V - 4 * kThreads * (C - 1);  // logits in a row's last chunk
+  for (long long u0 = g0; u0 < g1; u0 += kGreedyBatch) {
+    const int rem = g1 - u0 < kGreedyBatch ? int(g1 - u0) : kGreedyBatch;  // units of this batch
+    const int row0 = int(u0 / C), ch0 = int(u0 - (long long)row0 * C);
+    int ch = ch0;
+    const float* rp = p.t + size_t(nbeg + row0) * V;
+    float4 buf[kGreedyBatch];
+#pragma unroll
+    for (int j = 0; j < kGreedyBatch; ++j) {  // past the batch: an empty range, no memory access
+      const int nb = j < rem ? 4 * (ch == C - 1 ? tail : 4 * kThreads) : 0;
+      buf[j] = load4_bounded(rp + 4 * kThreads * ch, nb, voff);
+      if (++ch == C) {
+        ch = 0;
+        rp += V;
+      }
+    }
+    int row = row0;
+    ch = ch0;
+#pragma unroll
+    for (int j = 0; j < kGreedyBatch; ++j) {
+      if (j < rem) {
+        if (row != cur) {
+          finish(cur);
+          cur = row;
+        }
+        const int y0 = 4 * kThreads * ch + 4 * int(threadIdx.x);
+        float a[4] = {buf[j].x, buf[j].y, buf[j].z, buf[j].w};
+        chk = fmaf(a[0], 0.f, fmaf(a[1], 0.f, fmaf(a[2], 0.f, fmaf(a[3], 0.f, chk))));
+        if (ch == C - 1 && tail < 4 * kThreads) {  // the row's partial last chunk
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a[e] = 4 * int(threadIdx.x) + e < tail ? a[e] : -INFINITY;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool take = a[e] > bv[e];  // ascending offsets per lane: ties keep the first
+          bv[e] = take ? a[e] : bv[e];
+          bi[e] = take ? y0 : bi[e];
+        }
+      }
+      if (++ch == C) {
+        ch = 0;
+        ++row;
+      }
+    }
+  }
+  const bool bad = !(chk == 0.f);
+  if (g0 < g1) finish(cur);
+  if (bad) raise_status(p.status, TV_DEV_LOGITS);
+
+  // Shared rows, from the partials of the members covering them (the
+  // match-flag phase reads next_token only after the team barrier, whose
+  // release/acquire orders every member's stores before it).
+  if (W > 1) {
+    if (threadIdx.x < 4) {
+      const uint32_t w4[4] = {__float_as_uint(fv), uint32_t(fi), __float_as_uint(lv), uint32_t(li)};
+      uint32_t wv = w4[0];
+#pragma unroll
+      for (int k = 1; k < 4; ++k) wv = threadIdx.x == k ? w4[k] : wv;
+      ll_put(tm, int(threadIdx.x), wv, s_words);
+    }
+    ll_gather(tm, 4, s_words);
+    if (last_shared && g0 <= (long long)row_last * C && threadIdx.x == 0) {
+      // This member holds the first unit of its last row: fold in the later
+      // members that start inside that row.
+      float v = lv;
+      int i = li;
+      for (int m = tm.member + 1; m < W; ++m) {
+        const long long s0 = start(m), s1 = start(m + 1);
+        if (s0 >= (long long)(row_last + 1) * C) break;
+        if (s0 < s1) am_combine(v, i, __uint_as_float(s_words[4 * m]), int(s_words[4 * m + 1]));
+      }
+      __hip_atomic_store(p.next_token + nbeg + row_last, i == 0x7fffffff ? 0 : i, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 __global__ __launch_bounds__(kThreads, 4) void sample_kernel(SampleParams p) {
   __shared__ double tbl[64];
   __shared__ double tblz[kZTable];
@@ -1022,10 +1188,21 @@ __global__ __launch_bounds__(kThreads, 4) void sample_kernel(SampleParams p) {
     return;
   }
 
+  Team tm;
+  char* const rq = p.req + size_t(r) * kReqBytes;
+  uint32_t* const seq_word = reinterpret_cast<uint32_t*>(rq + 4);
+  tm.slots = reinterpret_cast<uint64_t*>(rq + kReqSlotsOff);
+  tm.seq = *seq_word;
+  tm.phase = 0;
+  tm.W = p.W;
+  tm.member = member;
+  tm.status = p.status;
+
   if (T == 0.f) {
-    Barrier bar{reinterpret_cast<uint32_t*>(p.req + size_t(r) * kReqBytes), 0u, p.W, p.status};
+    Barrier bar{reinterpret_cast<uint32_t*>(rq), 0u, p.W, p.status};
     // Greedy exact match: argmax of every row, then the match flags.
-    for (int i = member; i < N; i += p.W) {
+    if (vec4) greedy_rows(p, tm, nbeg, N, shv, shi, s_words);
+    for (int i = member; !vec4 && i < N; i += p.W) {
       const float* row = p.t + size_t(nbeg + i) * V;
       float bv = -INFINITY;
       int bi = 0x7fffffff;
@@ -1077,19 +1254,12 @@ __global__ __launch_bounds__(kThreads, 4) void sample_kernel(SampleParams p) {
       p.flag[nbeg + i] = f;
     }
     barrier_exit(bar);
+    if (member == 0 && threadIdx.x == 0 && p.W > 1 && tm.phase > 0)
+      __hip_atomic_store(seq_word, tm.seq + uint32_t(tm.phase), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
 
   // Sampled walk (T > 0). Member slices in float4 units when V % 4 == 0.
-  Team tm;
-  char* const rq = p.req + size_t(r) * kReqBytes;
-  uint32_t* const seq_word = reinterpret_cast<uint32_t*>(rq + 4);
-  tm.slots = reinterpret_cast<uint64_t*>(rq + kReqSlotsOff);
-  tm.seq = *seq_word;
-  tm.phase = 0;
-  tm.W = p.W;
-  tm.member = member;
-  tm.status = p.status;
   const double invT = 1.0 / double(T);
   // Vectorised rows are split in chunks of 1024 logits (kThreads float4),
   // member m taking chunks [m C / W, (m + 1) C / W) of the C in a row, so
