@@ -120,6 +120,90 @@ def cpu_baseline(cfg, budget_s=12.0):
                       f"attention + sampling walk + path, {dt:.1f} s"}
 
 
+def attn_sweep(names, rotate_bytes, reps):
+    """Attention alone on each named workload, launched back to back over
+    distinct copies of Q, K/V pages and outputs totalling >= rotate_bytes, so
+    the 256 MB Infinity Cache cannot serve a small layer from an earlier
+    launch. The launches of one pass over the copies are captured in one HIP
+    graph (host launch cost out of the way) and replayed `reps` times; the
+    output of the first copy is checked against an eager call after the
+    replays. Prints one JSON line per workload."""
+    import ctypes
+    import torch
+    import tree_verification_verify_amd as tv
+    from tree_verification_verify_amd import _lib
+    from workloads import make_config
+    from workloads.device import attention_tensors
+    lib = _lib.load()
+    stream = torch.cuda.Stream()
+    for name in names:
+        cfg = make_config(name, sampler=False)
+        inp = cfg.attn
+        a = attention_tensors(inp, "cuda")
+        desc = tv.attn_desc(inp.batch, inp.num_q_heads, inp.num_kv_heads, inp.head_dim,
+                            inp.max_nodes, inp.max_depth, inp.max_kv_len, inp.num_pages,
+                            inp.dtype)
+        abytes = attn_algorithmic_bytes(inp)
+        flops = attn_algorithmic_flops(cfg)
+        copy_bytes = (a["k_pages"].numel() + a["v_pages"].numel() + 2 * a["q"].numel()) * 2
+        n = max(1, -(-rotate_bytes // copy_bytes))
+        copies = []
+        for i in range(n):
+            k = a["k_pages"] if i == 0 else a["k_pages"].clone()
+            v = a["v_pages"] if i == 0 else a["v_pages"].clone()
+            q = a["q"] if i == 0 else a["q"].clone()
+            o = torch.empty_like(q)
+            ws = tv.alloc_workspace(tv.attn_workspace_size(desc))
+            copies.append((q, k, v, o, ws))
+        ref = torch.empty_like(a["q"])
+        tv.tree_verify_attn(desc, a["q"], a["k_pages"], a["v_pages"], a["page_indptr"],
+                            a["page_indices"], a["prefix_len"], a["node_indptr"], a["parent"],
+                            ref, copies[0][4])
+        torch.cuda.synchronize()
+        P = ctypes.c_void_p
+        calls = [(ctypes.byref(desc), P(q.data_ptr()), P(k.data_ptr()), P(v.data_ptr()),
+                  P(a["page_indptr"].data_ptr()), P(a["page_indices"].data_ptr()),
+                  P(a["prefix_len"].data_ptr()), P(a["node_indptr"].data_ptr()),
+                  P(a["parent"].data_ptr()), P(o.data_ptr()), P(ws.data_ptr()), ws.numel())
+                 for (q, k, v, o, ws) in copies]
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            for c in calls:  # warm-up outside the graph
+                st = lib.tree_verify_attn(*c, P(stream.cuda_stream))
+                if st != 0:
+                    raise SystemExit(f"{name}: tree_verify_attn returned {st}")
+            stream.synchronize()
+            with torch.cuda.graph(graph, stream=stream):
+                for c in calls:
+                    lib.tree_verify_attn(*c, P(stream.cuda_stream))
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):  # replay() launches on the current stream
+            graph.replay()
+            e0.record(stream)
+            for _ in range(reps):
+                graph.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        per_us = e0.elapsed_time(e1) * 1e3 / (reps * n)
+        err = (copies[0][3].float() - ref.float()).abs().max().item()
+        st, bits = tv.device_status(copies[0][4])
+        if st != 0 or err != 0.0:
+            raise SystemExit(f"{name}: graph replay differs from eager (max {err}) or status {st}/{bits}")
+        gbs = abytes / (per_us * 1e-6) / 1e9
+        tfl = flops / (per_us * 1e-6) / 1e12
+        print(json.dumps({
+            "workload": name, "batch": inp.batch, "tree_rows": inp.total_nodes,
+            "prefix": [int(inp.prefix_len.min()), int(inp.prefix_len.max())],
+            "copies": n, "reps": reps, "us_per_launch": per_us,
+            "nodes_per_s": inp.total_nodes / (per_us * 1e-6),
+            "algorithmic_bytes": abytes, "hbm_GBs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+            "algorithmic_flops": flops, "tflops": tfl, "mfma_frac_bf16": tfl / 2500.0}),
+            flush=True)
+        del copies, calls, graph
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -132,6 +216,10 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the workload, time a plain device copy of this many "
                          "bytes (calibrates the HBM byte counters)")
+    ap.add_argument("--attn-sweep", default="",
+                    help="comma-separated workloads: time tree_verify_attn alone on each, "
+                         "rotating >= --rotate-bytes of distinct copies (one JSON line each)")
+    ap.add_argument("--rotate-bytes", type=int, default=1 << 30)
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU; --gpus must be 1 "
@@ -140,6 +228,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.attn_sweep:
+        attn_sweep(args.attn_sweep.split(","), args.rotate_bytes, max(1, args.steps // 10))
+        return
     if args.copy_bytes:
         src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)

@@ -60,6 +60,7 @@ struct AttnParams {
   float* part_o;
   float* part_ml;
   uint32_t* counters;
+  int4* merge_desc;  // [nwg][3]: cut pair finished by each share (bf16 path)
   uint32_t* status;
   int B, Hq, Hkv, G, num_pages, max_nodes, max_kv_len, words;
   int rb_max, c_max, chunk_len, grid_real, nwg, lg_nwg;
@@ -251,102 +252,118 @@ __device__ inline int request_of(const int* off, int B, int x) {
   return lo;
 }
 
-// Merge kernel: workgroup w merges the cut pair whose first tile lies in
-// share w-1 and which has a tile in share w (a_{w-1} <= t0 < a_w <= the
-// first unit of its last tile), combining the partials of every share that
-// holds part of it, in share order (deterministic).
+// Merge descriptor of share w (logical workgroup lw of the streaming pass):
+// when the share's first pair was cut by earlier shares and ends in this
+// share, it records that pair (first share w0, nbeg, kv head, first row |
+// rows, first tile unit t0, units per tile, tiles | T); otherwise w0 = -1.
+// Every share writes its entry on every launch, so no entry outlives the
+// launch that wrote it.
+__device__ inline void write_merge_desc(const AttnParams& p, const int* off, int T, int a, int b,
+                                        int lw) {
+  int4 d0 = make_int4(-1, 0, 0, 0), d1 = make_int4(0, 0, 0, 0);
+  if (a < b) {
+    const int r = request_of(off, p.B, a);
+    const int nbeg = p.node_indptr[r];
+    const int N = p.node_indptr[r + 1] - nbeg;
+    const int L = p.prefix_len[r] + N;
+    const int R = N * p.G;
+    const int nt = ceil_div(L, kStage);
+    const PairAt q = pair_at(off[r], a, R, nt);
+    const int tlo = tiles_before(a, q.t0, q.c, nt);
+    const int thi = tiles_before(b, q.t0, q.c, nt);
+    if (tlo > 0 && tlo < thi && thi == nt) {
+      d0 = make_int4(share_of(T, q.t0, p.lg_nwg), nbeg, q.g, q.rb * kRowsPB);
+      d1 = make_int4(min(kRowsPB, R - q.rb * kRowsPB), q.t0, q.c, nt);
+    }
+  }
+  p.merge_desc[3 * lw] = d0;
+  p.merge_desc[3 * lw + 1] = d1;
+  p.merge_desc[3 * lw + 2] = make_int4(T, 0, 0, 0);
+}
+
+// Merge kernel: workgroup (w, rt) merges rows 16rt .. 16rt+15 of the cut
+// pair whose last tile lies in share w (its merge descriptor), combining the
+// (offset, l, acc) partials of every share holding part of the pair in share
+// order (deterministic), with a running offset so all loads of a group of
+// shares are in flight together. 16 threads per row, D/16 floats each.
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
-  constexpr int D4 = D / 4;
-  constexpr int IPT = kRowsPB * D4 / 256;  // float4 items per thread
-  __shared__ float s_M[kRowsPB];
-  __shared__ float s_invL[kRowsPB];
-  __shared__ int s_scan[4];
-  extern __shared__ int off[];  // [B + 1]
-  const int w = blockIdx.x;
-  if (w == 0) return;
-  const int T = scan_units(p, off, s_scan, false);
-  const int aw = share_begin(T, w, p.lg_nwg);
-  if (aw >= T) return;
-  const int r = request_of(off, p.B, aw);
-  const int nbeg = p.node_indptr[r];
-  const int N = p.node_indptr[r + 1] - nbeg;
-  const int L = p.prefix_len[r] + N;
-  const int R = N * p.G;
-  const int nt = ceil_div(L, kStage);
-  const PairAt q = pair_at(off[r], aw, R, nt);
-  const int t_last = q.t0 + (nt - 1) * q.c;  // first unit of the pair's last tile
-  if (!(share_begin(T, w - 1, p.lg_nwg) <= q.t0 && q.t0 < aw && aw <= t_last)) return;
-  const int g = q.g;
-  const int row0 = q.rb * kRowsPB;
-  const int rows_here = min(kRowsPB, R - row0);
-  const int w0 = w - 1, w1 = share_of(T, t_last, p.lg_nwg);
-  // Share v holds tiles [lo_v, hi_v) of the pair; shares without any are skipped.
-  auto part = [&](int v, int& lo) {
-    lo = tiles_before(share_begin(T, v, p.lg_nwg), q.t0, q.c, nt);
-    return tiles_before(share_begin(T, v + 1, p.lg_nwg), q.t0, q.c, nt) > lo;
-  };
+  constexpr int F = D / 64;  // float4 per thread
+  constexpr int U = 4;       // shares loaded together
+  const int w = blockIdx.x >> 3;
+  const int rt = blockIdx.x & 7;
+  const int4 d0 = p.merge_desc[3 * w];
+  if (d0.x < 0) return;
+  const int4 d1 = p.merge_desc[3 * w + 1];
+  const int T = p.merge_desc[3 * w + 2].x;
+  const int rows_here = d1.x;
+  if (rt * 16 >= rows_here) return;
+  const int row = rt * 16 + (threadIdx.x >> 4);
+  const int seg = threadIdx.x & 15;
+  const bool live = row < rows_here;
+  const int w0 = d0.x, t0 = d1.y, c = d1.z, nt = d1.w;
 
-  for (int row = threadIdx.x; row < rows_here; row += blockDim.x) {
-    float M = -INFINITY;
-    for (int v = w0; v <= w1; ++v) {
-      int lo;
-      if (!part(v, lo)) continue;
-      M = fmaxf(M, p.part_ml[(cut_slot(v, lo) * kRowsPB + row) * 2]);
+  float M = -INFINITY, Ls = 0.f;
+  float4 acc[F];
+#pragma unroll
+  for (int f = 0; f < F; ++f) acc[f] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int v0 = w0; v0 <= w; v0 += U) {
+    float m[U], l[U];
+    float4 o[U][F];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int v = v0 + u;
+      bool has = false;
+      size_t slot = 0;
+      if (v <= w) {
+        const int lo = tiles_before(share_begin(T, v, p.lg_nwg), t0, c, nt);
+        const int hi = tiles_before(share_begin(T, v + 1, p.lg_nwg), t0, c, nt);
+        has = hi > lo;
+        slot = cut_slot(v, lo);
+      }
+      has = has && live;
+      const size_t base = slot * kRowsPB + row;
+      m[u] = has ? p.part_ml[base * 2] : -INFINITY;
+      l[u] = has ? p.part_ml[base * 2 + 1] : 0.f;
+#pragma unroll
+      for (int f = 0; f < F; ++f)
+        o[u][f] = has ? *reinterpret_cast<const float4*>(p.part_o + base * D + (seg * F + f) * 4)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    float Ls = 0.f;
-    if (M != -INFINITY) {
-      for (int v = w0; v <= w1; ++v) {
-        int lo;
-        if (!part(v, lo)) continue;
-        const float* ml = p.part_ml + (cut_slot(v, lo) * kRowsPB + row) * 2;
-        Ls += ml[1] * exp2f(ml[0] - M);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (m[u] > M) {
+        const float sc = M == -INFINITY ? 0.f : exp2f(M - m[u]);
+        Ls *= sc;
+#pragma unroll
+        for (int f = 0; f < F; ++f) {
+          acc[f].x *= sc;
+          acc[f].y *= sc;
+          acc[f].z *= sc;
+          acc[f].w *= sc;
+        }
+        M = m[u];
+      }
+      const float wt = m[u] == -INFINITY ? 0.f : exp2f(m[u] - M);
+      Ls += wt * l[u];
+#pragma unroll
+      for (int f = 0; f < F; ++f) {
+        acc[f].x += wt * o[u][f].x;
+        acc[f].y += wt * o[u][f].y;
+        acc[f].z += wt * o[u][f].z;
+        acc[f].w += wt * o[u][f].w;
       }
     }
-    s_M[row] = M;
-    s_invL[row] = Ls > 0.f ? 1.f / Ls : 0.f;
   }
-  __syncthreads();
-  float4 acc[IPT];
+  if (!live) return;
+  const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+  uint16_t* dst = static_cast<uint16_t*>(p.out) + qo_offset(p, d0.y, d0.z, d0.w + row, D) + seg * F * 4;
 #pragma unroll
-  for (int k = 0; k < IPT; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int v = w0; v <= w1; ++v) {
-    int lo;
-    if (!part(v, lo)) continue;
-    const size_t slot = cut_slot(v, lo);
-    float4 o[IPT];
-    float m[IPT];
-#pragma unroll
-    for (int k = 0; k < IPT; ++k) {  // all loads of this share first
-      const int idx = threadIdx.x + 256 * k;
-      const int row = idx / D4;
-      const size_t base = slot * kRowsPB + row;
-      o[k] = row < rows_here ? *reinterpret_cast<const float4*>(p.part_o + base * D + (idx - row * D4) * 4)
-                             : make_float4(0.f, 0.f, 0.f, 0.f);
-      m[k] = row < rows_here ? p.part_ml[base * 2] : -INFINITY;
-    }
-#pragma unroll
-    for (int k = 0; k < IPT; ++k) {
-      const int row = (threadIdx.x + 256 * k) / D4;
-      const float Mr = row < rows_here ? s_M[row] : -INFINITY;
-      const float sc = (m[k] == -INFINITY) ? 0.f : exp2f(m[k] - Mr);
-      acc[k].x += sc * o[k].x;
-      acc[k].y += sc * o[k].y;
-      acc[k].z += sc * o[k].z;
-      acc[k].w += sc * o[k].w;
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < IPT; ++k) {
-    const int idx = threadIdx.x + 256 * k;
-    const int row = idx / D4;
-    if (row >= rows_here) continue;
-    const float inv = s_invL[row];
+  for (int f = 0; f < F; ++f) {
     uint2 pk;
-    pk.x = pack_bf16x2(acc[k].x * inv, acc[k].y * inv);
-    pk.y = pack_bf16x2(acc[k].z * inv, acc[k].w * inv);
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + qo_offset(p, nbeg, g, row0 + row, D) +
-                              (idx - row * D4) * 4) = pk;
+    pk.x = pack_bf16x2(acc[f].x * inv, acc[f].y * inv);
+    pk.y = pack_bf16x2(acc[f].z * inv, acc[f].w * inv);
+    *reinterpret_cast<uint2*>(dst + f * 4) = pk;
   }
 }
 
@@ -466,6 +483,7 @@ __global__ __launch_bounds__(kThreadsS, 1) void attn_stream_kernel(AttnParams p,
   const int T = scan_units(p, off, s_scan, lw == 0);
   const int a = share_begin(T, lw, p.lg_nwg);
   const int b = share_begin(T, lw + 1, p.lg_nwg);
+  if (tid == 0) write_merge_desc(p, off, T, a, b, lw);
   if (a >= b) return;
 
   int r = request_of(off, p.B, a);  // request holding unit a
@@ -1161,6 +1179,8 @@ bool plan_attn(const tv_attn_desc& d, AttnPlan* out) {
     const int nn_max = pl.rows_pb / pl.group + 2;
     pl.dyn_lds = size_t(nn_max) * pl.words * sizeof(uint32_t) + size_t(d.max_nodes) * sizeof(int);
   }
+  pl.off_desc = off;
+  off = align256(off + (pl.mfma ? size_t(pl.nwg) * 3 * sizeof(int4) : 0));
   pl.off_ml = off;
   off = align256(off + pl.slots * pl.rows_pb * 2 * sizeof(float));
   pl.off_o = off;
@@ -1185,6 +1205,7 @@ hipError_t launch_attn(const tv_attn_desc& d, const AttnPlan& pl, const AttnArgs
   char* ws = static_cast<char*>(a.workspace);
   p.status = reinterpret_cast<uint32_t*>(ws);
   p.counters = reinterpret_cast<uint32_t*>(ws + pl.off_counters);
+  p.merge_desc = reinterpret_cast<int4*>(ws + pl.off_desc);
   p.part_ml = reinterpret_cast<float*>(ws + pl.off_ml);
   p.part_o = reinterpret_cast<float*>(ws + pl.off_o);
   p.B = d.batch;
@@ -1208,20 +1229,20 @@ hipError_t launch_attn(const tv_attn_desc& d, const AttnPlan& pl, const AttnArgs
   if (pl.mfma) {
     // Streaming pass (whole pairs written, cut pairs left as partials), then
     // the merge of the cut pairs; the kernel boundary orders the two.
-    const size_t merge_lds = size_t(d.batch + 1) * sizeof(int);
+    const dim3 mgrid(unsigned(pl.nwg) * (kRowsPB / 16));
     const dim3 sblock(kThreadsS);
     if (d.head_dim == 128) {
       if (pl.ns == 4)
         attn_stream_kernel<128, 4><<<grid, sblock, lds, stream>>>(p, a.page_indices, a.node_indptr, a.prefix_len, a.page_indptr);
       else
         attn_stream_kernel<128, 2><<<grid, sblock, lds, stream>>>(p, a.page_indices, a.node_indptr, a.prefix_len, a.page_indptr);
-      hipLaunchKernelGGL(attn_merge_kernel<128>, grid, block, merge_lds, stream, p);
+      hipLaunchKernelGGL(attn_merge_kernel<128>, mgrid, block, 0, stream, p);
     } else {
       if (pl.ns == 4)
         attn_stream_kernel<64, 4><<<grid, sblock, lds, stream>>>(p, a.page_indices, a.node_indptr, a.prefix_len, a.page_indptr);
       else
         attn_stream_kernel<64, 2><<<grid, sblock, lds, stream>>>(p, a.page_indices, a.node_indptr, a.prefix_len, a.page_indptr);
-      hipLaunchKernelGGL(attn_merge_kernel<64>, grid, block, merge_lds, stream, p);
+      hipLaunchKernelGGL(attn_merge_kernel<64>, mgrid, block, 0, stream, p);
     }
   } else {
     if (d.head_dim == 128)

@@ -28,7 +28,7 @@ struct AttnPlan {
   size_t slots;       // partial-result slots
   size_t grid;        // launch size (multiple of 8: XCD-aware remap)
   size_t dyn_lds;     // dynamic LDS bytes per workgroup
-  size_t off_counters, off_ml, off_o, total_bytes;
+  size_t off_counters, off_desc, off_ml, off_o, total_bytes;
 };
 
 struct SamplePlan {
