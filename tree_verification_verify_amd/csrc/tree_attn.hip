@@ -289,7 +289,8 @@ __device__ inline void write_merge_desc(const AttnParams& p, const int* off, int
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   constexpr int F = D / 64;  // float4 per thread
-  constexpr int U = 4;       // shares loaded together
+  constexpr int U = 8;       // shares loaded together
+  __shared__ int s_slot[kMaxWG];  // partial slot of share w0 + i, -1 when it holds no tile
   const int w = blockIdx.x >> 3;
   const int rt = blockIdx.x & 7;
   const int4 d0 = p.merge_desc[3 * w];
@@ -302,36 +303,50 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   const int seg = threadIdx.x & 15;
   const bool live = row < rows_here;
   const int w0 = d0.x, t0 = d1.y, c = d1.z, nt = d1.w;
+  const int nsh = w - w0 + 1;  // shares w0 .. w
+  // Partial slot of share w0 + i, or -1 when that share holds no tile of
+  // the pair. Up to four shares (the common case) take one round with the
+  // slots formed in registers; more take rounds of U with the slots formed
+  // once in LDS.
+  auto slot_of = [&](int i) {
+    const int v = w0 + i;
+    const int lo = tiles_before(share_begin(T, v, p.lg_nwg), t0, c, nt);
+    const int hi = tiles_before(share_begin(T, v + 1, p.lg_nwg), t0, c, nt);
+    return hi > lo ? int(cut_slot(v, lo)) : -1;
+  };
+  const bool table = nsh > 4;
+  if (table) {
+    for (int i = threadIdx.x; i < nsh; i += blockDim.x) s_slot[i] = slot_of(i);
+    __syncthreads();
+  }
 
   float M = -INFINITY, Ls = 0.f;
   float4 acc[F];
 #pragma unroll
   for (int f = 0; f < F; ++f) acc[f] = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int v0 = w0; v0 <= w; v0 += U) {
-    float m[U], l[U];
-    float4 o[U][F];
+  auto round = [&](int i0, auto u_c) __attribute__((always_inline)) {
+    constexpr int NU = decltype(u_c)::value;
+    float m[NU], l[NU];
+    float4 o[NU][F];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int v = v0 + u;
-      bool has = false;
-      size_t slot = 0;
-      if (v <= w) {
-        const int lo = tiles_before(share_begin(T, v, p.lg_nwg), t0, c, nt);
-        const int hi = tiles_before(share_begin(T, v + 1, p.lg_nwg), t0, c, nt);
-        has = hi > lo;
-        slot = cut_slot(v, lo);
+    for (int u = 0; u < NU; ++u) {
+      const int i = i0 + u;
+      const int slot = i < nsh ? (table ? s_slot[i] : slot_of(i)) : -1;
+      m[u] = -INFINITY;
+      l[u] = 0.f;
+#pragma unroll
+      for (int f = 0; f < F; ++f) o[u][f] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (slot >= 0 && live) {
+        const size_t base = size_t(slot) * kRowsPB + row;
+        m[u] = p.part_ml[base * 2];
+        l[u] = p.part_ml[base * 2 + 1];
+#pragma unroll
+        for (int f = 0; f < F; ++f)
+          o[u][f] = *reinterpret_cast<const float4*>(p.part_o + base * D + (seg * F + f) * 4);
       }
-      has = has && live;
-      const size_t base = slot * kRowsPB + row;
-      m[u] = has ? p.part_ml[base * 2] : -INFINITY;
-      l[u] = has ? p.part_ml[base * 2 + 1] : 0.f;
-#pragma unroll
-      for (int f = 0; f < F; ++f)
-        o[u][f] = has ? *reinterpret_cast<const float4*>(p.part_o + base * D + (seg * F + f) * 4)
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < NU; ++u) {
       if (m[u] > M) {
         const float sc = M == -INFINITY ? 0.f : exp2f(M - m[u]);
         Ls *= sc;
@@ -354,7 +369,11 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
         acc[f].w += wt * o[u][f].w;
       }
     }
-  }
+  };
+  if (!table)
+    round(0, std::integral_constant<int, 4>{});
+  else
+    for (int i0 = 0; i0 < nsh; i0 += U) round(i0, std::integral_constant<int, U>{});
   if (!live) return;
   const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
   uint16_t* dst = static_cast<uint16_t*>(p.out) + qo_offset(p, d0.y, d0.z, d0.w + row, D) + seg * F * 4;
