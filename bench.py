@@ -204,6 +204,100 @@ def attn_sweep(names, rotate_bytes, reps):
         torch.cuda.empty_cache()
 
 
+def commit_bench(layers, reps):
+    """tree_kv_commit alone on the highload batch: keep-lists from the real
+    sampling walk and path kernels over the same inputs, `layers` distinct
+    K/V layer pools, a 1 GiB write before every timed call so the Infinity
+    Cache holds none of the pages it touches. Algorithmic bytes: K and V of
+    every entry that moves (kv_keep[j] != P + j), read once and written once,
+    in every layer and kv head."""
+    import torch
+    import tree_verification_verify_amd as tv
+    from workloads import make_config
+    from workloads.device import attention_tensors, sampler_tensors
+    cfg = make_config("highload")
+    inp, s = cfg.attn, cfg.sampler
+    a = attention_tensors(inp, "cuda")
+    st = sampler_tensors(s, "cuda")
+    md = max(8, inp.max_depth)
+    sdesc = tv.sample_desc(s.batch, s.vocab, s.max_nodes, md)
+    sws = tv.alloc_workspace(tv.sample_workspace_size(sdesc))
+    T = int(s.node_indptr[-1])
+    flag = torch.empty(T, dtype=torch.int8, device="cuda")
+    nt = torch.empty(T, dtype=torch.int32, device="cuda")
+    tv.tree_spec_sample(sdesc, st["target_logits"], st["draft_logits"], st["tokens"],
+                        st["node_indptr"], st["parent"], st["temperature"], st["uniforms"],
+                        flag, nt, sws)
+    B = s.batch
+    pn = torch.empty(B * (md + 1), dtype=torch.int32, device="cuda")
+    ot, kk = torch.empty_like(pn), torch.empty_like(pn)
+    ol = torch.empty(B, dtype=torch.int32, device="cuda")
+    tv.tree_accept_path(B, md, st["node_indptr"], st["parent"], st["tokens"], flag, nt,
+                        a["prefix_len"], pn, ot, ol, kk, sws)
+    del st
+    torch.cuda.synchronize()
+    keep = kk.cpu().numpy().reshape(B, md + 1)
+    olen = ol.cpu().numpy()
+    moved = sum(int((keep[r, :olen[r]] != inp.prefix_len[r] + np.arange(olen[r])).sum())
+                for r in range(B) if olen[r] > 0)
+    D, Hkv = inp.head_dim, inp.num_kv_heads
+    abytes = moved * layers * Hkv * D * 2 * 2 * 2
+    desc = tv.attn_desc(inp.batch, inp.num_q_heads, Hkv, D, inp.max_nodes, inp.max_depth,
+                        inp.max_kv_len, inp.num_pages, inp.dtype)
+    shape = (layers,) + tuple(a["k_pages"].shape)
+    kp = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    vp = torch.empty((layers,) + tuple(a["v_pages"].shape), dtype=torch.bfloat16, device="cuda")
+    ws = tv.alloc_workspace(4096)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    tv.tree_kv_commit(desc, kp, vp, a["page_indptr"], a["page_indices"], a["prefix_len"], kk,
+                      ol, md, num_layers=layers, status_workspace=ws)  # checked call
+    import ctypes
+    from tree_verification_verify_amd import _lib
+    lib = _lib.load()
+    P_ = ctypes.c_void_p
+    args = (ctypes.byref(desc), layers, kp[0].numel(), P_(kp.data_ptr()), P_(vp.data_ptr()),
+            P_(a["page_indptr"].data_ptr()), P_(a["page_indices"].data_ptr()),
+            P_(a["prefix_len"].data_ptr()), P_(kk.data_ptr()), P_(ol.data_ptr()), md,
+            P_(ws.data_ptr()), P_(stream.cuda_stream))
+
+    def call():  # the same call without the binding's Python-side checks
+        lib.tree_kv_commit(*args)
+    torch.cuda.synchronize()
+    status, bits = tv.device_status(ws)
+    if status != 0:
+        raise SystemExit(f"device status {status} bits {bits}")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for e0, e1 in ev:
+        flush.fill_(1)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e3
+    # the same calls back to back (keep-lists, page tables and the touched
+    # pages warm in the caches and translation buffers): context only
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0.record(stream)
+    for _ in range(reps):
+        call()
+    w1.record(stream)
+    torch.cuda.synchronize()
+    warm_us = w0.elapsed_time(w1) * 1e3 / reps
+    gbs = abytes / (us * 1e-6) / 1e9
+    print(json.dumps({
+        "kernel": "tree_kv_commit (kv_commit_kernel<128, bf16>)",
+        "workload": f"highload: {B} requests, keep-lists of the sampled paths "
+                    f"(mean out_len {float(olen.mean()):.2f}, {moved} entries move), "
+                    f"{layers} layers x {Hkv} kv heads x D {D} bf16",
+        "us_per_call_median": us, "reps": reps, "algorithmic_bytes": abytes,
+        "us_per_call_back_to_back": warm_us,
+        "hbm_GBs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+        "bytes_per_moved_entry_per_layer": Hkv * D * 2 * 2 * 2}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -220,6 +314,9 @@ def main():
                     help="comma-separated workloads: time tree_verify_attn alone on each, "
                          "rotating >= --rotate-bytes of distinct copies (one JSON line each)")
     ap.add_argument("--rotate-bytes", type=int, default=1 << 30)
+    ap.add_argument("--commit-bench", type=int, default=0, metavar="LAYERS",
+                    help="time tree_kv_commit alone on the highload batch over this many "
+                         "layers (one JSON line)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU; --gpus must be 1 "
@@ -228,6 +325,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.commit_bench:
+        commit_bench(args.commit_bench, max(1, args.steps))
+        return
     if args.attn_sweep:
         attn_sweep(args.attn_sweep.split(","), args.rotate_bytes, max(1, args.steps // 10))
         return

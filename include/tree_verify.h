@@ -213,6 +213,37 @@ tv_status tree_accept_path(int32_t batch, int32_t max_depth,
                            int32_t* out_len, int32_t* kv_keep,
                            void* status_workspace, hipStream_t stream);
 
+/* Commit of the accepted path's K/V ([survey] Systems, KV handling: the
+ * reference EAGLE implementation compacts the accepted slots in place with
+ * gathers over the accepted positions; [survey] Timeline: tree tokens sit in
+ * the KV cache in topological order). For every request r with
+ * n = out_len[r] >= 1, in every layer and kv head, logical position
+ * prefix_len[r] + j takes the K and V of logical position kv_keep[r][j],
+ * j = 0 .. n-1 (the layouts tree_accept_path writes; within a request every
+ * source is read before its destination is written). Logical positions map
+ * to pages as for tree_verify_attn; positions from prefix_len[r] + n on keep
+ * whatever they held.
+ *   desc: batch, num_kv_heads, head_dim (64|128), num_pages, max_nodes and
+ *     dtype as for tree_verify_attn (other fields unused).
+ *   k_pages, v_pages: num_layers page pools, layer l at element offset
+ *     l * layer_stride (>= num_pages*Hkv*16*D; pools and layer starts 16-byte
+ *     aligned); K pages [num_pages][Hkv][16][D], V pages [num_pages][Hkv][D][16].
+ *     Modified in place.
+ *   kv_keep [B][max_depth+1], out_len [B]: as written by tree_accept_path.
+ *     Requests with out_len < 1 are left untouched.
+ * The pages holding positions prefix_len[r] .. prefix_len[r]+n-1 must belong
+ * to request r alone. A keep-list that does not start at prefix_len[r], is
+ * not strictly increasing, has an entry below prefix_len[r] + j or at or past
+ * prefix_len[r] + max_nodes, or reaches past the listed pages sets
+ * TV_DEV_PATH (a page id outside the pool: TV_DEV_PAGES; out_len[r] >
+ * max_depth + 1: TV_DEV_SHAPE) in status_workspace (if not NULL), and the
+ * request is left untouched. */
+tv_status tree_kv_commit(const tv_attn_desc* desc, int32_t num_layers, int64_t layer_stride,
+                         void* k_pages, void* v_pages, const int32_t* page_indptr,
+                         const int32_t* page_indices, const int32_t* prefix_len,
+                         const int32_t* kv_keep, const int32_t* out_len, int32_t max_depth,
+                         void* status_workspace, hipStream_t stream);
+
 /* Tree metadata ([TreeSpark] §3.2 step 3 and §4: per-depth position ids and
  * ancestor bitmasks). For every row: depth (edges from the root),
  * anc_bits [T][ceil(max_nodes/32)] (bit j of word j/32 set iff j is an

@@ -138,3 +138,28 @@ def test_validate_pages():
     assert tv.validate_pages(pi, np.array([5, -1, 0]), prefix, ni, 6) == PAGES
     assert tv.validate_pages(np.array([0, 1, 3]), idx, prefix, ni, 6) == PAGES  # too few pages
     assert tv.validate_pages(pi, idx, np.array([29, 9]), ni, 6) == PAGES        # 33 tokens > 32
+
+
+def test_kv_commit_host_errors():
+    lib = tv.library()
+    d = _desc()
+    per_layer = 100 * 2 * 16 * 128
+
+    def call(desc=d, layers=2, stride=per_layer, max_depth=8, null=None, k=FAKE):
+        ptrs = [k, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE]
+        if null is not None:
+            ptrs[null] = None
+        return lib.tree_kv_commit(ctypes.byref(desc), layers, stride, *ptrs, max_depth, None, None)
+
+    assert call(layers=0) == SHAPE
+    assert call(stride=per_layer - 8) == SHAPE           # layers would overlap
+    assert call(stride=per_layer + 3) == SHAPE           # layer starts not 16-byte aligned
+    assert call(max_depth=-1) == SHAPE
+    assert call(desc=_desc(head_dim=96)) == SHAPE
+    assert call(desc=_desc(dtype="fp32"), stride=per_layer + 2) == SHAPE
+    assert call(k=ctypes.c_void_p(0x100008)) == SHAPE    # misaligned pool
+    for i in range(7):
+        assert call(null=i) == NULL
+    bad = _desc()
+    bad.dtype = 7
+    assert call(desc=bad) == DTYPE

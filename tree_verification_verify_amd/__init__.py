@@ -23,7 +23,8 @@ __all__ = [
     "TVError", "AttnDesc", "SampleDesc", "TV_BF16", "TV_FP32", "attn_desc",
     "sample_desc", "attn_workspace_size", "sample_workspace_size", "alloc_workspace",
     "workspace_init", "device_status", "tree_verify_attn", "tree_spec_sample",
-    "tree_accept_path", "tv_tree_meta", "validate_tree", "validate_pages", "library",
+    "tree_accept_path", "tree_kv_commit", "tv_tree_meta", "validate_tree", "validate_pages",
+    "library",
 ]
 
 
@@ -183,6 +184,36 @@ def tree_accept_path(batch, max_depth, node_indptr, parent, tokens, accept_flag,
         batch, max_depth, _ptr(node_indptr), _ptr(parent), _ptr(tokens), _ptr(accept_flag),
         _ptr(next_token), _ptr(prefix_len), _ptr(path_nodes), _ptr(out_tokens), _ptr(out_len),
         _ptr(kv_keep), _ptr(status_workspace), _stream(stream)), "tree_accept_path")
+
+
+def tree_kv_commit(desc, k_pages, v_pages, page_indptr, page_indices, prefix_len, kv_keep,
+                   out_len, max_depth, num_layers=None, layer_stride=None,
+                   status_workspace=None, stream=None):
+    """k_pages / v_pages: [L][num_pages][Hkv][16][D] and [L][num_pages][Hkv][D][16]
+    (or one layer without the leading L), modified in place."""
+    import torch
+    dt = torch.bfloat16 if desc.dtype == TV_BF16 else torch.float32
+    for t, n in ((k_pages, "k_pages"), (v_pages, "v_pages")):
+        _need(t, n, dt)
+    for t, n in ((page_indptr, "page_indptr"), (page_indices, "page_indices"),
+                 (prefix_len, "prefix_len"), (kv_keep, "kv_keep"), (out_len, "out_len")):
+        _need(t, n, torch.int32)
+    per_layer = desc.num_pages * desc.num_kv_heads * 16 * desc.head_dim
+    if num_layers is None:
+        num_layers = k_pages.numel() // per_layer
+    if layer_stride is None:
+        layer_stride = per_layer
+    if k_pages.shape != v_pages.shape[:-2] + (16, desc.head_dim) and \
+            k_pages.numel() != v_pages.numel():
+        raise ValueError("k_pages and v_pages disagree")
+    if k_pages.numel() < (num_layers - 1) * layer_stride + per_layer:
+        raise ValueError("k_pages holds fewer layers than num_layers")
+    if kv_keep.numel() < desc.batch * (max_depth + 1):
+        raise ValueError("kv_keep must hold [B][max_depth+1]")
+    _check(_lib.load().tree_kv_commit(
+        ctypes.byref(desc), int(num_layers), int(layer_stride), _ptr(k_pages), _ptr(v_pages),
+        _ptr(page_indptr), _ptr(page_indices), _ptr(prefix_len), _ptr(kv_keep), _ptr(out_len),
+        int(max_depth), _ptr(status_workspace), _stream(stream)), "tree_kv_commit")
 
 
 def tv_tree_meta(batch, max_nodes, node_indptr, parent, depth=None, anc_bits=None,

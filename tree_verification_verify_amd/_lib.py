@@ -32,6 +32,7 @@ class SampleDesc(ctypes.Structure):
 EXPORTS = [
     "tv_attn_workspace_size", "tv_sample_workspace_size", "tv_workspace_init",
     "tv_device_status", "tree_verify_attn", "tree_spec_sample", "tree_accept_path",
+    "tree_kv_commit",
     "tv_tree_meta", "tv_validate_tree", "tv_validate_pages", "tv_status_string",
     "tv_last_hip_error", "tv_version",
 ]
@@ -61,6 +62,8 @@ def load():
         "tree_verify_attn": (st, [ctypes.POINTER(AttnDesc)] + [P] * 9 + [P, S, P]),
         "tree_spec_sample": (st, [ctypes.POINTER(SampleDesc)] + [P] * 9 + [P, S, P]),
         "tree_accept_path": (st, [I32, I32] + [P] * 10 + [P, P]),
+        "tree_kv_commit": (st, [ctypes.POINTER(AttnDesc), I32, ctypes.c_int64] + [P] * 7
+                           + [I32, P, P]),
         "tv_tree_meta": (st, [I32, I32] + [P] * 6 + [P, P]),
         "tv_validate_tree": (st, [I32, P, P, I32, I32]),
         "tv_validate_pages": (st, [I32, P, P, P, P, I32, I32]),

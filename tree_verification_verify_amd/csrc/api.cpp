@@ -142,6 +142,32 @@ tv_status tree_accept_path(int32_t batch, int32_t max_depth, const int32_t* node
   return TV_OK;
 }
 
+tv_status tree_kv_commit(const tv_attn_desc* desc, int32_t num_layers, int64_t layer_stride,
+                         void* k_pages, void* v_pages, const int32_t* page_indptr,
+                         const int32_t* page_indices, const int32_t* prefix_len,
+                         const int32_t* kv_keep, const int32_t* out_len, int32_t max_depth,
+                         void* status_workspace, hipStream_t stream) {
+  if (!desc) return TV_ERR_NULL;
+  const tv_attn_desc& d = *desc;
+  if (d.dtype != TV_BF16 && d.dtype != TV_FP32) return TV_ERR_DTYPE;
+  if (d.batch < 1 || d.num_kv_heads < 1 || (d.head_dim != 64 && d.head_dim != 128) ||
+      d.num_pages < 1 || d.max_nodes < 1 || num_layers < 1 || max_depth < 0 || max_depth > 65535)
+    return TV_ERR_SHAPE;
+  const long long pool = (long long)d.num_pages * d.num_kv_heads * tv::kPage * d.head_dim;
+  const int elem = d.dtype == TV_BF16 ? 2 : 4;
+  if (layer_stride < pool || (layer_stride * elem) % 16 != 0) return TV_ERR_SHAPE;
+  if ((long long)d.batch * num_layers > 0x7fffffffLL) return TV_ERR_SHAPE;
+  if (!k_pages || !v_pages || !page_indptr || !page_indices || !prefix_len || !kv_keep || !out_len)
+    return TV_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(k_pages) | reinterpret_cast<uintptr_t>(v_pages)) & 15u)
+    return TV_ERR_SHAPE;
+  hipError_t e = tv::launch_kv_commit(d, num_layers, layer_stride, k_pages, v_pages, page_indptr,
+                                      page_indices, prefix_len, kv_keep, out_len, max_depth,
+                                      static_cast<uint32_t*>(status_workspace), stream);
+  if (e != hipSuccess) return hip_fail(e, "tree_kv_commit");
+  return TV_OK;
+}
+
 tv_status tv_tree_meta(int32_t batch, int32_t max_nodes, const int32_t* node_indptr,
                        const int32_t* parent, int32_t* depth, uint32_t* anc_bits,
                        int32_t* first_child, int32_t* next_sibling, void* status_workspace,

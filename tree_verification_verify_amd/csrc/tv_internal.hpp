@@ -84,6 +84,12 @@ hipError_t launch_tree_meta(int32_t batch, int32_t max_nodes, const int32_t* nod
                             int32_t* first_child, int32_t* next_sibling, uint32_t* status,
                             hipStream_t stream);
 
+hipError_t launch_kv_commit(const tv_attn_desc& d, int32_t num_layers, long long layer_stride,
+                            void* k_pages, void* v_pages, const int32_t* page_indptr,
+                            const int32_t* page_indices, const int32_t* prefix_len,
+                            const int32_t* kv_keep, const int32_t* out_len, int32_t max_depth,
+                            uint32_t* status, hipStream_t stream);
+
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream);
 
 }  // namespace tv
