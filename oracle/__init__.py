@@ -3,7 +3,8 @@
 Plain, slow, obviously-correct NumPy (fp64) definitions of what the hot path
 computes: tree metadata, tree-masked attention over a paged prefix, the
 multi-step speculative-sampling walk with siblings drawn without replacement,
-longest-accepted-path selection, and the commit of the accepted path's K/V. Each function cites the passage of the
+longest-accepted-path selection, the commit of the accepted path's K/V, and
+the draw of a node's children without replacement (Gumbel-top-k). Each function cites the passage of the
 source pages it follows:
 
   [survey]    "Tree-based speculative decoding: draft trees win latency, lose
@@ -23,6 +24,7 @@ from .sampler import (softmax_T, proposal_without, residual_update,
                       walk_request, tree_spec_sample)
 from .path import accept_path_request, tree_accept_path
 from .commit import BadKeepList, check_keep, kv_commit_layer, kv_commit
+from .siblings import philox4x32_10, draw_children, tree_draw_siblings
 from .enumerate import enumerate_node_laws
 
 __all__ = [
@@ -32,5 +34,6 @@ __all__ = [
     "acceptance_ratio", "inverse_cdf", "greedy_request", "walk_request",
     "tree_spec_sample", "accept_path_request", "tree_accept_path",
     "BadKeepList", "check_keep", "kv_commit_layer", "kv_commit",
+    "philox4x32_10", "draw_children", "tree_draw_siblings",
     "enumerate_node_laws",
 ]
