@@ -298,6 +298,64 @@ def commit_bench(layers, reps):
         "bytes_per_moved_entry_per_layer": Hkv * D * 2 * 2 * 2}), flush=True)
 
 
+def siblings_bench(reps):
+    """tree_draw_siblings alone: every expanded node of the highload trees
+    (k = its child count, its request's temperature), draft logits over
+    V = 151936 resident in HBM. Algorithmic bytes: each expanded row's draft
+    logits read once (the outputs are 64 bytes per row)."""
+    import ctypes
+    import torch
+    import tree_verification_verify_amd as tv
+    from tree_verification_verify_amd import _lib
+    from workloads import make_config
+    cfg = make_config("highload")
+    s = cfg.sampler
+    rows, counts, temps = [], [], []
+    for r in range(s.batch):
+        a, b = int(s.node_indptr[r]), int(s.node_indptr[r + 1])
+        ch = np.bincount(s.parent[a + 1:b], minlength=b - a)
+        for i in np.nonzero(ch)[0]:
+            rows.append(a + int(i))
+            counts.append(int(ch[i]))
+            temps.append(float(s.temperature[r]))
+    R, V = len(rows), s.vocab
+    logits = torch.from_numpy(np.ascontiguousarray(s.draft_logits[rows])).to("cuda")
+    c = torch.tensor(counts, dtype=torch.int32, device="cuda")
+    t = torch.tensor(temps, dtype=torch.float32, device="cuda")
+    out = torch.empty((R, _lib.MAX_CHILDREN), dtype=torch.int32, device="cuda")
+    ws = tv.alloc_workspace(4096)
+    tv.tree_draw_siblings(logits, c, t, out, stream_id=1, seed=42, status_workspace=ws)
+    torch.cuda.synchronize()
+    status, bits = tv.device_status(ws)
+    if status != 0:
+        raise SystemExit(f"device status {status} bits {bits}")
+    lib = _lib.load()
+    stream = torch.cuda.current_stream()
+    P_ = ctypes.c_void_p
+    args = (R, V, P_(logits.data_ptr()), P_(c.data_ptr()), P_(t.data_ptr()), 1, 42,
+            P_(out.data_ptr()), P_(ws.data_ptr()), P_(stream.cuda_stream))
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for e0, e1 in ev:
+        flush.fill_(1)  # the 256 MB Infinity Cache holds none of the rows
+        e0.record(stream)
+        lib.tree_draw_siblings(*args)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e3
+    abytes = R * V * 4
+    gbs = abytes / (us * 1e-6) / 1e9
+    nT = sum(1 for x in temps if x > 0)
+    print(json.dumps({
+        "kernel": "tree_draw_siblings (draw_siblings_kernel)",
+        "workload": f"highload: {R} expanded nodes ({sum(counts)} children, k <= {max(counts)}; "
+                    f"{nT} rows at T > 0), V {V} fp32 draft logits",
+        "us_per_call_median": us, "reps": reps, "algorithmic_bytes": abytes,
+        "hbm_GBs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+        "tokens_per_s": R * V / (us * 1e-6)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -314,6 +372,8 @@ def main():
                     help="comma-separated workloads: time tree_verify_attn alone on each, "
                          "rotating >= --rotate-bytes of distinct copies (one JSON line each)")
     ap.add_argument("--rotate-bytes", type=int, default=1 << 30)
+    ap.add_argument("--siblings-bench", action="store_true",
+                    help="time tree_draw_siblings alone on the highload trees' expansions")
     ap.add_argument("--commit-bench", type=int, default=0, metavar="LAYERS",
                     help="time tree_kv_commit alone on the highload batch over this many "
                          "layers (one JSON line)")
@@ -325,6 +385,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.siblings_bench:
+        siblings_bench(max(1, args.steps))
+        return
     if args.commit_bench:
         commit_bench(args.commit_bench, max(1, args.steps))
         return

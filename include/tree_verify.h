@@ -244,6 +244,31 @@ tv_status tree_kv_commit(const tv_attn_desc* desc, int32_t num_layers, int64_t l
                          const int32_t* kv_keep, const int32_t* out_len, int32_t max_depth,
                          void* status_workspace, hipStream_t stream);
 
+/* Children of each expanded node, drawn without replacement ([survey]
+ * Timeline: Recursive Speculative Decoding draws tree siblings without
+ * replacement via Gumbel-Top-k; [TreeSpark] §1, §3.3: siblings are drawn
+ * without replacement from q_T, in a draw order the verifier replays).
+ * For row r with k = counts[r] children (0..TV_MAX_CHILDREN) and temperature
+ * T = temperature[r] >= 0: tokens[r][0..k-1] = the k tokens of largest
+ * score, in descending score, lower token id first on ties, where
+ * score(y) = d[y]/T - ln(-ln u(y)) at T > 0 and d[y] at T = 0; the rest of
+ * tokens[r] is -1. u(y) = ((w >> 8) + 1/2) / 2^24 with w the (y % 4)-th word
+ * of Philox4x32-10 (Salmon et al., SC 2011) at counter (y/4, r, stream_id, 0)
+ * and key (seed mod 2^32, seed >> 32).
+ *   draft_logits [rows][vocab] fp32 (rows 16-byte aligned when vocab % 4 == 0
+ *     for the vector path); counts [rows] int32; temperature [rows] fp32;
+ *   tokens [rows][TV_MAX_CHILDREN] int32 output.
+ * The noise is computed in fp32 (the exact -ln u via log1p near u = 1), so
+ * draws match an fp64 evaluation except where two scores lie within ~1e-5.
+ * counts outside [0, TV_MAX_CHILDREN] set TV_DEV_SHAPE, a negative or
+ * non-finite temperature or non-finite logits TV_DEV_LOGITS in
+ * status_workspace (if not NULL); such a row's tokens are all -1. */
+#define TV_MAX_CHILDREN 16
+tv_status tree_draw_siblings(int32_t rows, int32_t vocab, const float* draft_logits,
+                             const int32_t* counts, const float* temperature, uint32_t stream_id,
+                             uint64_t seed, int32_t* tokens, void* status_workspace,
+                             hipStream_t stream);
+
 /* Tree metadata ([TreeSpark] §3.2 step 3 and §4: per-depth position ids and
  * ancestor bitmasks). For every row: depth (edges from the root),
  * anc_bits [T][ceil(max_nodes/32)] (bit j of word j/32 set iff j is an

@@ -88,7 +88,7 @@ def tree_draw_siblings(draft_logits, counts, temperature, stream, seed, kmax):
             continue
         s = scores(draft_logits[r], float(temperature[r]), r, stream, seed)
         order = np.lexsort((np.arange(s.shape[0]), -s))[:k + 1]
-        tokens[r, :k] = order[:k]
+        tokens[r, :min(k, len(order))] = order[:k]  # fewer tokens than k: the rest stay -1
         top = s[order]
         if len(top) > 1:
             min_gap[r] = float(np.min(top[:-1] - top[1:]))

@@ -163,3 +163,16 @@ def test_kv_commit_host_errors():
     bad = _desc()
     bad.dtype = 7
     assert call(desc=bad) == DTYPE
+
+
+def test_draw_siblings_host_errors():
+    lib = tv.library()
+    args = [4, 100, FAKE, FAKE, FAKE, 0, 0, FAKE, None, None]
+    for i, bad in ((0, 0), (1, 0)):
+        a = list(args)
+        a[i] = bad
+        assert lib.tree_draw_siblings(*a) == SHAPE
+    for i in (2, 3, 4, 7):
+        a = list(args)
+        a[i] = None
+        assert lib.tree_draw_siblings(*a) == NULL

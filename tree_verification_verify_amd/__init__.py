@@ -23,7 +23,7 @@ __all__ = [
     "TVError", "AttnDesc", "SampleDesc", "TV_BF16", "TV_FP32", "attn_desc",
     "sample_desc", "attn_workspace_size", "sample_workspace_size", "alloc_workspace",
     "workspace_init", "device_status", "tree_verify_attn", "tree_spec_sample",
-    "tree_accept_path", "tree_kv_commit", "tv_tree_meta", "validate_tree", "validate_pages",
+    "tree_accept_path", "tree_kv_commit", "tree_draw_siblings", "tv_tree_meta", "validate_tree", "validate_pages",
     "library",
 ]
 
@@ -214,6 +214,27 @@ def tree_kv_commit(desc, k_pages, v_pages, page_indptr, page_indices, prefix_len
         ctypes.byref(desc), int(num_layers), int(layer_stride), _ptr(k_pages), _ptr(v_pages),
         _ptr(page_indptr), _ptr(page_indices), _ptr(prefix_len), _ptr(kv_keep), _ptr(out_len),
         int(max_depth), _ptr(status_workspace), _stream(stream)), "tree_kv_commit")
+
+
+def tree_draw_siblings(draft_logits, counts, temperature, tokens, stream_id=0, seed=0,
+                       status_workspace=None, stream=None):
+    """draft_logits [rows][V] fp32, counts [rows] int32, temperature [rows] fp32;
+    tokens [rows][MAX_CHILDREN] int32 (output)."""
+    import torch
+    _need(draft_logits, "draft_logits", torch.float32)
+    _need(temperature, "temperature", torch.float32)
+    _need(counts, "counts", torch.int32)
+    _need(tokens, "tokens", torch.int32)
+    if draft_logits.dim() != 2:
+        raise ValueError("draft_logits must be [rows][V]")
+    rows, V = draft_logits.shape
+    if tokens.numel() < rows * _lib.MAX_CHILDREN or counts.numel() < rows or \
+            temperature.numel() < rows:
+        raise ValueError("counts / temperature must hold [rows], tokens [rows][16]")
+    _check(_lib.load().tree_draw_siblings(
+        rows, V, _ptr(draft_logits), _ptr(counts), _ptr(temperature), int(stream_id) & 0xFFFFFFFF,
+        int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(tokens), _ptr(status_workspace), _stream(stream)),
+        "tree_draw_siblings")
 
 
 def tv_tree_meta(batch, max_nodes, node_indptr, parent, depth=None, anc_bits=None,

@@ -6,6 +6,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libtreeverify.so")
 
 TV_FP32, TV_BF16 = 0, 1
+MAX_CHILDREN = 16
 
 STATUS_NAMES = {
     0: "TV_OK", 1: "TV_ERR_NULL", 2: "TV_ERR_SHAPE", 3: "TV_ERR_DTYPE",
@@ -32,7 +33,7 @@ class SampleDesc(ctypes.Structure):
 EXPORTS = [
     "tv_attn_workspace_size", "tv_sample_workspace_size", "tv_workspace_init",
     "tv_device_status", "tree_verify_attn", "tree_spec_sample", "tree_accept_path",
-    "tree_kv_commit",
+    "tree_kv_commit", "tree_draw_siblings",
     "tv_tree_meta", "tv_validate_tree", "tv_validate_pages", "tv_status_string",
     "tv_last_hip_error", "tv_version",
 ]
@@ -64,6 +65,7 @@ def load():
         "tree_accept_path": (st, [I32, I32] + [P] * 10 + [P, P]),
         "tree_kv_commit": (st, [ctypes.POINTER(AttnDesc), I32, ctypes.c_int64] + [P] * 7
                            + [I32, P, P]),
+        "tree_draw_siblings": (st, [I32, I32, P, P, P, ctypes.c_uint32, ctypes.c_uint64, P, P, P]),
         "tv_tree_meta": (st, [I32, I32] + [P] * 6 + [P, P]),
         "tv_validate_tree": (st, [I32, P, P, I32, I32]),
         "tv_validate_pages": (st, [I32, P, P, P, P, I32, I32]),

@@ -168,6 +168,19 @@ tv_status tree_kv_commit(const tv_attn_desc* desc, int32_t num_layers, int64_t l
   return TV_OK;
 }
 
+tv_status tree_draw_siblings(int32_t rows, int32_t vocab, const float* draft_logits,
+                             const int32_t* counts, const float* temperature, uint32_t stream_id,
+                             uint64_t seed, int32_t* tokens, void* status_workspace,
+                             hipStream_t stream) {
+  if (rows < 1 || vocab < 1 || rows > 0x7fffffff) return TV_ERR_SHAPE;
+  if (!draft_logits || !counts || !temperature || !tokens) return TV_ERR_NULL;
+  hipError_t e = tv::launch_draw_siblings(rows, vocab, draft_logits, counts, temperature, stream_id,
+                                          seed, tokens, static_cast<uint32_t*>(status_workspace),
+                                          stream);
+  if (e != hipSuccess) return hip_fail(e, "tree_draw_siblings");
+  return TV_OK;
+}
+
 tv_status tv_tree_meta(int32_t batch, int32_t max_nodes, const int32_t* node_indptr,
                        const int32_t* parent, int32_t* depth, uint32_t* anc_bits,
                        int32_t* first_child, int32_t* next_sibling, void* status_workspace,

@@ -90,6 +90,11 @@ hipError_t launch_kv_commit(const tv_attn_desc& d, int32_t num_layers, long long
                             const int32_t* kv_keep, const int32_t* out_len, int32_t max_depth,
                             uint32_t* status, hipStream_t stream);
 
+hipError_t launch_draw_siblings(int32_t rows, int32_t vocab, const float* draft_logits,
+                                const int32_t* counts, const float* temperature, uint32_t stream_id,
+                                uint64_t seed, int32_t* tokens, uint32_t* status,
+                                hipStream_t stream);
+
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream);
 
 }  // namespace tv
