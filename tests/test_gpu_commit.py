@@ -148,9 +148,6 @@ def test_bad_keep_lists_are_reported_and_untouched(mutation, bit):
     rng = np.random.default_rng(4)
     trees = [random_tree(rng, 24, depth_cap=6) for _ in range(4)]
     inp = make_attention_inputs(rng, rng, trees, [10, 20, 30, 40], 4, 2, 64, dtype="bf16")
-
-    def force_deep(kv_keep, out_len):
-        pass
     kv_keep, out_len, W = _keep_lists(inp, trees, rng, W=10)
     r = int(np.argmax(out_len))
     n = int(out_len[r])
@@ -173,3 +170,57 @@ def test_bad_keep_lists_are_reported_and_untouched(mutation, bit):
                               kv_keep, good_o)
     assert np.array_equal(kg.view(np.uint8), ko.view(np.uint8))
     assert np.array_equal(vg.view(np.uint8), vo.view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_attend_commit_then_decode_matches_tree_row(dtype):
+    """End to end on the GPU: tree attention over a tree, commit of a root
+    path's K/V, then a one-row tree at the committed position (prefix
+    P + n - 1, the row's own key at P + n - 1) must give the tree row of the
+    path's last node (SpecInfer's equivalence; [survey, Timeline])."""
+    import torch
+    import tree_verification_verify_amd as tv
+    from workloads.device import attention_tensors
+    from workloads.inputs import AttentionInputs
+    from gpu_run import run_attention
+    rng = np.random.default_rng(11)
+    trees = [random_tree(rng, int(n), depth_cap=7) for n in rng.integers(8, 33, size=6)]
+    prefixes = [int(x) for x in rng.integers(200, 900, size=6)]
+    D = 128 if dtype == "bf16" else 64
+    inp = make_attention_inputs(rng, rng, trees, prefixes, 8, 2, D, dtype=dtype)
+    kv_keep, out_len, W = _keep_lists(inp, trees, rng)
+    ends = []
+    for r in range(inp.batch):
+        n = int(out_len[r])
+        ends.append(int(kv_keep[r, n - 1]) - prefixes[r])
+    tree_out, st, _ = run_attention(inp)
+    assert st == 0
+    # commit on the GPU (one layer: the pools themselves)
+    t = attention_tensors(inp)
+    desc = tv.attn_desc(inp.batch, inp.num_q_heads, inp.num_kv_heads, inp.head_dim,
+                        inp.max_nodes, inp.max_depth, inp.max_kv_len, inp.num_pages, dtype)
+    ws = tv.alloc_workspace(4096)
+    tv.tree_kv_commit(desc, t["k_pages"], t["v_pages"], t["page_indptr"], t["page_indices"],
+                      t["prefix_len"], torch.from_numpy(kv_keep).cuda(),
+                      torch.from_numpy(out_len).cuda(), W - 1, num_layers=1, status_workspace=ws)
+    assert tv.device_status(ws)[0] == 0
+    bits = (lambda x: x.view(torch.int16).cpu().numpy().view(np.uint16)) if dtype == "bf16" else \
+        (lambda x: x.cpu().numpy())
+    k_new, v_new = bits(t["k_pages"]), bits(t["v_pages"])
+    # one-row trees at P + n - 1 with the queries of the paths' last nodes
+    q_rows = np.stack([inp.q[int(inp.node_indptr[r]) + ends[r]] for r in range(inp.batch)])
+    one = AttentionInputs(
+        dtype=dtype, num_q_heads=inp.num_q_heads, num_kv_heads=inp.num_kv_heads, head_dim=D,
+        q=q_rows, k_pages=k_new, v_pages=v_new, page_indptr=inp.page_indptr,
+        page_indices=inp.page_indices,
+        prefix_len=np.array([prefixes[r] + int(out_len[r]) - 1 for r in range(inp.batch)],
+                            dtype=np.int32),
+        node_indptr=np.arange(inp.batch + 1, dtype=np.int32),
+        parent=np.full(inp.batch, -1, dtype=np.int32), sm_scale=inp.sm_scale)
+    dec_out, st, _ = run_attention(one)
+    assert st == 0
+    tol = 2e-2 if dtype == "bf16" else 1e-5
+    ref = oracle.tree_attention_rows(inp, [(r, ends[r]) for r in range(inp.batch)])
+    for r in range(inp.batch):
+        assert np.abs(dec_out[r] - ref[r]).max() <= tol
+        assert np.abs(tree_out[int(inp.node_indptr[r]) + ends[r]] - ref[r]).max() <= tol
