@@ -14,13 +14,15 @@
 // output word y%4: u = ((word >> 8) + 1/2) / 2^24, strictly inside (0, 1).
 //
 // One workgroup of 256 threads per row streams the row once (float4 loads,
-// one Philox call per float4). Each thread keeps its K best (score, id) in
-// registers, sorted (K = the next power of two >= k); a token enters only if
-// an upper bound of its score reaches the wave's threshold (below) and the
-// thread's K-th: -ln u >= 1 - u gives g <= -ln(1 - u), evaluated with the
-// fast hardware log plus a margin, so the exact noise (log1p for u near 1,
-// where ln u loses its relative precision) is computed for few tokens. The
-// threads' lists are merged by k rounds of a block argmax.
+// two ahead of the one being scored; one Philox call per float4). Each thread
+// keeps its K best (score, id) in registers, sorted (K = the next power of
+// two >= k). Per float4 the four score bounds (-ln u >= 1 - u gives
+// g <= -ln(1 - u), fast hardware log plus a margin) are tested against the
+// wave's threshold (below) at once: a wave executes per-token work when any
+// lane needs it, so it is entered only for the few float4 that can enter a
+// list; there each token is scored exactly (log1p for u near 1, where ln u
+// loses its relative precision) and inserted. The threads' lists are merged
+// by k rounds of a block argmax.
 #include "tv_device.hpp"
 #include "tv_internal.hpp"
 
@@ -156,26 +158,41 @@ __device__ void draw_row(const SibParams& p, int r, int k, float T, int32_t* out
   const bool vec = (V & 3) == 0 && (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
   int step = 0;
   if (vec) {
-    constexpr int U = 1;
     const int n4 = V >> 2;
     const float4* row4 = reinterpret_cast<const float4*>(row);
-    for (int base = tid; base < n4; base += U * kSibThreads) {
-      float4 d[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c4 = base + u * kSibThreads;
-        d[u] = c4 < n4 ? row4[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c4 = base + u * kSibThreads;
-        if (c4 >= n4) break;
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (noisy) w = philox4x32_10(make_uint4(uint32_t(c4), uint32_t(r), p.stream, 0u), p.key0, p.key1);
-        consider(d[u].x, w.x, 4 * c4);
-        consider(d[u].y, w.y, 4 * c4 + 1);
-        consider(d[u].z, w.z, 4 * c4 + 2);
-        consider(d[u].w, w.w, 4 * c4 + 3);
+    // the next two float4 of this thread load while the current one is scored
+    const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 d1 = tid < n4 ? row4[tid] : zero4;
+    float4 d2 = tid + kSibThreads < n4 ? row4[tid + kSibThreads] : zero4;
+    for (int c4 = tid; c4 < n4; c4 += kSibThreads) {
+      const float4 d = d1;
+      d1 = d2;
+      d2 = c4 + 2 * kSibThreads < n4 ? row4[c4 + 2 * kSibThreads] : zero4;
+      // Finite check for the four logits at once, then one test of the
+      // largest score bound against the threshold: the per-token work below
+      // runs only for the few float4 that can enter a list.
+      bad |= !(fabsf(d.x) <= 3.4e38f) | !(fabsf(d.y) <= 3.4e38f) | !(fabsf(d.z) <= 3.4e38f) |
+             !(fabsf(d.w) <= 3.4e38f);
+      if (!noisy) {
+        if (fmaxf(fmaxf(d.x, d.y), fmaxf(d.z, d.w)) >= theta) {
+          consider(d.x, 0u, 4 * c4);
+          consider(d.y, 0u, 4 * c4 + 1);
+          consider(d.z, 0u, 4 * c4 + 2);
+          consider(d.w, 0u, 4 * c4 + 3);
+        }
+      } else {
+        const uint4 w = philox4x32_10(make_uint4(uint32_t(c4), uint32_t(r), p.stream, 0u), p.key0, p.key1);
+        auto bound = [&](float dv, uint32_t wv) __attribute__((always_inline)) {
+          const float x = (float(16777216u - (wv >> 8)) - 0.5f) * (1.f / 16777216.f);  // 1 - u
+          return dv * invT - __logf(x) + 1e-3f;  // g <= -ln(1 - u)
+        };
+        const float bmax = fmaxf(fmaxf(bound(d.x, w.x), bound(d.y, w.y)), fmaxf(bound(d.z, w.z), bound(d.w, w.w)));
+        if (bmax >= theta) {
+          consider(d.x, w.x, 4 * c4);
+          consider(d.y, w.y, 4 * c4 + 1);
+          consider(d.z, w.z, 4 * c4 + 2);
+          consider(d.w, w.w, 4 * c4 + 3);
+        }
       }
       if ((++step & 7) == 0) refresh();
     }
