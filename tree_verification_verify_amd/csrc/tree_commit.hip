@@ -15,7 +15,9 @@
 // 16-byte pieces; V is transposed within each page ([page][head][D][slot]), so
 // a token's V is one element per channel: the writes run with the entry index
 // fastest, so a channel's run of consecutive destination slots is one
-// contiguous store.
+// contiguous store. Every store is non-temporal: a moved V column dirties one
+// line in each of 32 rows of its page block, and stores kept in L2 left that
+// many dirty lines for the end of the kernel to write back.
 #include "tv_device.hpp"
 #include "tv_internal.hpp"
 
@@ -172,7 +174,8 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(CommitParams 
           const int q = q0 + i / KP, piece = i % KP;
           const int h = q / m, e = q - h * m;
           T* row = kb + (size_t(s_dpg[e]) * p.Hkv + h) * head_block + size_t(s_dsl[e]) * D;
-          reinterpret_cast<uint4*>(row)[piece] = kr[k];
+          typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+          __builtin_nontemporal_store(__builtin_bit_cast(u32x4, kr[k]), reinterpret_cast<u32x4*>(row) + piece);
         }
       }
 #pragma unroll
@@ -182,7 +185,7 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(CommitParams 
           const int ch = i / c, qq = i - ch * c;
           const int q = q0 + qq;
           const int h = q / m, e = q - h * m;
-          vb[(size_t(s_dpg[e]) * p.Hkv + h) * head_block + size_t(ch) * kPage + s_dsl[e]] = vr[k];
+          __builtin_nontemporal_store(vr[k], vb + (size_t(s_dpg[e]) * p.Hkv + h) * head_block + size_t(ch) * kPage + s_dsl[e]);
         }
       }
       __syncthreads();  // every store of this chunk precedes the next chunk's reads
