@@ -224,3 +224,43 @@ def test_attend_commit_then_decode_matches_tree_row(dtype):
     for r in range(inp.batch):
         assert np.abs(dec_out[r] - ref[r]).max() <= tol
         assert np.abs(tree_out[int(inp.node_indptr[r]) + ends[r]] - ref[r]).max() <= tol
+
+
+def test_walk_path_commit_on_the_gpu_matches_the_oracle():
+    """The next-step chain on the GPU: sampling walk and accepted path on a
+    highload sub-batch, then the commit of the GPU's own keep-lists over two
+    layers; the keep-lists equal the oracle's and the pools are bit-exact
+    with the oracle's commit."""
+    import torch
+    import tree_verification_verify_amd as tv
+    from workloads.device import sampler_tensors
+    cfg = make_config("highload", batch=12, vocab=4096)
+    s, inp = cfg.sampler, cfg.attn
+    st = sampler_tensors(s)
+    md = 16
+    sdesc = tv.sample_desc(s.batch, s.vocab, s.max_nodes, md)
+    sws = tv.alloc_workspace(tv.sample_workspace_size(sdesc))
+    T = int(s.node_indptr[-1])
+    flag = torch.empty(T, dtype=torch.int8, device="cuda")
+    nt = torch.empty(T, dtype=torch.int32, device="cuda")
+    tv.tree_spec_sample(sdesc, st["target_logits"], st["draft_logits"], st["tokens"],
+                        st["node_indptr"], st["parent"], st["temperature"], st["uniforms"],
+                        flag, nt, sws)
+    B = s.batch
+    pn = torch.empty(B * (md + 1), dtype=torch.int32, device="cuda")
+    ot, kk = torch.empty_like(pn), torch.empty_like(pn)
+    ol = torch.empty(B, dtype=torch.int32, device="cuda")
+    prefix = torch.from_numpy(np.asarray(inp.prefix_len, dtype=np.int32)).cuda()
+    tv.tree_accept_path(B, md, st["node_indptr"], st["parent"], st["tokens"], flag, nt, prefix,
+                        pn, ot, ol, kk, sws)
+    assert tv.device_status(sws)[0] == 0
+    keep = kk.cpu().numpy().reshape(B, md + 1)
+    olen = ol.cpu().numpy()
+    rf, rn, logs = oracle.tree_spec_sample(s)
+    _, _, rol, rkeep = oracle.tree_accept_path(s.node_indptr, s.parent, s.tokens, rf, rn,
+                                               cfg.prefix_lens, md)
+    # requests whose walk met a near-threshold decision may differ; none expected here
+    assert np.array_equal(olen, rol) and np.array_equal(keep, rkeep)
+    rng = np.random.default_rng(21)
+    k, v = _layers(inp, 2, rng)
+    _compare(inp, k, v, keep, olen, md)
