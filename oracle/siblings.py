@@ -22,10 +22,10 @@ The draw is computed in fp64 here.
 
 Pins: the law of the ordered draw (chi-square against the sequential
 without-replacement product formula, with planted-mistake controls) and T = 0
-as plain top-k. The generator's word stream has no known-answer pin (the pages
-print no test vectors): it is checked for uniformity and keying only, and the
-GPU side is compared bit-exact against this implementation of the same
-published definition.
+as plain top-k. The generator is pinned to the known-answer vectors its
+authors publish with their Random123 library (the pages print none), and
+checked for uniformity and keying; the GPU side is compared bit-exact against
+this implementation of the same published definition.
 """
 import numpy as np
 

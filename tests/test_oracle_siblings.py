@@ -4,9 +4,11 @@ The law of the ordered k-tuple is checked against the product formula of k
 sequential draws without replacement from softmax(d/T) (what RSD and TreeSpark
 mean by drawing siblings without replacement), by a chi-square test over many
 independent rows; planted mistakes in the noise must fail it. T = 0 is the
-closed-form top-k with lowest-index ties.
+closed-form top-k with lowest-index ties. The generator itself is pinned to
+the known-answer vectors its authors publish (tests/golden/philox4x32_10_kat.txt).
 """
 import itertools
+import pathlib
 
 import numpy as np
 import pytest
@@ -110,3 +112,41 @@ def test_philox_uniforms_are_uniform_and_keyed():
     for other in (S.uniforms(64, 4, 1, 2024), S.uniforms(64, 3, 2, 2024),
                   S.uniforms(64, 3, 1, 2025), S.uniforms(64, 3, 1, 2024 + (1 << 32))):
         assert (other != base).mean() > 0.9
+
+
+def _kat_vectors():
+    path = pathlib.Path(__file__).parent / "golden" / "philox4x32_10_kat.txt"
+    out = []
+    for line in path.read_text().splitlines():
+        if line.strip() and not line.startswith("#"):
+            c, k, w = (tuple(int(x, 16) for x in part.split()) for part in line.split("|"))
+            out.append((c, k, w))
+    return out
+
+
+def test_philox_matches_the_published_known_answers():
+    vectors = _kat_vectors()
+    assert len(vectors) == 3
+    for c, k, want in vectors:
+        got = S.philox4x32_10(*c, *k)
+        assert tuple(int(x) for x in got) == want
+
+
+def test_philox_known_answers_catch_planted_round_mistakes():
+    """Nine rounds, or a key schedule bumped before the first round, miss the vectors."""
+    c, k, want = _kat_vectors()[2]
+
+    def variant(rounds, bump_first):
+        c0, c1, c2, c3 = (np.uint64(x) for x in c)
+        k0, k1 = k
+        for rnd in range(rounds):
+            if rnd or bump_first:
+                k0, k1 = (k0 + S.W0) & S.MASK, (k1 + S.W1) & S.MASK
+            p0, p1 = np.uint64(S.M0) * c0, np.uint64(S.M1) * c2
+            c0, c1, c2, c3 = ((p1 >> np.uint64(32)) ^ c1 ^ np.uint64(k0), p1 & np.uint64(S.MASK),
+                              (p0 >> np.uint64(32)) ^ c3 ^ np.uint64(k1), p0 & np.uint64(S.MASK))
+        return tuple(int(x) for x in (c0, c1, c2, c3))
+
+    assert variant(10, False) == want   # the same construction, unplanted, meets the vector
+    assert variant(9, False) != want
+    assert variant(10, True) != want
