@@ -19,7 +19,7 @@ never calls it.
 from .tree import (check_tree, depths, ancestors_or_self, children,
                    ancestor_bitsets, first_child_next_sibling)
 from .attention import tree_attention, tree_attention_rows, decode_values
-from .sampler import (softmax_T, proposal_without, residual_update,
+from .sampler import (softmax_T, proposal_without, proposal_with, residual_update,
                       acceptance_ratio, inverse_cdf, greedy_request,
                       walk_request, tree_spec_sample)
 from .path import accept_path_request, tree_accept_path
@@ -30,7 +30,7 @@ from .enumerate import enumerate_node_laws
 __all__ = [
     "check_tree", "depths", "ancestors_or_self", "children", "ancestor_bitsets",
     "first_child_next_sibling", "tree_attention", "tree_attention_rows",
-    "decode_values", "softmax_T", "proposal_without", "residual_update",
+    "decode_values", "softmax_T", "proposal_without", "proposal_with", "residual_update",
     "acceptance_ratio", "inverse_cdf", "greedy_request", "walk_request",
     "tree_spec_sample", "accept_path_request", "tree_accept_path",
     "BadKeepList", "check_keep", "kv_commit_layer", "kv_commit",

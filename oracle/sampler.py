@@ -3,8 +3,10 @@
 Sources:
   [survey, Timeline]   SpecInfer's multi-step speculative sampling: a
                        recursive, residual-renormalising rejection walk.
-  [survey, Taxonomy]   rule (a) greedy exact match; rule (c) recursive
-                       rejection sampling without replacement.
+  [survey, Taxonomy]   rule (a) greedy exact match; rule (b) multi-draft
+                       rejection sampling with replacement (SpecInfer's MSS,
+                       MCSD Algorithm 1); rule (c) recursive rejection
+                       sampling without replacement.
   [TreeSpark §1, §3.3] siblings drawn without replacement from the residual
                        q_T; each proposal is rebuilt from the shared logits and
                        the sibling draw order; accept child x with probability
@@ -20,8 +22,12 @@ Readings of points the pages leave open (each also listed in the design notes):
   * row i of the logits is the distribution of the token after node i
     ([TreeSpark §3.1] LM-shifted alignment);
   * children of v are tested in ascending row index (= draw order);
-  * the stage-j proposal is q with the already-drawn siblings zeroed, divided
-    by 1 - sum of their q mass; the residual subtracts that proposal;
+  * rule (c): the stage-j proposal is q with the already-drawn siblings
+    zeroed, divided by 1 - sum of their q mass; the residual subtracts that
+    proposal;
+  * rule (b): siblings are independent draws from q, so every stage's
+    proposal is q itself (a repeated token meets a residual that is already 0
+    there and is rejected);
   * accept iff u < ratio (ratio >= 1 always accepts); u_acc = uniforms[c][0]
     for node c's own test, u_res = uniforms[v][1] for the draw if the walk
     stops at v;
@@ -54,6 +60,13 @@ def proposal_without(q, drawn):
         qj[idx] = 0.0
         qj /= (1.0 - mass)
     return qj
+
+
+def proposal_with(q, drawn):
+    """Stage proposal of rule (b): the siblings are independent draws from q
+    ([survey, Taxonomy] rule (b): SpecInfer's MSS, MCSD Algorithm 1), so the
+    proposal stays q whatever was drawn before."""
+    return np.array(q, dtype=np.float64, copy=True)
 
 
 def residual_update(pres, qj):
@@ -102,8 +115,9 @@ def greedy_request(t_rows, tokens, parent):
     return flag, nt, []
 
 
-def walk_request(t_rows, d_rows, tokens, parent, T, uniforms):
-    """T > 0: the recursive rejection walk without replacement.
+def walk_request(t_rows, d_rows, tokens, parent, T, uniforms, replacement=False):
+    """T > 0: the recursive rejection walk, without replacement (rule (c)) or,
+    with replacement=True, with replacement (rule (b)).
 
     Returns (flag[n] int8, next_token[n] int32, log) where log lists
     (kind, node, margin) for every acceptance test with ratio < 1 ('accept'),
@@ -125,7 +139,7 @@ def walk_request(t_rows, d_rows, tokens, parent, T, uniforms):
         accepted = None
         for c in ch[v]:
             x = int(tokens[c])
-            qj = proposal_without(q, drawn)
+            qj = proposal_with(q, drawn) if replacement else proposal_without(q, drawn)
             ratio = acceptance_ratio(pres[x], qj[x])
             u = float(uniforms[c][0])
             if ratio < 1.0:
@@ -147,9 +161,10 @@ def walk_request(t_rows, d_rows, tokens, parent, T, uniforms):
         return flag, nt, log
 
 
-def tree_spec_sample(inp):
+def tree_spec_sample(inp, replacement=False):
     """Whole batch. Returns accept_flag [T] int8, next_token [T] int32 and a
-    per-request list of decision logs."""
+    per-request list of decision logs. replacement selects rule (b) for the
+    T > 0 requests (rule (c) otherwise)."""
     T_total = int(inp.node_indptr[-1])
     flags = np.zeros(T_total, dtype=np.int8)
     nts = np.full(T_total, -1, dtype=np.int32)
@@ -162,7 +177,8 @@ def tree_spec_sample(inp):
             f, nt, log = greedy_request(inp.target_logits[a:b], inp.tokens[a:b], par)
         else:
             f, nt, log = walk_request(inp.target_logits[a:b], inp.draft_logits[a:b],
-                                      inp.tokens[a:b], par, temp, inp.uniforms[a:b])
+                                      inp.tokens[a:b], par, temp, inp.uniforms[a:b],
+                                      replacement=replacement)
         flags[a:b] = f
         nts[a:b] = nt
         logs.append(log)

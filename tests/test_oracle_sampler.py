@@ -54,6 +54,64 @@ def test_exact_enumeration_law_equals_target(seed):
         np.testing.assert_allclose(law / reach, dist("p", path), rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_exact_enumeration_law_with_replacement_equals_target(seed):
+    """Rule (b) (SpecInfer's MSS, MCSD Algorithm 1): with siblings drawn
+    independently from q and the proposal kept at q, the next emitted token
+    after any reached node has law p_node exactly, also with more siblings
+    than tokens (repeats)."""
+    rng = np.random.default_rng(100 + seed)
+    V = int(rng.integers(2, 5))
+    cache = {}
+
+    def dist(kind, path):
+        key = (kind, path)
+        if key not in cache:
+            cache[key] = _rand_dist(rng, V, zeros=int(rng.integers(0, 2)) if V > 2 else 0)
+        return cache[key]
+
+    k_by_depth = [int(rng.integers(1, 5)), int(rng.integers(0, 3)), 0]
+    laws = oracle.enumerate_node_laws(lambda pth: dist("p", pth), lambda pth: dist("q", pth),
+                                      lambda pth: k_by_depth[len(pth)] if len(pth) < 3 else 0, V,
+                                      rule="with")
+    assert abs(laws[()][0] - 1.0) < 1e-15
+    for path, (reach, law) in laws.items():
+        if reach < 1e-300:
+            continue
+        np.testing.assert_allclose(law / reach, dist("p", path), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("rule,draws", [("without", "with"), ("with", "without"),
+                                        ("without", "topk"), ("with", "topk")])
+def test_mismatched_draws_and_rules_are_biased(rule, draws):
+    """Each rule is exact only for its own draw scheme; deterministic top-k
+    siblings ([TreeSpark §5.4, Table 9]) are biased under either rule."""
+    rng = np.random.default_rng(7)
+    p, q = _rand_dist(rng, 4), _rand_dist(rng, 4)
+    laws = oracle.enumerate_node_laws(lambda _: p, lambda _: q, lambda pth: 2 if not pth else 0, 4,
+                                      rule=rule, draws=draws)
+    reach, law = laws[()]
+    assert abs(reach - 1.0) < 1e-12
+    assert 0.5 * np.abs(law - p).sum() > 1e-3
+
+
+@pytest.mark.parametrize("rule", ["without", "with"])
+def test_topk_siblings_with_q_equal_p_emit_only_the_argmax(rule):
+    """[TreeSpark §5.4]: when q is close to p the first top-k candidate is
+    almost always accepted. At q = p its ratio is 1, so the emitted token is
+    the argmax with probability 1 (TV distance 1 - max p), while sampled
+    siblings keep the law p."""
+    p = np.array([0.344, 0.25, 0.2, 0.126, 0.08])
+    laws = oracle.enumerate_node_laws(lambda _: p, lambda _: p, lambda pth: 3 if not pth else 0, 5,
+                                      rule=rule, draws="topk")
+    reach, law = laws[()]
+    np.testing.assert_allclose(law, np.eye(5)[0], atol=1e-15)
+    assert abs(0.5 * np.abs(law - p).sum() - (1 - p.max())) < 1e-12
+    fair = oracle.enumerate_node_laws(lambda _: p, lambda _: p, lambda pth: 3 if not pth else 0, 5,
+                                      rule=rule)[()][1]
+    np.testing.assert_allclose(fair, p, atol=1e-12)
+
+
 def test_enumeration_detects_a_planted_mistake(monkeypatch):
     """The enumeration pin fails when the residual forgets to subtract q."""
     import oracle.enumerate as en
@@ -68,9 +126,9 @@ def test_enumeration_detects_a_planted_mistake(monkeypatch):
     assert np.abs(law / reach - p).max() > 1e-3
 
 
-def _parse_hand_cases():
+def _parse_hand_cases(name="sampler_hand_cases.txt"):
     cases = []
-    for line in open(os.path.join(GOLDEN, "sampler_hand_cases.txt")):
+    for line in open(os.path.join(GOLDEN, name)):
         if not line.strip() or line.startswith("#"):
             continue
         f = [s.strip() for s in line.split("|")]
@@ -81,7 +139,11 @@ def _parse_hand_cases():
     return cases
 
 
-@pytest.mark.parametrize("case", _parse_hand_cases(), ids=lambda c: c["name"])
+_HAND = ([dict(c, replacement=False) for c in _parse_hand_cases()]
+         + [dict(c, replacement=True) for c in _parse_hand_cases("sampler_hand_cases_with_replacement.txt")])
+
+
+@pytest.mark.parametrize("case", _HAND, ids=lambda c: c["name"])
 def test_hand_derived_cases(case):
     k = len(case["tokens"])
     parent = star_tree(k + 1)
@@ -96,7 +158,7 @@ def test_hand_derived_cases(case):
     u[1:, 0] = case["u_acc"]
     u[0, 1] = case["u_res"]
     u[1:, 1] = 0.5
-    flag, nt, _ = oracle.walk_request(t, d, tokens, parent, 1.0, u)
+    flag, nt, _ = oracle.walk_request(t, d, tokens, parent, 1.0, u, replacement=case["replacement"])
     assert list(flag[1:]) == case["flags"]
     assert nt[0] == case["nt"]
 
