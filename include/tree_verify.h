@@ -63,6 +63,14 @@ typedef enum {
 
 typedef enum { TV_FP32 = 0, TV_BF16 = 1 } tv_dtype;
 
+/* Verification rule of tree_spec_sample at T > 0 ([survey] Taxonomy).
+ * Without replacement (rule (c)): siblings are distinct draws, each from q
+ * without the tokens drawn before it. With replacement (rule (b), SpecInfer's
+ * multi-step speculative sampling, MCSD Algorithm 1): siblings are
+ * independent draws from q. Each rule reproduces the target distribution
+ * only for siblings drawn its own way. */
+typedef enum { TV_RULE_WITHOUT_REPLACEMENT = 0, TV_RULE_WITH_REPLACEMENT = 1 } tv_rule;
+
 /* Bits of the device status word (first 4 bytes of a workspace). */
 enum {
   TV_DEV_TREE = 1u << 0,
@@ -96,6 +104,7 @@ typedef struct {
   int32_t vocab;         /* V >= 1 */
   int32_t max_nodes;     /* >= max_r N_r, <= 65536 */
   int32_t max_depth;     /* >= deepest node */
+  int32_t rule;          /* tv_rule; 0 (a zero-filled desc) is without replacement */
 } tv_sample_desc;
 
 /* ---- workspace -------------------------------------------------------- */
@@ -157,19 +166,22 @@ tv_status tree_verify_attn(const tv_attn_desc* desc,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Multi-step speculative sampling over the tree ([survey] Timeline and
- * Taxonomy rules (a) and (c); [TreeSpark] §1 and §3.3, Proposition 1).
+ * Taxonomy rules (a), (c) and (b); [TreeSpark] §1 and §3.3, Proposition 1).
  *
+ * Returns TV_ERR_SHAPE when desc->rule is not a tv_rule value.
  * Row i of the logits is the distribution of the token AFTER node i
  * ([TreeSpark] §3.1, LM-shifted alignment). Per request r with T = temperature[r]:
  *   T == 0 (greedy exact match): next_token[i] = argmax target row i (lowest
  *     index on ties) for EVERY node; accept_flag[i] = (tokens[i] ==
  *     next_token[parent[i]]); accept_flag[root] = 1.
- *   T > 0 (rejection walk without replacement): starting at the root v, with
+ *   T > 0 (rejection walk): starting at the root v, with
  *     p = softmax(target_v / T), q = softmax(draft_v / T), the children
  *     c_1 < c_2 < ... of v (draw order) are tested in turn: c_j is accepted
  *     iff uniforms[c_j][0] < p_j(x_j) / q_j(x_j), where q_j is q with the
- *     tokens x_1..x_{j-1} removed and renormalised and p_j the residual
- *     (p_1 = p; after a rejection p_{j+1} = max(p_j - q_j, 0) renormalised).
+ *     tokens x_1..x_{j-1} removed and renormalised (desc->rule ==
+ *     TV_RULE_WITHOUT_REPLACEMENT) or q itself (TV_RULE_WITH_REPLACEMENT), and
+ *     p_j the residual (p_1 = p; after a rejection p_{j+1} = max(p_j - q_j, 0)
+ *     renormalised).
  *     An accepted child becomes v. When no child is accepted (or v is a
  *     leaf) the walk stops: next_token[v] = smallest y with
  *     cumsum(p_final)[y] > uniforms[v][1] * sum(p_final), p_final being the
@@ -179,7 +191,8 @@ tv_status tree_verify_attn(const tv_attn_desc* desc,
  * Arguments:
  *   target_logits, draft_logits [T][V] fp32; draft_logits may be NULL when
  *     every temperature is 0 (a T > 0 request then sets TV_DEV_LOGITS).
- *   tokens [T] int32 token of each node (root ignored); siblings distinct.
+ *   tokens [T] int32 token of each node (root ignored); siblings distinct
+ *     under the without-replacement rule, repeats allowed with replacement.
  *   node_indptr [B+1], parent [T] int32; temperature [B] fp32 >= 0;
  *   uniforms [T][2] fp32 in [0,1).
  *   accept_flag [T] int8, next_token [T] int32: outputs.

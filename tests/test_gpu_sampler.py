@@ -20,9 +20,9 @@ def _run(inp, **kw):
     return run_sampler(inp, **kw)
 
 
-def _compare(inp, got, prefix_lens=None, allow_near=0):
+def _compare(inp, got, prefix_lens=None, allow_near=0, replacement=False):
     assert got["status"] == 0, (got["status"], got["bits"])
-    flags, nts, logs = oracle.tree_spec_sample(inp)
+    flags, nts, logs = oracle.tree_spec_sample(inp, replacement=replacement)
     md = got["max_depth"]
     B = inp.batch
     prefix_lens = prefix_lens if prefix_lens is not None else [0] * B
@@ -246,3 +246,83 @@ def test_greedy_split_rows_and_ties(V):
     assert got["next_token"][0] == 100
     assert got["next_token"][1] == V - 1
     _compare(inp, got)
+
+
+# ---- the with-replacement rule (survey page, Taxonomy rule (b)) ----------
+
+
+@pytest.mark.parametrize("temp", ["mixed", 1.0])
+def test_highload_with_replacement(temp):
+    cfg = make_config("highload", attention=False, temperature=temp, draws="with")
+    inp = cfg.sampler
+    _compare(inp, _run(inp, max_depth=8, prefix_lens=cfg.prefix_lens, replacement=True),
+             cfg.prefix_lens, replacement=True)
+
+
+@pytest.mark.parametrize("V", [3, 7, 64, 1000])
+def test_random_small_with_replacement(V):
+    """Small vocabularies make repeated siblings common, and more children
+    than tokens possible (so no T = 0 request here: greedy exact match needs
+    distinct siblings)."""
+    rng = np.random.default_rng(300 + V)
+    trees = [random_tree(rng, int(rng.integers(1, 25)), depth_cap=int(rng.integers(1, 6)))
+             for _ in range(40)]
+    temps = rng.choice([0.25, 0.5, 1.0, 2.0], size=40)
+    inp = make_sampler_inputs(rng, rng, rng, trees, V, temps,
+                              mode="independent" if V < 100 else "correlated", draws="with")
+    repeats = 0
+    for r in range(inp.batch):
+        a, b = int(inp.node_indptr[r]), int(inp.node_indptr[r + 1])
+        par, tok = inp.parent[a:b], inp.tokens[a:b]
+        for v in range(b - a):
+            kids = tok[par == v]
+            repeats += len(set(kids.tolist())) < len(kids)
+    assert repeats > 0  # the repeated-token case is exercised
+    _compare(inp, _run(inp, max_depth=6, replacement=True), replacement=True)
+
+
+def test_rules_differ_on_the_same_draws():
+    """The same without-replacement draws under both rules on a vocabulary
+    small enough that the drawn siblings hold much of q's mass (on a large
+    vocabulary the two proposals nearly coincide): the kernel follows the rule
+    it is given (each side against its own oracle rule)."""
+    rng = np.random.default_rng(21)
+    trees = [random_tree(rng, int(rng.integers(4, 25)), depth_cap=4) for _ in range(64)]
+    inp = make_sampler_inputs(rng, rng, rng, trees, 8, [1.0] * 64, mode="independent")
+    a = _run(inp, max_depth=4, replacement=False)
+    b = _run(inp, max_depth=4, replacement=True)
+    _compare(inp, a, replacement=False)
+    _compare(inp, b, replacement=True)
+    assert (a["flag"] != b["flag"]).any() or (a["next_token"] != b["next_token"]).any()
+
+
+def test_more_children_than_listed_with_replacement():
+    """150 independent draws at the root (past the per-visit list of 64)."""
+    rng = np.random.default_rng(13)
+    inp = make_sampler_inputs(rng, rng, rng, [star_tree(151), star_tree(90)], 4096, [1.0, 2.0],
+                              mode="independent", draws="with")
+    _compare(inp, _run(inp, max_depth=1, replacement=True), replacement=True)
+
+
+def test_monte_carlo_tv_with_replacement_on_gpu():
+    """Rule (b) on the GPU path: 3000 one-level walks, root with 3 independent
+    draws from q; the first emitted token's TV to p is within the 99th
+    percentile of direct sampling's TV at equal n."""
+    rng = np.random.default_rng(17)
+    V, k, n = 16, 3, 3000
+    logits = (rng.standard_normal(V) * 1.2).astype(np.float32)
+    dl = (logits + rng.standard_normal(V).astype(np.float32) * 0.4).astype(np.float32)
+    inp = make_sampler_inputs(rng, rng, rng, [star_tree(k + 1)] * n, V, [1.0] * n)
+    inp.target_logits[:] = logits
+    inp.draft_logits[:] = dl
+    from workloads import independent_draw_tokens
+    for r in range(n):
+        inp.tokens[r * (k + 1) + 1:(r + 1) * (k + 1)] = independent_draw_tokens(rng, dl, k, 1.0)
+    got = _run(inp, max_depth=1, replacement=True)
+    first = got["out_tokens"][:, 0]
+    p = np.exp(logits.astype(np.float64) - logits.max())
+    p /= p.sum()
+    tv_walk = 0.5 * np.abs(np.bincount(first, minlength=V) / n - p).sum()
+    tvs = [0.5 * np.abs(rng.multinomial(n, p) / n - p).sum() for _ in range(300)]
+    assert tv_walk <= np.percentile(tvs, 99), (tv_walk, np.percentile(tvs, 99))
+    _compare(inp, got, replacement=True)

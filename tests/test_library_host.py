@@ -97,6 +97,14 @@ def test_sampler_host_errors():
                 tv.sample_desc(1, 10, 70000, 2)):
         assert lib.tv_sample_workspace_size(ctypes.byref(bad)) == 0
         assert call(bad, ok_ptrs) == SHAPE
+    for rule in (-1, 2):
+        bad = tv.sample_desc(4, 151936, 32, 8)
+        bad.rule = rule
+        assert lib.tv_sample_workspace_size(ctypes.byref(bad)) == 0
+        assert call(bad, ok_ptrs) == SHAPE
+    rep = tv.sample_desc(4, 151936, 32, 8, replacement=True)
+    assert rep.rule == tv.TV_RULE_WITH_REPLACEMENT
+    assert lib.tv_sample_workspace_size(ctypes.byref(rep)) == need
 
 
 def test_path_and_meta_host_errors():

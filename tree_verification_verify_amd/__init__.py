@@ -8,7 +8,7 @@ fallback: if the library is missing, calls raise.
 
 Entry points (same names as the C ABI):
   tree_verify_attn   tree-masked paged attention, one layer
-  tree_spec_sample   greedy / without-replacement rejection walk
+  tree_spec_sample   greedy / rejection walk without or with replacement
   tree_accept_path   longest accepted path, emitted tokens, KV keep-list
   tv_tree_meta       depth, ancestor bitsets, children lists
 """
@@ -17,10 +17,12 @@ import ctypes
 import numpy as np
 
 from . import _lib
-from ._lib import AttnDesc, SampleDesc, TV_BF16, TV_FP32, STATUS_NAMES, DEV_BITS
+from ._lib import (AttnDesc, SampleDesc, TV_BF16, TV_FP32, STATUS_NAMES, DEV_BITS,
+                   TV_RULE_WITHOUT_REPLACEMENT, TV_RULE_WITH_REPLACEMENT)
 
 __all__ = [
-    "TVError", "AttnDesc", "SampleDesc", "TV_BF16", "TV_FP32", "attn_desc",
+    "TVError", "AttnDesc", "SampleDesc", "TV_BF16", "TV_FP32", "TV_RULE_WITHOUT_REPLACEMENT",
+    "TV_RULE_WITH_REPLACEMENT", "attn_desc",
     "sample_desc", "attn_workspace_size", "sample_workspace_size", "alloc_workspace",
     "workspace_init", "device_status", "tree_verify_attn", "tree_spec_sample",
     "tree_accept_path", "tree_kv_commit", "tree_draw_siblings", "tv_tree_meta", "validate_tree", "validate_pages",
@@ -79,8 +81,11 @@ def attn_desc(batch, num_q_heads, num_kv_heads, head_dim, max_nodes, max_depth,
                     float(sm_scale))
 
 
-def sample_desc(batch, vocab, max_nodes, max_depth):
-    return SampleDesc(batch, vocab, max_nodes, max_depth)
+def sample_desc(batch, vocab, max_nodes, max_depth, replacement=False):
+    """replacement selects the with-replacement walk (independent sibling
+    draws) instead of the without-replacement one."""
+    return SampleDesc(batch, vocab, max_nodes, max_depth,
+                      TV_RULE_WITH_REPLACEMENT if replacement else TV_RULE_WITHOUT_REPLACEMENT)
 
 
 def attn_workspace_size(desc):

@@ -27,7 +27,12 @@ class AttnDesc(ctypes.Structure):
 
 class SampleDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("vocab", ctypes.c_int32),
-                ("max_nodes", ctypes.c_int32), ("max_depth", ctypes.c_int32)]
+                ("max_nodes", ctypes.c_int32), ("max_depth", ctypes.c_int32),
+                ("rule", ctypes.c_int32)]
+
+
+TV_RULE_WITHOUT_REPLACEMENT = 0
+TV_RULE_WITH_REPLACEMENT = 1
 
 
 EXPORTS = [

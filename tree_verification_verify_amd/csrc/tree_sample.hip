@@ -1,7 +1,8 @@
 // Multi-step speculative sampling over a draft tree (the verification walk).
 //
-// Rules: greedy exact match at T = 0 and recursive rejection sampling without
-// replacement at T > 0 (survey page, Taxonomy rules (a) and (c); SpecInfer's
+// Rules: greedy exact match at T = 0 and, at T > 0, recursive rejection
+// sampling without replacement or, as a per-call choice, with replacement
+// (survey page, Taxonomy rules (a), (c) and (b); SpecInfer's
 // residual-renormalising walk in its Timeline section), with the sibling
 // proposals rebuilt from the shared draft logits and the sibling draw order
 // (TreeSpark §1, §3.3 and Proposition 1), and one correction or bonus token
@@ -31,7 +32,7 @@
 //    residual is max(p - a q, 0) / B with scalars a_{j+1} = a_j + B_j / S_j,
 //    B_{j+1} = sum_y max(p(y) - a_{j+1} q(y), 0), S_j = 1 - sum_{i<j} q(x_i)
 //    (a rejected token's residual is already 0, so removing it from the
-//    proposal is implicit). The per-slice sums of the last pass (or of p, at
+//    proposal is implicit). With replacement the proposal stays q: S_j = 1. The per-slice sums of the last pass (or of p, at
 //    a leaf) locate the slice of the correction/bonus draw, so the draw
 //    rescans one slice only.
 //  * Arithmetic is fp64 (logits widened exactly). Vocabulary sums use a
@@ -80,6 +81,7 @@ struct SampleParams {
   uint32_t* status;
   char* req;  // per-request blocks of kReqBytes
   int B, V, W, max_nodes;
+  int with_replacement;  // rule (b): the stage proposal stays q
 };
 
 // ---------------------------------------------------------------------------
@@ -939,7 +941,7 @@ __device__ __attribute__((always_inline)) inline void walk(
         B = F;
         if (threadIdx.x < tm.W) L.s_slice[threadIdx.x] = pw;
       }
-      Sq -= qx;
+      if (!p.with_replacement) Sq -= qx;
       ++k;
       if (k < min(nkk, kKids))
         c = __builtin_amdgcn_readfirstlane(L.s_kid[k]);
@@ -1294,6 +1296,7 @@ __global__ __launch_bounds__(kThreads, 4) void sample_kernel(SampleParams p) {
 bool plan_sample(const tv_sample_desc& d, SamplePlan* out) {
   if (d.batch < 1 || d.vocab < 1 || d.max_nodes < 1 || d.max_nodes > 65536 || d.max_depth < 0)
     return false;
+  if (d.rule != TV_RULE_WITHOUT_REPLACEMENT && d.rule != TV_RULE_WITH_REPLACEMENT) return false;
   SamplePlan pl{};
   pl.threads = kThreads;
   pl.off_req = kHeaderBytes;
@@ -1348,6 +1351,7 @@ hipError_t launch_sample(const tv_sample_desc& d, const SamplePlan& pl, const Sa
   p.V = d.vocab;
   p.W = W;
   p.max_nodes = d.max_nodes;
+  p.with_replacement = d.rule == TV_RULE_WITH_REPLACEMENT;
   const dim3 grid(unsigned(grid_for(W))), block(kThreads);
   if (W == 1) {
     hipLaunchKernelGGL(sample_kernel, grid, block, 0, stream, p);

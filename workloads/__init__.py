@@ -12,7 +12,8 @@ from .trees import (expansion_vector_tree, random_tree, chain_tree, star_tree,
                     eagle2_tree, bfs_renumber, relabel_random_topological,
                     relabel_dfs, tree_depths)
 from .inputs import (make_attention_inputs, make_sampler_inputs,
-                     gumbel_topk_tokens, AttentionInputs, SamplerInputs)
+                     gumbel_topk_tokens, independent_draw_tokens, AttentionInputs,
+                     SamplerInputs)
 from .configs import CONFIGS, make_config, Config
 
 __all__ = [
@@ -20,6 +21,6 @@ __all__ = [
     "expansion_vector_tree", "random_tree", "chain_tree", "star_tree",
     "eagle2_tree", "bfs_renumber", "relabel_random_topological", "relabel_dfs",
     "tree_depths", "make_attention_inputs", "make_sampler_inputs",
-    "gumbel_topk_tokens", "AttentionInputs", "SamplerInputs",
+    "gumbel_topk_tokens", "independent_draw_tokens", "AttentionInputs", "SamplerInputs",
     "CONFIGS", "make_config", "Config",
 ]

@@ -47,7 +47,7 @@ def _streams(index, seed_offset=0):
 
 
 def make_config(name, attention=True, sampler=True, batch=None, vocab=None,
-                temperature="mixed", seed_offset=0, mode=None):
+                temperature="mixed", seed_offset=0, mode=None, draws="without"):
     """Build a config's inputs.
 
     batch: keep only the first ``batch`` requests (trees and prefixes are
@@ -124,5 +124,5 @@ def make_config(name, attention=True, sampler=True, batch=None, vocab=None,
     if sampler and V is not None:
         cfg.sampler = make_sampler_inputs(g_logits, g_draws, g_unif, trees,
                                           vocab if vocab is not None else V,
-                                          temps, mode=smode)
+                                          temps, mode=smode, draws=draws)
     return cfg

@@ -182,14 +182,31 @@ def gumbel_topk_tokens(rng, draft_row, k, temperature):
     return top.astype(np.int32)
 
 
+def independent_draw_tokens(rng, draft_row, k, temperature):
+    """k tokens drawn independently (repeats allowed) from softmax(d/T), one
+    Gumbel-max draw each: the sibling draws of the with-replacement rule
+    (SpecInfer's MSS, survey page Taxonomy rule (b)). T == 0 requests are
+    verified by greedy exact match, which needs distinct siblings: the k
+    largest draft logits, as for the without-replacement draws."""
+    if k <= 0:
+        return np.zeros(0, dtype=np.int32)
+    d = draft_row.astype(np.float64)
+    if temperature <= 0:
+        return gumbel_topk_tokens(rng, draft_row, k, 0.0)
+    g = rng.gumbel(size=(k, d.shape[0]))
+    return np.argmax(d[None, :] / float(temperature) + g, axis=1).astype(np.int32)
+
+
 def make_sampler_inputs(rng_logits, rng_draws, rng_uniforms, trees, vocab,
                         temperatures, mode="correlated", sigma=2.0,
-                        noise=0.5, need_draft=None):
+                        noise=0.5, need_draft=None, draws="without"):
     """Per-node target/draft logits (row i = distribution of the token after
     node i), sibling tokens drawn from the parent's draft row, and uniforms.
 
     mode "correlated": t ~ N(0, sigma), d = t + N(0, noise).
     mode "independent": t, d i.i.d. N(0, sigma).
+    draws "without": distinct siblings (Gumbel-top-k); "with": independent
+    draws, repeats allowed.
     """
     B = len(trees)
     node_counts = [len(t) for t in trees]
@@ -216,7 +233,8 @@ def make_sampler_inputs(rng_logits, rng_draws, rng_uniforms, trees, vocab,
             children[p[i]].append(i)
         for v in range(n):
             if children[v]:
-                toks = gumbel_topk_tokens(rng_draws, d[a + v], len(children[v]), float(temps[r]))
+                draw = gumbel_topk_tokens if draws == "without" else independent_draw_tokens
+                toks = draw(rng_draws, d[a + v], len(children[v]), float(temps[r]))
                 for c, x in zip(children[v], toks):
                     tokens[a + c] = x
     uniforms = rng_uniforms.random((T, 2), dtype=np.float32)
