@@ -2,7 +2,7 @@
 
 One step = one pass of the whole hot path over one batch:
   tree_verify_attn (one attention layer, every tree row of every request)
-  -> tree_spec_sample (greedy / without-replacement rejection walk)
+  -> tree_spec_sample (greedy / rejection walk without or with replacement)
   -> tree_accept_path (longest accepted path, emitted tokens, KV keep-list).
 Workload (default): "highload" — 64 requests, prefixes U{512..8192}, per-request
 budget from {8-row chain, 16-row tree, 32-row tree}, 32 q / 8 kv heads, D 128,
@@ -84,7 +84,7 @@ def read_traffic():
     return float(m_b.group(1))
 
 
-def cpu_baseline(cfg, budget_s=12.0):
+def cpu_baseline(cfg, budget_s=12.0, replacement=False):
     """The oracle as it stands on the first requests of the same workload,
     until ~budget_s of CPU time; returns nodes/s and what was sampled."""
     import oracle
@@ -107,7 +107,7 @@ def cpu_baseline(cfg, budget_s=12.0):
                             tokens=s.tokens[a:b], node_indptr=np.array([0, b - a], np.int32),
                             parent=s.parent[a:b], temperature=s.temperature[r:r + 1],
                             uniforms=s.uniforms[a:b])
-        f, nt, _ = oracle.tree_spec_sample(one)
+        f, nt, _ = oracle.tree_spec_sample(one, replacement=replacement)
         oracle.tree_accept_path(one.node_indptr, one.parent, one.tokens, f, nt,
                                 [int(inp.prefix_len[r])], 16)
         nodes += n
@@ -372,6 +372,9 @@ def main():
                     help="comma-separated workloads: time tree_verify_attn alone on each, "
                          "rotating >= --rotate-bytes of distinct copies (one JSON line each)")
     ap.add_argument("--rotate-bytes", type=int, default=1 << 30)
+    ap.add_argument("--replacement", action="store_true",
+                    help="siblings drawn independently (with replacement) and verified by "
+                         "the with-replacement rule")
     ap.add_argument("--siblings-bench", action="store_true",
                     help="time tree_draw_siblings alone on the highload trees' expansions")
     ap.add_argument("--commit-bench", type=int, default=0, metavar="LAYERS",
@@ -413,7 +416,8 @@ def main():
     from workloads.device import attention_tensors, sampler_tensors
 
     temp = args.temperature if args.temperature == "mixed" else float(args.temperature)
-    cfg = make_config(args.config, temperature=temp)
+    cfg = make_config(args.config, temperature=temp,
+                      draws="with" if args.replacement else "without")
     inp, s = cfg.attn, cfg.sampler
     dev = "cuda"
     torch.cuda.set_device(0)
@@ -426,7 +430,7 @@ def main():
     if have_sampler:
         st = sampler_tensors(s, dev)
         md = max(8, inp.max_depth)
-        sdesc = tv.sample_desc(s.batch, s.vocab, s.max_nodes, md)
+        sdesc = tv.sample_desc(s.batch, s.vocab, s.max_nodes, md, replacement=args.replacement)
         sws = tv.alloc_workspace(tv.sample_workspace_size(sdesc), dev)
         T = int(s.node_indptr[-1])
         flag = torch.empty(T, dtype=torch.int8, device=dev)
@@ -499,7 +503,8 @@ def main():
                                f"prefix {int(inp.prefix_len.min())}-{int(inp.prefix_len.max())}, "
                                f"Hq {inp.num_q_heads}/Hkv {inp.num_kv_heads}/D {inp.head_dim} "
                                f"{inp.dtype} paged KV"
-                               + (f"; sampler V {s.vocab}, T {args.temperature}" if have_sampler else ""),
+                               + (f"; sampler V {s.vocab}, T {args.temperature}" if have_sampler else "")
+                               + ("; siblings with replacement, rule (b)" if args.replacement else ""),
                    "batch": inp.batch, "tree_rows": nodes, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
@@ -519,7 +524,7 @@ def main():
                           "achieved_GBs": sbytes / (samp_ms * 1e-3) / 1e9 if samp_ms > 0 else None,
                           "mean_emitted": float(out_len.mean()), "dtype": "f64"}
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
+        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget, args.replacement)
     print(json.dumps(res))
 
 
