@@ -26,6 +26,7 @@ from .path import accept_path_request, tree_accept_path
 from .commit import BadKeepList, check_keep, kv_commit_layer, kv_commit
 from .siblings import philox4x32_10, draw_children, tree_draw_siblings
 from .enumerate import enumerate_node_laws
+from . import construct
 
 __all__ = [
     "check_tree", "depths", "ancestors_or_self", "children", "ancestor_bitsets",
@@ -35,5 +36,5 @@ __all__ = [
     "tree_spec_sample", "accept_path_request", "tree_accept_path",
     "BadKeepList", "check_keep", "kv_commit_layer", "kv_commit",
     "philox4x32_10", "draw_children", "tree_draw_siblings",
-    "enumerate_node_laws",
+    "enumerate_node_laws", "construct",
 ]
