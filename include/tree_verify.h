@@ -282,6 +282,54 @@ tv_status tree_draw_siblings(int32_t rows, int32_t vocab, const float* draft_log
                              uint64_t seed, int32_t* tokens, void* status_workspace,
                              hipStream_t stream);
 
+/* Draft-tree construction by expansion and rerank ([survey] Timeline:
+ * EAGLE-2 expands the top-k nodes by path-product value and reranks to keep
+ * the top-m; [survey] Taxonomy: the value is the cumulative draft probability
+ * along the root path). Values are logs: value(node) = sum over its root
+ * path of log softmax(draft row of the edge's parent)[token].
+ *
+ * Candidates are kept per request in caller-owned arrays of cand_capacity
+ * entries, numbered in generation order. One expansion round:
+ * tree_expand_step takes the k_in frontier nodes of every request (their
+ * candidate ids; NULL frontier = every slot is the root, value 0) and their
+ * draft logit rows, gives each node its k children = the k largest logits,
+ * descending, lower token id first on ties, stores child (slot s, rank j) at
+ * id cand_offset + s*k + j with value = value(frontier) + log q(token), and
+ * writes the k best of the round's k_in*k new ids (value descending, lower
+ * id on ties) to next_frontier, best first.
+ *   draft_logits [batch][k_in][vocab] fp32 (the drafter's rows for the
+ *     frontier slots, in slot order); frontier [batch][k_in] int32 or NULL;
+ *   cand_value [batch][cand_capacity] fp32, cand_token and cand_parent
+ *     [batch][cand_capacity] int32 (parent = candidate id, -1 = root): read
+ *     below cand_offset, written at cand_offset .. cand_offset + k_in*k - 1;
+ *   next_frontier [batch][k] int32 output.
+ * 1 <= k, k_in <= 16, vocab >= k, cand_offset + k_in*k <= cand_capacity,
+ * else TV_ERR_SHAPE. A frontier id outside [-1, cand_offset) sets
+ * TV_DEV_TREE (the slot is expanded as the root); non-finite logits set
+ * TV_DEV_LOGITS (status_workspace, if not NULL). The log-sum-exp is formed
+ * in fp32 and combined in fp64, so values agree with an fp64 evaluation to
+ * ~1e-6; selections can differ only where two values lie that close. */
+tv_status tree_expand_step(int32_t batch, int32_t vocab, int32_t k_in, int32_t k,
+                           const float* draft_logits, const int32_t* frontier,
+                           int32_t cand_capacity, int32_t cand_offset, float* cand_value,
+                           int32_t* cand_token, int32_t* cand_parent, int32_t* next_frontier,
+                           void* status_workspace, hipStream_t stream);
+
+/* Rerank: keep the m best of candidates 0 .. num_cand-1 of every request
+ * (value descending, lower id on ties; a child's value never exceeds its
+ * parent's and its id is larger, so the kept set is closed under ancestors)
+ * and emit the tree: out_parent / out_token [batch][m+1] int32 hold the root
+ * (parent -1, token -1: the caller's last accepted token) at 0, then the
+ * kept candidates in ascending id (topological order, siblings in draw
+ * order) with request-local parents; -1 past out_count[b] = 1 + kept.
+ * 1 <= num_cand <= min(cand_capacity, 4096), m >= 1, else TV_ERR_SHAPE. A kept
+ * candidate whose parent is not kept (values not from tree_expand_step) sets
+ * TV_DEV_TREE and is attached to the root. */
+tv_status tree_rerank(int32_t batch, int32_t num_cand, int32_t cand_capacity, int32_t m,
+                      const float* cand_value, const int32_t* cand_token,
+                      const int32_t* cand_parent, int32_t* out_parent, int32_t* out_token,
+                      int32_t* out_count, void* status_workspace, hipStream_t stream);
+
 /* Tree metadata ([TreeSpark] §3.2 step 3 and §4: per-depth position ids and
  * ancestor bitmasks). For every row: depth (edges from the root),
  * anc_bits [T][ceil(max_nodes/32)] (bit j of word j/32 set iff j is an

@@ -110,23 +110,31 @@ def eagle2_tree(root_row, round_rows, k, m):
 
 
 def near_ties(cands, frontiers, k, m, eps):
-    """True when a frontier choice or the rerank cut lies within eps (a
-    decision that fp32 arithmetic may take the other way)."""
+    """True when a decision lies within eps of going the other way: the order
+    of a round's k best values (the frontier's slot order decides which draft
+    row each slot reads next) and its cut, or the rerank cut. Exact ties
+    (siblings with equal logits: identical arithmetic on any side) are
+    broken by id and do not count."""
     v = np.asarray(cands.value)
 
-    def cut_gap(vals, n):
-        if len(vals) <= n:
-            return np.inf
+    def close(vals, n, whole_order):
         s = np.sort(np.asarray(vals))[::-1]
-        return s[n - 1] - s[n]
+        if len(s) <= 1:
+            return False
+        if whole_order:
+            gaps = s[:min(n + 1, len(s)) - 1] - s[1:min(n + 1, len(s))]
+        else:
+            if len(s) <= n:
+                return False
+            gaps = np.array([s[n - 1] - s[n]])
+        return bool(((gaps > 0) & (gaps < eps)).any())
 
     # round r created ids [start_r, start_r + count_r)
     start, count = 0, k
-    gaps = [cut_gap(v[start:start + count], k)]
+    hit = close(v[start:start + count], k, True)
     start += count
     for _ in frontiers[1:]:
         count = k * k
-        gaps.append(cut_gap(v[start:start + count], k))
+        hit |= close(v[start:start + count], k, True)
         start += count
-    gaps.append(cut_gap(v, m))
-    return min(gaps) < eps
+    return hit or close(v, m, False)

@@ -57,3 +57,41 @@ def run_sampler(inp, max_depth=None, prefix_lens=None, ws=None, replacement=Fals
                 path_nodes=pn.cpu().numpy().reshape(B, W), out_tokens=ot.cpu().numpy().reshape(B, W),
                 out_len=ol.cpu().numpy(), kv_keep=kk.cpu().numpy().reshape(B, W),
                 status=st, bits=bits, max_depth=md)
+
+
+def run_construct(root, rows, k, m, num_rounds=None, bad_frontier=None):
+    """EAGLE-2 construction on the GPU: rounds of tree_expand_step, then
+    tree_rerank. root [B][V], rows [B][R-1][k][V] (numpy fp32)."""
+    import torch
+    import tree_verification_verify_amd as tv
+    B, V = root.shape
+    R = rows.shape[1] + 1 if num_rounds is None else num_rounds
+    cap = k + (R - 1) * k * k
+    ws = tv.alloc_workspace(256)
+    cv = torch.full((B, cap), float("nan"), dtype=torch.float32, device="cuda")
+    ct = torch.full((B, cap), -7, dtype=torch.int32, device="cuda")
+    cp = torch.full((B, cap), -7, dtype=torch.int32, device="cuda")
+    frontiers = []
+    nxt = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
+    tv.tree_expand_step(torch.from_numpy(root).cuda().view(B, 1, V), None, 0, cv, ct, cp, nxt, ws)
+    frontiers.append(nxt)
+    off = k
+    for d in range(R - 1):
+        fr = frontiers[-1]
+        if bad_frontier is not None and d == 0:
+            fr = fr.clone()
+            fr[0, 0] = bad_frontier
+        nxt = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
+        tv.tree_expand_step(torch.from_numpy(np.ascontiguousarray(rows[:, d])).cuda(), fr, off,
+                            cv, ct, cp, nxt, ws)
+        frontiers.append(nxt)
+        off += k * k
+    op = torch.full((B, m + 1), -7, dtype=torch.int32, device="cuda")
+    ot = torch.full_like(op, -7)
+    oc = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    tv.tree_rerank(off, m, cv, ct, cp, op, ot, oc, ws)
+    st, bits = tv.device_status(ws)
+    return dict(value=cv.cpu().numpy(), token=ct.cpu().numpy(), parent=cp.cpu().numpy(),
+                frontiers=[f.cpu().numpy() for f in frontiers], out_parent=op.cpu().numpy(),
+                out_token=ot.cpu().numpy(), out_count=oc.cpu().numpy(), status=st, bits=bits,
+                num_cand=off)

@@ -1,0 +1,91 @@
+"""GPU parity: tree_expand_step + tree_rerank (EAGLE-2 construction, HIP,
+via the C ABI) against the fp64 oracle. Tokens, parents, frontiers and the
+final tree are compared exactly; values within 1e-5. A request whose oracle
+has a frontier or rerank cut within EPS (a choice fp32 may take either way)
+is excluded and counted."""
+import numpy as np
+import pytest
+
+import oracle.construct as C
+from workloads import make_construct_inputs
+
+pytestmark = pytest.mark.gpu
+
+EPS = 1e-4
+
+
+def _run(*a, **kw):
+    from gpu_run import run_construct
+    return run_construct(*a, **kw)
+
+
+def _compare(root, rows, k, m, got, requests=None, allow_near=0):
+    assert got["status"] == 0, (got["status"], got["bits"])
+    B = root.shape[0]
+    R = rows.shape[1] + 1
+    near = 0
+    for b in (range(B) if requests is None else requests):
+        parent, token, cands, frontiers = C.eagle2_tree(root[b], list(rows[b]), k, m)
+        if C.near_ties(cands, frontiers, k, m, EPS):
+            near += 1
+            continue
+        n = len(cands.value)
+        assert got["num_cand"] == n
+        np.testing.assert_array_equal(got["token"][b, :n], cands.token, err_msg=f"request {b}")
+        np.testing.assert_array_equal(got["parent"][b, :n], cands.parent, err_msg=f"request {b}")
+        np.testing.assert_allclose(got["value"][b, :n], cands.value, rtol=0, atol=1e-5)
+        for d in range(R):
+            np.testing.assert_array_equal(got["frontiers"][d][b], frontiers[d], err_msg=f"{b} {d}")
+        cnt = len(parent)
+        assert got["out_count"][b] == cnt
+        np.testing.assert_array_equal(got["out_parent"][b, :cnt], parent)
+        np.testing.assert_array_equal(got["out_token"][b, :cnt], token)
+        assert (got["out_parent"][b, cnt:] == -1).all() and (got["out_token"][b, cnt:] == -1).all()
+    assert near <= allow_near, near
+    return near
+
+
+@pytest.mark.parametrize("V,k,R,m", [(7, 3, 3, 8), (64, 4, 4, 20), (1000, 10, 6, 60),
+                                     (4099, 16, 3, 100), (4096, 1, 5, 10), (300, 8, 2, 1000),
+                                     (50, 2, 6, 1)])
+def test_random_shapes(V, k, R, m):
+    """Scalar (V % 4 != 0) and vector rows, k from 1 to 16, m below, at and
+    above the candidate count."""
+    rng = np.random.default_rng(V + 7 * k + R)
+    root, rows = make_construct_inputs(rng, 6, V, k, R)
+    _compare(root, rows, k, m, _run(root, rows, k, m), allow_near=1)
+
+
+def test_integer_logits_with_ties():
+    """Integer logits: many exact ties inside rows (lower token id first) and
+    between sibling values (lower candidate id first)."""
+    rng = np.random.default_rng(3)
+    root, rows = make_construct_inputs(rng, 8, 257, 6, 4, integer_levels=5)
+    _compare(root, rows, 6, 40, _run(root, rows, 6, 40), allow_near=8)
+
+
+def test_eagle2_shape_full_vocab():
+    """The EAGLE-2 shape (top-k 10, depth 6, 60 kept nodes) over V = 151936 for
+    a 64-request batch; the oracle checks 10 sampled requests one by one (at
+    most 3 of them excluded for near ties; 4 of the 64 have one) and every
+    request's tree is checked for shape."""
+    rng = np.random.default_rng(2024)
+    B, V, k, R, m = 64, 151936, 10, 6, 60
+    root, rows = make_construct_inputs(rng, B, V, k, R)
+    got = _run(root, rows, k, m)
+    _compare(root, rows, k, m, got, requests=[0, 5, 9, 17, 21, 30, 38, 44, 50, 63], allow_near=3)
+    for b in range(B):
+        par = got["out_parent"][b]
+        assert got["out_count"][b] == m + 1 and par[0] == -1
+        assert all(0 <= par[i] < i for i in range(1, m + 1))
+        assert ((got["out_token"][b, 1:] >= 0) & (got["out_token"][b, 1:] < V)).all()
+
+
+def test_bad_frontier_and_nonfinite_logits_are_reported():
+    rng = np.random.default_rng(4)
+    root, rows = make_construct_inputs(rng, 3, 128, 4, 3)
+    got = _run(root, rows, 4, 10, bad_frontier=999)
+    assert got["status"] != 0 and got["bits"] & 1      # TV_DEV_TREE
+    root[1, 5] = np.nan
+    got = _run(root, rows, 4, 10)
+    assert got["bits"] & 4                             # TV_DEV_LOGITS

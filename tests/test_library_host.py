@@ -184,3 +184,29 @@ def test_draw_siblings_host_errors():
         a = list(args)
         a[i] = None
         assert lib.tree_draw_siblings(*a) == NULL
+
+
+def test_construct_host_errors():
+    lib = tv.library()
+    P = FAKE
+    exp = lambda B, V, kin, k, logits, cap, off, *outs: lib.tree_expand_step(
+        B, V, kin, k, logits, None, cap, off, *outs, None, None)
+    outs = [P, P, P, P]
+    for bad in ((0, 100, 1, 4, 40, 0), (2, 3, 1, 4, 40, 0), (2, 100, 1, 17, 40, 0),
+                (2, 100, 17, 4, 400, 0), (2, 100, 2, 4, 40, 33), (2, 100, 1, 0, 40, 0),
+                (2, 100, 1, 4, 40, -1)):
+        B, V, kin, k, cap, off = bad
+        assert exp(B, V, kin, k, P, cap, off, *outs) == SHAPE, bad
+    assert exp(2, 100, 1, 4, None, 40, 0, *outs) == NULL
+    for i in range(4):
+        o = list(outs)
+        o[i] = None
+        assert exp(2, 100, 1, 4, P, 40, 0, *o) == NULL, i
+    rr = lambda B, n, cap, m, *ptrs: lib.tree_rerank(B, n, cap, m, *ptrs, None, None)
+    ptrs = [P] * 6
+    for bad in ((0, 10, 10, 5), (2, 0, 10, 5), (2, 11, 10, 5), (2, 5000, 5000, 5), (2, 10, 10, 0)):
+        assert rr(*bad, *ptrs) == SHAPE, bad
+    for i in range(6):
+        p = list(ptrs)
+        p[i] = None
+        assert rr(2, 10, 10, 5, *p) == NULL, i

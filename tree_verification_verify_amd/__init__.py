@@ -25,7 +25,7 @@ __all__ = [
     "TV_RULE_WITH_REPLACEMENT", "attn_desc",
     "sample_desc", "attn_workspace_size", "sample_workspace_size", "alloc_workspace",
     "workspace_init", "device_status", "tree_verify_attn", "tree_spec_sample",
-    "tree_accept_path", "tree_kv_commit", "tree_draw_siblings", "tv_tree_meta", "validate_tree", "validate_pages",
+    "tree_accept_path", "tree_kv_commit", "tree_draw_siblings", "tree_expand_step", "tree_rerank", "tv_tree_meta", "validate_tree", "validate_pages",
     "library",
 ]
 
@@ -240,6 +240,55 @@ def tree_draw_siblings(draft_logits, counts, temperature, tokens, stream_id=0, s
         rows, V, _ptr(draft_logits), _ptr(counts), _ptr(temperature), int(stream_id) & 0xFFFFFFFF,
         int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(tokens), _ptr(status_workspace), _stream(stream)),
         "tree_draw_siblings")
+
+
+def tree_expand_step(draft_logits, frontier, cand_offset, cand_value, cand_token, cand_parent,
+                     next_frontier, status_workspace=None, stream=None):
+    """One expansion round. draft_logits [B][k_in][V] fp32; frontier [B][k_in]
+    int32 candidate ids or None (every slot is the root); cand_* [B][C];
+    next_frontier [B][k] int32 (k = children per node = its second size)."""
+    import torch
+    _need(draft_logits, "draft_logits", torch.float32)
+    _need(cand_value, "cand_value", torch.float32)
+    for t, n in ((cand_token, "cand_token"), (cand_parent, "cand_parent"),
+                 (next_frontier, "next_frontier")):
+        _need(t, n, torch.int32)
+    if draft_logits.dim() != 3 or cand_value.dim() != 2 or next_frontier.dim() != 2:
+        raise ValueError("draft_logits [B][k_in][V], cand_value [B][C], next_frontier [B][k]")
+    B, k_in, V = draft_logits.shape
+    k = next_frontier.shape[1]
+    C = cand_value.shape[1]
+    if frontier is not None:
+        _need(frontier, "frontier", torch.int32)
+        if tuple(frontier.shape) != (B, k_in):
+            raise ValueError("frontier must be [B][k_in]")
+    if cand_value.shape[0] != B or next_frontier.shape[0] != B or \
+            tuple(cand_token.shape) != (B, C) or tuple(cand_parent.shape) != (B, C):
+        raise ValueError("candidate arrays must be [B][C]")
+    _check(_lib.load().tree_expand_step(
+        B, V, k_in, k, _ptr(draft_logits), _ptr(frontier), C, int(cand_offset), _ptr(cand_value),
+        _ptr(cand_token), _ptr(cand_parent), _ptr(next_frontier), _ptr(status_workspace),
+        _stream(stream)), "tree_expand_step")
+
+
+def tree_rerank(num_cand, m, cand_value, cand_token, cand_parent, out_parent, out_token,
+                out_count, status_workspace=None, stream=None):
+    """Keep the m best of the first num_cand candidates per request; out_parent /
+    out_token [B][m+1] int32, out_count [B] int32 (outputs)."""
+    import torch
+    _need(cand_value, "cand_value", torch.float32)
+    for t, n in ((cand_token, "cand_token"), (cand_parent, "cand_parent"),
+                 (out_parent, "out_parent"), (out_token, "out_token"), (out_count, "out_count")):
+        _need(t, n, torch.int32)
+    B, C = cand_value.shape
+    if tuple(out_parent.shape) != (B, m + 1) or tuple(out_token.shape) != (B, m + 1) or \
+            out_count.numel() != B or tuple(cand_token.shape) != (B, C) or \
+            tuple(cand_parent.shape) != (B, C):
+        raise ValueError("out_parent / out_token must be [B][m+1], out_count [B]")
+    _check(_lib.load().tree_rerank(
+        B, int(num_cand), C, int(m), _ptr(cand_value), _ptr(cand_token), _ptr(cand_parent),
+        _ptr(out_parent), _ptr(out_token), _ptr(out_count), _ptr(status_workspace),
+        _stream(stream)), "tree_rerank")
 
 
 def tv_tree_meta(batch, max_nodes, node_indptr, parent, depth=None, anc_bits=None,

@@ -181,6 +181,42 @@ tv_status tree_draw_siblings(int32_t rows, int32_t vocab, const float* draft_log
   return TV_OK;
 }
 
+tv_status tree_expand_step(int32_t batch, int32_t vocab, int32_t k_in, int32_t k,
+                           const float* draft_logits, const int32_t* frontier,
+                           int32_t cand_capacity, int32_t cand_offset, float* cand_value,
+                           int32_t* cand_token, int32_t* cand_parent, int32_t* next_frontier,
+                           void* status_workspace, hipStream_t stream) {
+  if (batch < 1 || k < 1 || k > tv::kMaxExpand || k_in < 1 || k_in > tv::kMaxExpand ||
+      vocab < k || cand_offset < 0 || cand_capacity < 1 ||
+      long(cand_offset) + long(k_in) * k > long(cand_capacity) ||
+      long(batch) * k_in > 0x7fffffffL)
+    return TV_ERR_SHAPE;
+  if (!draft_logits || !cand_value || !cand_token || !cand_parent || !next_frontier)
+    return TV_ERR_NULL;
+  hipError_t e = tv::launch_expand_step(batch, vocab, k_in, k, draft_logits, frontier,
+                                        cand_capacity, cand_offset, cand_value, cand_token,
+                                        cand_parent, next_frontier,
+                                        static_cast<uint32_t*>(status_workspace), stream);
+  if (e != hipSuccess) return hip_fail(e, "tree_expand_step");
+  return TV_OK;
+}
+
+tv_status tree_rerank(int32_t batch, int32_t num_cand, int32_t cand_capacity, int32_t m,
+                      const float* cand_value, const int32_t* cand_token,
+                      const int32_t* cand_parent, int32_t* out_parent, int32_t* out_token,
+                      int32_t* out_count, void* status_workspace, hipStream_t stream) {
+  if (batch < 1 || num_cand < 1 || num_cand > cand_capacity || num_cand > tv::kMaxRerank ||
+      m < 1 || m >= 0x7fffffff)
+    return TV_ERR_SHAPE;
+  if (!cand_value || !cand_token || !cand_parent || !out_parent || !out_token || !out_count)
+    return TV_ERR_NULL;
+  hipError_t e = tv::launch_rerank(batch, num_cand, cand_capacity, m, cand_value, cand_token,
+                                   cand_parent, out_parent, out_token, out_count,
+                                   static_cast<uint32_t*>(status_workspace), stream);
+  if (e != hipSuccess) return hip_fail(e, "tree_rerank");
+  return TV_OK;
+}
+
 tv_status tv_tree_meta(int32_t batch, int32_t max_nodes, const int32_t* node_indptr,
                        const int32_t* parent, int32_t* depth, uint32_t* anc_bits,
                        int32_t* first_child, int32_t* next_sibling, void* status_workspace,

@@ -1,0 +1,334 @@
+// Dynamic draft-tree construction by expansion and rerank (EAGLE-2).
+//
+// Survey page, Timeline: EAGLE-2 grows the draft tree by expanding the top-k
+// nodes by path-product value and reranking to keep the top-m nodes; the
+// value is the cumulative draft probability along the root path (survey
+// page, Taxonomy, construction policy axis). Values here are logs: a node's
+// value is the sum of log q along its root path, q = softmax(draft row).
+//
+// One expansion round (tree_expand_step) = expand_kernel + select_kernel:
+//  * expand_kernel: one workgroup per frontier row. One pass over the row's
+//    logits keeps, per thread, its K best logits (ascending-index scan, so a
+//    tie keeps the lower id ahead) and an online log-sum-exp (fp32 running
+//    max and sum, combined across the block in fp64). k rounds of a block
+//    argmax over the threads' list heads then give the row's top-k in
+//    descending logit, lowest id first on ties; child value = frontier value
+//    + (logit - lse). Children are stored at candidate ids cand_offset +
+//    slot * k + rank (generation order).
+//  * select_kernel: one workgroup per request ranks the round's k_in * k new
+//    candidates (value descending, id ascending) and writes the k best ids,
+//    best first: the next frontier.
+// tree_rerank = rerank_kernel: one workgroup per request ranks all
+// candidates, keeps ranks < m, and places the kept ones in ascending id
+// (prefix count of kept flags): root at 0, then the tree in topological
+// order with request-local parents.
+//
+// The row pass is bound by HBM (4 bytes per logit); the selections touch a
+// few KB per request.
+#include <math.h>
+
+#include "tv_device.hpp"
+#include "tv_internal.hpp"
+
+namespace tv {
+
+namespace {
+
+constexpr int kConThreads = 256;
+constexpr int kConWaves = kConThreads / kWave;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// (value, id) order of every selection: larger value first, lower id on ties.
+// Values pass through key() first: NaN (from non-finite logits, already
+// reported) orders as -inf, so the order stays total and ranks unique.
+__device__ inline float key(float v) { return v != v ? -INFINITY : v; }
+__device__ inline bool better(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+struct ExpandParams {
+  const float* logits;      // [batch][k_in][V]
+  const int32_t* frontier;  // [batch][k_in] candidate ids, -1 = root; NULL: every slot is the root
+  float* value;             // [batch][cap]
+  int32_t* token;           // [batch][cap]
+  int32_t* parent;          // [batch][cap]
+  uint32_t* status;
+  int V, k_in, k, cap, offset;
+};
+
+// Per-thread list of the K best (value, id) seen, best first.
+template <int K>
+struct TopList {
+  float v[K];
+  int i[K];
+  __device__ void init() {
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      v[j] = -INFINITY;
+      i[j] = 0x7fffffff;
+    }
+  }
+  // Elements arrive in ascending id, so strict comparisons keep a tie's
+  // earlier (lower) id ahead.
+  __device__ void insert(float x, int id) {
+    if (!(x > v[K - 1])) return;
+#pragma unroll
+    for (int j = K - 1; j > 0; --j) {
+      const bool up = x > v[j - 1];
+      const bool here = !up && x > v[j];
+      v[j] = up ? v[j - 1] : (here ? x : v[j]);
+      i[j] = up ? i[j - 1] : (here ? id : i[j]);
+    }
+    if (x > v[0]) {
+      v[0] = x;
+      i[0] = id;
+    }
+  }
+  __device__ void pop() {
+#pragma unroll
+    for (int j = 0; j + 1 < K; ++j) {
+      v[j] = v[j + 1];
+      i[j] = i[j + 1];
+    }
+    v[K - 1] = -INFINITY;
+    i[K - 1] = 0x7fffffff;
+  }
+};
+
+template <int K>
+__global__ __launch_bounds__(kConThreads) void expand_kernel(ExpandParams p) {
+  __shared__ float s_v[kConWaves];
+  __shared__ int s_i[kConWaves];
+  __shared__ float s_m[kConWaves];
+  __shared__ double s_s[kConWaves];
+  const int row = blockIdx.x;  // request * k_in + slot
+  const int b = row / p.k_in, slot = row - b * p.k_in;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const float* x = p.logits + size_t(row) * p.V;
+
+  TopList<K> L;
+  L.init();
+  float m = -INFINITY, s = 0.f;
+  bool bad = false;
+  auto take = [&](float a, int id) __attribute__((always_inline)) {
+    bad |= !(a - a == 0.f);  // NaN or +-Inf
+    L.insert(a, id);
+  };
+  const bool vec = (p.V & 3) == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+  if (vec) {
+    const float4* x4 = reinterpret_cast<const float4*>(x);
+    const int n4 = p.V >> 2;
+    for (int e = tid; e < n4; e += kConThreads) {
+      const float4 a = x4[e];
+      const float mx = fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w));
+      if (mx > m) {
+        s *= exp2f((m - mx) * kLog2e);
+        m = mx;
+      }
+      s += exp2f((a.x - m) * kLog2e) + exp2f((a.y - m) * kLog2e) + exp2f((a.z - m) * kLog2e) +
+           exp2f((a.w - m) * kLog2e);
+      take(a.x, 4 * e);
+      take(a.y, 4 * e + 1);
+      take(a.z, 4 * e + 2);
+      take(a.w, 4 * e + 3);
+    }
+  } else {
+    for (int e = tid; e < p.V; e += kConThreads) {
+      const float a = x[e];
+      if (a > m) {
+        s *= exp2f((m - a) * kLog2e);
+        m = a;
+      }
+      s += exp2f((a - m) * kLog2e);
+      take(a, e);
+    }
+  }
+  if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) raise_status(p.status, TV_DEV_LOGITS);
+
+  // Block log-sum-exp: max in fp32, the rescaled sums in fp64.
+  float mw = m;
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) mw = fmaxf(mw, shfl_xor(mw, o));
+  if (lane == 0) s_m[wave] = mw;
+  __syncthreads();
+  float M = s_m[0];
+#pragma unroll
+  for (int w = 1; w < kConWaves; ++w) M = fmaxf(M, s_m[w]);
+  double sd = m == -INFINITY ? 0.0 : double(s) * exp(double(m) - double(M));
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) sd += shfl_xor_d(sd, o);
+  if (lane == 0) s_s[wave] = sd;
+  __syncthreads();
+  double S = 0.0;
+#pragma unroll
+  for (int w = 0; w < kConWaves; ++w) S += s_s[w];
+  const double lse = double(M) + log(S);
+
+  // Frontier value (root: 0); a frontier id outside the earlier candidates
+  // is reported and taken as the root.
+  int f = p.frontier ? p.frontier[size_t(b) * p.k_in + slot] : -1;
+  if (f < -1 || f >= p.offset) {
+    if (tid == 0) raise_status(p.status, TV_DEV_TREE);
+    f = -1;
+  }
+  const size_t cb = size_t(b) * p.cap;
+  const double base = f < 0 ? 0.0 : double(p.value[cb + f]);
+
+  // k rounds of block argmax over the list heads.
+  for (int r = 0; r < p.k; ++r) {
+    float bv = L.v[0];
+    int bi = L.i[0];
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+      const float ov = shfl_xor(bv, o);
+      const int oi = shfl_xor(bi, o);
+      if (better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (lane == 0) {
+      s_v[wave] = bv;
+      s_i[wave] = bi;
+    }
+    __syncthreads();
+    float wv = s_v[0];
+    int wi = s_i[0];
+#pragma unroll
+    for (int w = 1; w < kConWaves; ++w)
+      if (better(s_v[w], s_i[w], wv, wi)) {
+        wv = s_v[w];
+        wi = s_i[w];
+      }
+    __syncthreads();  // every thread has read this round's winners
+    if (L.i[0] == wi) L.pop();  // ids are unique across threads
+    if (tid == 0) {
+      const size_t c = cb + size_t(p.offset) + size_t(slot) * p.k + r;
+      const bool ok = wi < p.V;
+      p.token[c] = ok ? wi : -1;
+      p.value[c] = ok ? float(base + (double(wv) - lse)) : -INFINITY;
+      p.parent[c] = f;
+    }
+  }
+}
+
+struct SelectParams {
+  const float* value;     // [batch][cap]
+  int32_t* next;          // [batch][k]
+  int cap, offset, n, k;  // candidates offset .. offset + n - 1
+};
+
+__global__ __launch_bounds__(kConThreads) void select_kernel(SelectParams p) {
+  __shared__ float s_v[kConThreads];
+  const int b = blockIdx.x, t = threadIdx.x;
+  const float* v = p.value + size_t(b) * p.cap + p.offset;
+  const float mine = t < p.n ? key(v[t]) : -INFINITY;
+  s_v[t] = mine;
+  __syncthreads();
+  if (t < p.n) {
+    int rank = 0;
+    for (int j = 0; j < p.n; ++j) rank += better(s_v[j], j, mine, t);
+    if (rank < p.k) p.next[size_t(b) * p.k + rank] = p.offset + t;
+  }
+}
+
+struct RerankParams {
+  const float* value;     // [batch][cap]
+  const int32_t* token;   // [batch][cap]
+  const int32_t* parent;  // [batch][cap]
+  int32_t* out_parent;    // [batch][m + 1]
+  int32_t* out_token;     // [batch][m + 1]
+  int32_t* out_count;     // [batch]
+  uint32_t* status;
+  int cap, n, m;
+};
+
+__global__ __launch_bounds__(kConThreads) void rerank_kernel(RerankParams p) {
+  __shared__ float s_v[kMaxRerank];
+  __shared__ int s_pos[kMaxRerank];
+  __shared__ int s_cnt[kConThreads];
+  const int b = blockIdx.x, t = threadIdx.x;
+  const size_t cb = size_t(b) * p.cap;
+  for (int i = t; i < p.n; i += kConThreads) s_v[i] = key(p.value[cb + i]);
+  __syncthreads();
+  // Thread t owns ids [t * per, t * per + per).
+  const int per = (p.n + kConThreads - 1) / kConThreads;
+  const int lo = min(p.n, t * per), hi = min(p.n, lo + per);
+  uint32_t kept = 0;  // bit j: id lo + j is kept (per <= 32)
+  for (int i = lo; i < hi; ++i) {
+    const float vi = s_v[i];
+    int rank = 0;
+    for (int j = 0; j < p.n; ++j) rank += better(s_v[j], j, vi, i);
+    if (rank < p.m) kept |= 1u << (i - lo);
+  }
+  s_cnt[t] = __builtin_popcount(kept);
+  __syncthreads();
+  // Exclusive prefix of the kept counts (thread order = id order).
+  int before = 0;
+  for (int w = 0; w < t; ++w) before += s_cnt[w];
+  int total = before;
+  for (int w = t; w < kConThreads; ++w) total += s_cnt[w];
+  int pos = 1 + before;
+  for (int i = lo; i < hi; ++i) s_pos[i] = (kept >> (i - lo)) & 1 ? pos++ : 0;
+  __syncthreads();
+  const int W = p.m + 1;
+  int32_t* op = p.out_parent + size_t(b) * W;
+  int32_t* ot = p.out_token + size_t(b) * W;
+  for (int i = lo; i < hi; ++i) {
+    const int q = s_pos[i];
+    if (!q || q > p.m) continue;  // ranks are unique, so at most m are kept
+    int par = p.parent[cb + i];
+    int pp;
+    if (par < 0) {
+      pp = 0;
+    } else if (par < i && s_pos[par] > 0) {
+      pp = s_pos[par];
+    } else {  // a kept node whose parent is not kept (or not earlier): not a tree
+      raise_status(p.status, TV_DEV_TREE);
+      pp = 0;
+    }
+    op[q] = pp;
+    ot[q] = p.token[cb + i];
+  }
+  for (int q = 1 + total + t; q < W; q += kConThreads) {
+    op[q] = -1;
+    ot[q] = -1;
+  }
+  if (t == 0) {
+    op[0] = -1;
+    ot[0] = -1;
+    p.out_count[b] = 1 + total;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_expand_step(int32_t batch, int32_t vocab, int32_t k_in, int32_t k,
+                              const float* logits, const int32_t* frontier, int32_t cap,
+                              int32_t offset, float* value, int32_t* token, int32_t* parent,
+                              int32_t* next, uint32_t* status, hipStream_t stream) {
+  ExpandParams e{logits, frontier, value, token, parent, status, vocab, k_in, k, cap, offset};
+  const dim3 grid(unsigned(batch) * unsigned(k_in));
+  if (k <= 4)
+    hipLaunchKernelGGL(expand_kernel<4>, grid, dim3(kConThreads), 0, stream, e);
+  else if (k <= 8)
+    hipLaunchKernelGGL(expand_kernel<8>, grid, dim3(kConThreads), 0, stream, e);
+  else
+    hipLaunchKernelGGL(expand_kernel<16>, grid, dim3(kConThreads), 0, stream, e);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  SelectParams s{value, next, cap, offset, k_in * k, k};
+  hipLaunchKernelGGL(select_kernel, dim3(unsigned(batch)), dim3(kConThreads), 0, stream, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_rerank(int32_t batch, int32_t num_cand, int32_t cap, int32_t m,
+                         const float* value, const int32_t* token, const int32_t* parent,
+                         int32_t* out_parent, int32_t* out_token, int32_t* out_count,
+                         uint32_t* status, hipStream_t stream) {
+  RerankParams r{value, token, parent, out_parent, out_token, out_count, status, cap, num_cand, m};
+  hipLaunchKernelGGL(rerank_kernel, dim3(unsigned(batch)), dim3(kConThreads), 0, stream, r);
+  return hipGetLastError();
+}
+
+}  // namespace tv

@@ -11,7 +11,7 @@ from .bf16 import f32_to_bf16_bits, bf16_bits_to_f32
 from .trees import (expansion_vector_tree, random_tree, chain_tree, star_tree,
                     eagle2_tree, bfs_renumber, relabel_random_topological,
                     relabel_dfs, tree_depths)
-from .inputs import (make_attention_inputs, make_sampler_inputs,
+from .inputs import (make_attention_inputs, make_sampler_inputs, make_construct_inputs,
                      gumbel_topk_tokens, independent_draw_tokens, AttentionInputs,
                      SamplerInputs)
 from .configs import CONFIGS, make_config, Config
@@ -20,7 +20,7 @@ __all__ = [
     "f32_to_bf16_bits", "bf16_bits_to_f32",
     "expansion_vector_tree", "random_tree", "chain_tree", "star_tree",
     "eagle2_tree", "bfs_renumber", "relabel_random_topological", "relabel_dfs",
-    "tree_depths", "make_attention_inputs", "make_sampler_inputs",
+    "tree_depths", "make_attention_inputs", "make_sampler_inputs", "make_construct_inputs",
     "gumbel_topk_tokens", "independent_draw_tokens", "AttentionInputs", "SamplerInputs",
     "CONFIGS", "make_config", "Config",
 ]

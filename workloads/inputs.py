@@ -244,3 +244,19 @@ def make_sampler_inputs(rng_logits, rng_draws, rng_uniforms, trees, vocab,
                          draft_logits=d if need_draft else None,
                          tokens=tokens, node_indptr=node_indptr, parent=parent,
                          temperature=temps, uniforms=uniforms)
+
+
+def make_construct_inputs(rng, batch, vocab, k, rounds, sigma=2.0, integer_levels=0):
+    """Draft logit rows for tree construction by expansion rounds: root
+    [B][V] and, for rounds 2..rounds, [B][rounds-1][k][V] (the drafter's rows
+    for the k frontier slots of each round). N(0, sigma) logits; with
+    integer_levels > 0, logits are integers in [0, integer_levels) (many
+    exact ties)."""
+    shape_rows = (batch, max(rounds - 1, 0), k, vocab)
+    if integer_levels:
+        root = rng.integers(0, integer_levels, size=(batch, vocab)).astype(np.float32)
+        rows = rng.integers(0, integer_levels, size=shape_rows).astype(np.float32)
+    else:
+        root = _normal_f32(rng, (batch, vocab), scale=sigma)
+        rows = _normal_f32(rng, shape_rows, scale=sigma)
+    return root, rows
