@@ -356,6 +356,80 @@ def siblings_bench(reps):
         "tokens_per_s": R * V / (us * 1e-6)}), flush=True)
 
 
+def construct_bench(reps, batch=64, vocab=151936, k=10, rounds=6, m=60):
+    """EAGLE-2 construction alone (top-k 10, depth 6, 60 kept nodes, the
+    survey's EAGLE-2 setting) for a 64-request batch over V = 151936: round 1
+    expands each root row, rounds 2..6 the 10 frontier rows of every request
+    (synthetic drafter rows resident in HBM), then the rerank. Algorithmic
+    bytes of a round: its draft rows read once (outputs are a few KB)."""
+    import ctypes
+    import torch
+    import tree_verification_verify_amd as tv
+    from tree_verification_verify_amd import _lib
+    from workloads import make_construct_inputs
+    rng = np.random.default_rng(2024)
+    root_np, rows_np = make_construct_inputs(rng, batch, vocab, k, rounds)
+    root = torch.from_numpy(root_np).to("cuda")
+    rows = [torch.from_numpy(np.ascontiguousarray(rows_np[:, d])).to("cuda")
+            for d in range(rounds - 1)]
+    del root_np, rows_np
+    cap = k + (rounds - 1) * k * k
+    cv = torch.empty((batch, cap), dtype=torch.float32, device="cuda")
+    ct = torch.empty((batch, cap), dtype=torch.int32, device="cuda")
+    cp = torch.empty_like(ct)
+    fr = [torch.empty((batch, k), dtype=torch.int32, device="cuda") for _ in range(rounds)]
+    op = torch.empty((batch, m + 1), dtype=torch.int32, device="cuda")
+    ot = torch.empty_like(op)
+    oc = torch.empty(batch, dtype=torch.int32, device="cuda")
+    ws = tv.alloc_workspace(256)
+    lib = _lib.load()
+    stream = torch.cuda.current_stream()
+    P_ = ctypes.c_void_p
+    ptr = lambda t: P_(t.data_ptr())
+    outs = (ptr(cv), ptr(ct), ptr(cp))
+    calls = [lambda: lib.tree_expand_step(batch, vocab, 1, k, ptr(root), None, cap, 0, *outs,
+                                          ptr(fr[0]), ptr(ws), P_(stream.cuda_stream))]
+    for d in range(rounds - 1):
+        calls.append(lambda d=d: lib.tree_expand_step(
+            batch, vocab, k, k, ptr(rows[d]), ptr(fr[d]), cap, k + d * k * k, *outs,
+            ptr(fr[d + 1]), ptr(ws), P_(stream.cuda_stream)))
+    calls.append(lambda: lib.tree_rerank(batch, cap, cap, m, *outs, ptr(op), ptr(ot), ptr(oc),
+                                         ptr(ws), P_(stream.cuda_stream)))
+    for c in calls:
+        assert c() == 0
+    torch.cuda.synchronize()
+    status, bits = tv.device_status(ws)
+    if status != 0:
+        raise SystemExit(f"device status {status} bits {bits}")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+          for _ in range(reps)]
+    for e in ev:
+        e[0].record(stream)
+        for j, c in enumerate(calls):
+            c()
+            e[j + 1].record(stream)
+    torch.cuda.synchronize()
+    per = np.median([[e[j].elapsed_time(e[j + 1]) * 1e3 for j in range(len(calls))] for e in ev],
+                    axis=0)
+    total = float(np.median([e[0].elapsed_time(e[-1]) * 1e3 for e in ev]))
+    row_bytes = vocab * 4
+    b_root, b_round = batch * row_bytes, batch * k * row_bytes
+    abytes = b_root + (rounds - 1) * b_round
+    rest = float(np.mean(per[1:rounds]))
+    print(json.dumps({
+        "kernel": "tree_expand_step x rounds + tree_rerank (expand_kernel<16>, select_kernel, "
+                  "rerank_kernel)",
+        "workload": f"EAGLE-2 construction: {batch} requests, top-k {k}, depth {rounds}, "
+                    f"keep {m}; V {vocab} fp32 synthetic draft rows",
+        "us_total_median": total, "reps": reps,
+        "us_round1": float(per[0]), "us_round_2_to_%d_mean" % rounds: rest,
+        "us_rerank": float(per[-1]), "algorithmic_bytes": abytes,
+        "hbm_GBs_total": abytes / (total * 1e-6) / 1e9,
+        "hbm_GBs_round": b_round / (rest * 1e-6) / 1e9,
+        "hbm_frac_round": b_round / (rest * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "trees_per_s": batch / (total * 1e-6)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -375,6 +449,8 @@ def main():
     ap.add_argument("--replacement", action="store_true",
                     help="siblings drawn independently (with replacement) and verified by "
                          "the with-replacement rule")
+    ap.add_argument("--construct-bench", action="store_true",
+                    help="time the EAGLE-2 construction (expansion rounds + rerank) alone")
     ap.add_argument("--siblings-bench", action="store_true",
                     help="time tree_draw_siblings alone on the highload trees' expansions")
     ap.add_argument("--commit-bench", type=int, default=0, metavar="LAYERS",
@@ -390,6 +466,9 @@ def main():
     import torch
     if args.siblings_bench:
         siblings_bench(max(1, args.steps))
+        return
+    if args.construct_bench:
+        construct_bench(max(1, args.steps))
         return
     if args.commit_bench:
         commit_bench(args.commit_bench, max(1, args.steps))

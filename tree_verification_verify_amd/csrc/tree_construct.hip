@@ -10,7 +10,8 @@
 //  * expand_kernel: one workgroup per frontier row. One pass over the row's
 //    logits keeps, per thread, its K best logits (ascending-index scan, so a
 //    tie keeps the lower id ahead) and an online log-sum-exp (fp32 running
-//    max and sum, combined across the block in fp64). k rounds of a block
+//    max and sum of the hardware exp2, within 1 ulp on normal results; the
+//    block combines them in fp64). k rounds of a block
 //    argmax over the threads' list heads then give the row's top-k in
 //    descending logit, lowest id first on ties; child value = frontier value
 //    + (logit - lse). Children are stored at candidate ids cand_offset +
@@ -55,6 +56,23 @@ struct ExpandParams {
   uint32_t* status;
   int V, k_in, k, cap, offset;
 };
+
+// The K-th largest (K <= 64) of one value per lane, by a bitonic sort across
+// the wave (descending), read from lane K-1.
+__device__ inline float wave_kth_largest(float v, int K) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int size = 2; size <= kWave; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const float o = shfl_xor(v, stride);
+      const bool desc = (lane & size) == 0;  // this block of `size` lanes sorts descending
+      const bool low = (lane & stride) == 0;
+      v = (low == desc) ? fmaxf(v, o) : fminf(v, o);
+    }
+  }
+  return __shfl(v, K - 1, kWave);
+}
 
 // Per-thread list of the K best (value, id) seen, best first.
 template <int K>
@@ -116,30 +134,55 @@ __global__ __launch_bounds__(kConThreads) void expand_kernel(ExpandParams p) {
   };
   const bool vec = (p.V & 3) == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0;
   if (vec) {
+    // kBatch float4 loads per thread in flight before any is consumed; each
+    // thread still visits its elements in ascending index.
     const float4* x4 = reinterpret_cast<const float4*>(x);
     const int n4 = p.V >> 2;
-    for (int e = tid; e < n4; e += kConThreads) {
-      const float4 a = x4[e];
+    // theta: the K-th largest of the wave's lane maxima. Those K lanes hold
+    // K distinct elements >= theta, so an element below theta is not among
+    // the row's K best; a float4 enters the list update only when some lane
+    // of the wave has an element that passes both its own K-th best and
+    // theta (one wave-level test per float4).
+    float theta = -INFINITY;
+    auto use = [&](const float4 a, int e) __attribute__((always_inline)) {
       const float mx = fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w));
+      bad |= !(((a.x - a.x) + (a.y - a.y)) + ((a.z - a.z) + (a.w - a.w)) == 0.f);  // NaN or Inf
       if (mx > m) {
-        s *= exp2f((m - mx) * kLog2e);
+        s *= __builtin_amdgcn_exp2f((m - mx) * kLog2e);
         m = mx;
       }
-      s += exp2f((a.x - m) * kLog2e) + exp2f((a.y - m) * kLog2e) + exp2f((a.z - m) * kLog2e) +
-           exp2f((a.w - m) * kLog2e);
-      take(a.x, 4 * e);
-      take(a.y, 4 * e + 1);
-      take(a.z, 4 * e + 2);
-      take(a.w, 4 * e + 3);
+      s += __builtin_amdgcn_exp2f((a.x - m) * kLog2e) + __builtin_amdgcn_exp2f((a.y - m) * kLog2e) + __builtin_amdgcn_exp2f((a.z - m) * kLog2e) +
+           __builtin_amdgcn_exp2f((a.w - m) * kLog2e);
+      if (__builtin_amdgcn_ballot_w64((mx >= theta) & (mx > L.v[K - 1])) != 0) {
+        L.insert(a.x, 4 * e);
+        L.insert(a.y, 4 * e + 1);
+        L.insert(a.z, 4 * e + 2);
+        L.insert(a.w, 4 * e + 3);
+      }
+    };
+    // The batch loop's exit test is taken on the wave's last lane, so every
+    // lane of a wave runs the same batches (the sort needs all 64 lanes);
+    // the remainder runs lane by lane without refreshing theta.
+    constexpr int kBatch = 8;
+    const int to_last = (kWave - 1) - lane;
+    int e = tid;
+    for (; e + to_last + (kBatch - 1) * kConThreads < n4; e += kBatch * kConThreads) {
+      float4 a[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) a[u] = x4[e + u * kConThreads];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) use(a[u], e + u * kConThreads);
+      theta = wave_kth_largest(L.v[0], K);
     }
+    for (; e < n4; e += kConThreads) use(x4[e], e);
   } else {
     for (int e = tid; e < p.V; e += kConThreads) {
       const float a = x[e];
       if (a > m) {
-        s *= exp2f((m - a) * kLog2e);
+        s *= __builtin_amdgcn_exp2f((m - a) * kLog2e);
         m = a;
       }
-      s += exp2f((a - m) * kLog2e);
+      s += __builtin_amdgcn_exp2f((a - m) * kLog2e);
       take(a, e);
     }
   }
