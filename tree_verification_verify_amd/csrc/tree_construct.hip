@@ -138,9 +138,9 @@ __global__ __launch_bounds__(kConThreads) void expand_kernel(ExpandParams p) {
     // thread still visits its elements in ascending index.
     const float4* x4 = reinterpret_cast<const float4*>(x);
     const int n4 = p.V >> 2;
-    // theta: the K-th largest of the wave's lane maxima. Those K lanes hold
-    // K distinct elements >= theta, so an element below theta is not among
-    // the row's K best; a float4 enters the list update only when some lane
+    // theta: the k-th largest of the wave's lane maxima. Those k lanes hold
+    // k distinct elements >= theta, so an element below theta is not among
+    // the row's k best (the lists keep K >= k entries; only k are used); a float4 enters the list update only when some lane
     // of the wave has an element that passes both its own K-th best and
     // theta (one wave-level test per float4).
     float theta = -INFINITY;
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kConThreads) void expand_kernel(ExpandParams p) {
       for (int u = 0; u < kBatch; ++u) a[u] = x4[e + u * kConThreads];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) use(a[u], e + u * kConThreads);
-      theta = wave_kth_largest(L.v[0], K);
+      theta = wave_kth_largest(L.v[0], p.k);
     }
     for (; e < n4; e += kConThreads) use(x4[e], e);
   } else {
