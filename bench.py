@@ -417,7 +417,7 @@ def construct_bench(reps, batch=64, vocab=151936, k=10, rounds=6, m=60):
     abytes = b_root + (rounds - 1) * b_round
     rest = float(np.mean(per[1:rounds]))
     print(json.dumps({
-        "kernel": "tree_expand_step x rounds + tree_rerank (expand_kernel<16>, select_kernel, "
+        "kernel": "tree_expand_step x rounds + tree_rerank (expand_kernel<12>, select_kernel, "
                   "rerank_kernel)",
         "workload": f"EAGLE-2 construction: {batch} requests, top-k {k}, depth {rounds}, "
                     f"keep {m}; V {vocab} fp32 synthetic draft rows",

@@ -19,10 +19,10 @@
 //  * select_kernel: one workgroup per request ranks the round's k_in * k new
 //    candidates (value descending, id ascending) and writes the k best ids,
 //    best first: the next frontier.
-// tree_rerank = rerank_kernel: one workgroup per request ranks all
-// candidates, keeps ranks < m, and places the kept ones in ascending id
-// (prefix count of kept flags): root at 0, then the tree in topological
-// order with request-local parents.
+// tree_rerank = rerank_kernel: one 1024-thread workgroup per request ranks
+// all candidates (float4 reads of the values in LDS), keeps ranks < m, and
+// places the kept ones in ascending id (block prefix count of kept flags):
+// root at 0, then the tree in topological order with request-local parents.
 //
 // The row pass is bound by HBM (4 bytes per logit); the selections touch a
 // few KB per request.
@@ -37,6 +37,8 @@ namespace {
 
 constexpr int kConThreads = 256;
 constexpr int kConWaves = kConThreads / kWave;
+constexpr int kRrThreads = 1024;  // rerank_kernel
+constexpr int kRrWaves = kRrThreads / kWave;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // (value, id) order of every selection: larger value first, lower id on ties.
@@ -154,10 +156,11 @@ __global__ __launch_bounds__(kConThreads) void expand_kernel(ExpandParams p) {
       s += __builtin_amdgcn_exp2f((a.x - m) * kLog2e) + __builtin_amdgcn_exp2f((a.y - m) * kLog2e) + __builtin_amdgcn_exp2f((a.z - m) * kLog2e) +
            __builtin_amdgcn_exp2f((a.w - m) * kLog2e);
       if (__builtin_amdgcn_ballot_w64((mx >= theta) & (mx > L.v[K - 1])) != 0) {
-        L.insert(a.x, 4 * e);
-        L.insert(a.y, 4 * e + 1);
-        L.insert(a.z, 4 * e + 2);
-        L.insert(a.w, 4 * e + 3);
+        // Only elements at or above theta can be among the row's k best.
+        if (a.x >= theta) L.insert(a.x, 4 * e);
+        if (a.y >= theta) L.insert(a.y, 4 * e + 1);
+        if (a.z >= theta) L.insert(a.z, 4 * e + 2);
+        if (a.w >= theta) L.insert(a.w, 4 * e + 3);
       }
     };
     // The batch loop's exit test is taken on the wave's last lane, so every
@@ -286,31 +289,48 @@ struct RerankParams {
   int cap, n, m;
 };
 
-__global__ __launch_bounds__(kConThreads) void rerank_kernel(RerankParams p) {
-  __shared__ float s_v[kMaxRerank];
+__global__ __launch_bounds__(kRrThreads) void rerank_kernel(RerankParams p) {
+  __shared__ __align__(16) float s_v[kMaxRerank];
   __shared__ int s_pos[kMaxRerank];
-  __shared__ int s_cnt[kConThreads];
-  const int b = blockIdx.x, t = threadIdx.x;
+  __shared__ int s_wsum[kRrWaves];
+  const int b = blockIdx.x, t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
   const size_t cb = size_t(b) * p.cap;
-  for (int i = t; i < p.n; i += kConThreads) s_v[i] = key(p.value[cb + i]);
+  const int n4 = (p.n + 3) >> 2;  // values padded with -inf to whole float4s
+  for (int i = t; i < 4 * n4; i += kRrThreads) s_v[i] = i < p.n ? key(p.value[cb + i]) : -INFINITY;
   __syncthreads();
-  // Thread t owns ids [t * per, t * per + per).
-  const int per = (p.n + kConThreads - 1) / kConThreads;
+  // Thread t owns ids [t * per, t * per + per), per <= 4. A padded id j >= n
+  // is never better than a real one (its value is -inf and its id larger).
+  const int per = (p.n + kRrThreads - 1) / kRrThreads;
   const int lo = min(p.n, t * per), hi = min(p.n, lo + per);
-  uint32_t kept = 0;  // bit j: id lo + j is kept (per <= 32)
+  uint32_t kept = 0;  // bit j: id lo + j is kept
+  const float4* v4 = reinterpret_cast<const float4*>(s_v);
   for (int i = lo; i < hi; ++i) {
     const float vi = s_v[i];
     int rank = 0;
-    for (int j = 0; j < p.n; ++j) rank += better(s_v[j], j, vi, i);
+    for (int j4 = 0; j4 < n4; ++j4) {
+      const float4 w = v4[j4];
+      const int j = 4 * j4;
+      rank += better(w.x, j, vi, i) + better(w.y, j + 1, vi, i) + better(w.z, j + 2, vi, i) +
+              better(w.w, j + 3, vi, i);
+    }
     if (rank < p.m) kept |= 1u << (i - lo);
   }
-  s_cnt[t] = __builtin_popcount(kept);
+  // Block exclusive prefix of the kept counts (thread order = id order).
+  const int mine = __builtin_popcount(kept);
+  int incl = mine;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int u = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += u;
+  }
+  if (lane == kWave - 1) s_wsum[wave] = incl;
   __syncthreads();
-  // Exclusive prefix of the kept counts (thread order = id order).
-  int before = 0;
-  for (int w = 0; w < t; ++w) before += s_cnt[w];
-  int total = before;
-  for (int w = t; w < kConThreads; ++w) total += s_cnt[w];
+  int before = incl - mine, total = 0;
+  for (int w = 0; w < kRrWaves; ++w) {
+    const int c = s_wsum[w];
+    before += w < wave ? c : 0;
+    total += c;
+  }
   int pos = 1 + before;
   for (int i = lo; i < hi; ++i) s_pos[i] = (kept >> (i - lo)) & 1 ? pos++ : 0;
   __syncthreads();
@@ -333,7 +353,7 @@ __global__ __launch_bounds__(kConThreads) void rerank_kernel(RerankParams p) {
     op[q] = pp;
     ot[q] = p.token[cb + i];
   }
-  for (int q = 1 + total + t; q < W; q += kConThreads) {
+  for (int q = 1 + total + t; q < W; q += kRrThreads) {
     op[q] = -1;
     ot[q] = -1;
   }
@@ -356,6 +376,8 @@ hipError_t launch_expand_step(int32_t batch, int32_t vocab, int32_t k_in, int32_
     hipLaunchKernelGGL(expand_kernel<4>, grid, dim3(kConThreads), 0, stream, e);
   else if (k <= 8)
     hipLaunchKernelGGL(expand_kernel<8>, grid, dim3(kConThreads), 0, stream, e);
+  else if (k <= 12)
+    hipLaunchKernelGGL(expand_kernel<12>, grid, dim3(kConThreads), 0, stream, e);
   else
     hipLaunchKernelGGL(expand_kernel<16>, grid, dim3(kConThreads), 0, stream, e);
   hipError_t err = hipGetLastError();
@@ -370,7 +392,7 @@ hipError_t launch_rerank(int32_t batch, int32_t num_cand, int32_t cap, int32_t m
                          int32_t* out_parent, int32_t* out_token, int32_t* out_count,
                          uint32_t* status, hipStream_t stream) {
   RerankParams r{value, token, parent, out_parent, out_token, out_count, status, cap, num_cand, m};
-  hipLaunchKernelGGL(rerank_kernel, dim3(unsigned(batch)), dim3(kConThreads), 0, stream, r);
+  hipLaunchKernelGGL(rerank_kernel, dim3(unsigned(batch)), dim3(kRrThreads), 0, stream, r);
   return hipGetLastError();
 }
 
