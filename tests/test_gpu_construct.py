@@ -89,3 +89,53 @@ def test_bad_frontier_and_nonfinite_logits_are_reported():
     root[1, 5] = np.nan
     got = _run(root, rows, 4, 10)
     assert got["bits"] & 4                             # TV_DEV_LOGITS
+
+
+def test_construct_then_greedy_verify_matches_the_oracle():
+    """The rows composed: the GPU builds EAGLE-2 trees, and its parent and
+    token arrays feed greedy verification (tree_spec_sample at T = 0) and
+    tree_accept_path on the GPU; the oracle runs its own construction, walk
+    and path. Target rows are the expanded nodes' draft rows plus noise, so
+    paths of several tokens are accepted."""
+    import oracle
+    from gpu_run import run_sampler
+    from workloads.inputs import SamplerInputs
+    rng = np.random.default_rng(77)
+    B, V, k, R, m = 8, 4096, 4, 4, 20
+    root, rows = make_construct_inputs(rng, B, V, k, R)
+    got = _run(root, rows, k, m)
+    assert got["status"] == 0
+    n = m + 1
+    target = np.empty((B * n, V), dtype=np.float32)
+    for b in range(B):
+        parent, token, cands, frontiers = C.eagle2_tree(root[b], list(rows[b]), k, m)
+        assert not C.near_ties(cands, frontiers, k, m, EPS)
+        np.testing.assert_array_equal(got["out_parent"][b], parent)
+        np.testing.assert_array_equal(got["out_token"][b], token)
+        _, _, keep = C.rerank(cands, m)
+        row_of = {-1: root[b]}
+        for d, fr in enumerate(frontiers[:-1]):
+            for s, f in enumerate(fr):
+                row_of[f] = rows[b, d, s]
+        for j, c in enumerate([-1] + list(keep)):
+            base = row_of.get(c)
+            if base is None:  # a leaf: its row only decides a bonus token
+                base = (rng.standard_normal(V) * 2).astype(np.float32)
+            target[b * n + j] = base + (rng.standard_normal(V) * 0.3).astype(np.float32)
+    inp = SamplerInputs(vocab=V, target_logits=target, draft_logits=None,
+                        tokens=got["out_token"].reshape(-1).astype(np.int32),
+                        node_indptr=(np.arange(B + 1) * n).astype(np.int32),
+                        parent=got["out_parent"].reshape(-1).astype(np.int32),
+                        temperature=np.zeros(B, np.float32),
+                        uniforms=np.zeros((B * n, 2), np.float32))
+    ver = run_sampler(inp, max_depth=R)
+    assert ver["status"] == 0, (ver["status"], ver["bits"])
+    flags, nts, _ = oracle.tree_spec_sample(inp)
+    pn, ot, ol, kk = oracle.tree_accept_path(inp.node_indptr, inp.parent, inp.tokens, flags, nts,
+                                             [0] * B, R)
+    np.testing.assert_array_equal(ver["flag"], flags)
+    np.testing.assert_array_equal(ver["next_token"], nts)
+    np.testing.assert_array_equal(ver["out_len"], ol)
+    np.testing.assert_array_equal(ver["out_tokens"], ot)
+    np.testing.assert_array_equal(ver["path_nodes"], pn)
+    assert ol.max() >= 3  # some request accepts at least two drafted tokens
