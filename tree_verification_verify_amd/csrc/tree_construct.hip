@@ -142,19 +142,23 @@ __global__ __launch_bounds__(kConThreads) void expand_kernel(ExpandParams p) {
     const int n4 = p.V >> 2;
     // theta: the k-th largest of the wave's lane maxima. Those k lanes hold
     // k distinct elements >= theta, so an element below theta is not among
-    // the row's k best (the lists keep K >= k entries; only k are used); a float4 enters the list update only when some lane
-    // of the wave has an element that passes both its own K-th best and
-    // theta (one wave-level test per float4).
+    // the row's k best (the lists keep K >= k entries; only k are used). A
+    // float4 enters the list update only when some lane of the wave has an
+    // element that passes both its own K-th best and theta (one wave-level
+    // test per float4); theta is refreshed every other batch.
     float theta = -INFINITY;
+    // Non-finite logits show in the sums: a NaN or a +Inf (Inf - Inf) makes
+    // the running sum NaN; -Inf shows in the running minimum.
+    float lo = INFINITY;
     auto use = [&](const float4 a, int e) __attribute__((always_inline)) {
       const float mx = fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w));
-      bad |= !(((a.x - a.x) + (a.y - a.y)) + ((a.z - a.z) + (a.w - a.w)) == 0.f);  // NaN or Inf
+      lo = fminf(lo, fminf(fminf(a.x, a.y), fminf(a.z, a.w)));
       if (mx > m) {
         s *= __builtin_amdgcn_exp2f((m - mx) * kLog2e);
         m = mx;
       }
-      s += __builtin_amdgcn_exp2f((a.x - m) * kLog2e) + __builtin_amdgcn_exp2f((a.y - m) * kLog2e) + __builtin_amdgcn_exp2f((a.z - m) * kLog2e) +
-           __builtin_amdgcn_exp2f((a.w - m) * kLog2e);
+      s += __builtin_amdgcn_exp2f((a.x - m) * kLog2e) + __builtin_amdgcn_exp2f((a.y - m) * kLog2e) +
+           __builtin_amdgcn_exp2f((a.z - m) * kLog2e) + __builtin_amdgcn_exp2f((a.w - m) * kLog2e);
       if (__builtin_amdgcn_ballot_w64((mx >= theta) & (mx > L.v[K - 1])) != 0) {
         // Only elements at or above theta can be among the row's k best.
         if (a.x >= theta) L.insert(a.x, 4 * e);
@@ -168,16 +172,17 @@ __global__ __launch_bounds__(kConThreads) void expand_kernel(ExpandParams p) {
     // the remainder runs lane by lane without refreshing theta.
     constexpr int kBatch = 8;
     const int to_last = (kWave - 1) - lane;
-    int e = tid;
+    int e = tid, nb = 0;
     for (; e + to_last + (kBatch - 1) * kConThreads < n4; e += kBatch * kConThreads) {
       float4 a[kBatch];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) a[u] = x4[e + u * kConThreads];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) use(a[u], e + u * kConThreads);
-      theta = wave_kth_largest(L.v[0], p.k);
+      if ((++nb & 1) == 1) theta = wave_kth_largest(L.v[0], p.k);  // every other batch
     }
     for (; e < n4; e += kConThreads) use(x4[e], e);
+    bad |= !(s - s == 0.f) | (lo == -INFINITY);
   } else {
     for (int e = tid; e < p.V; e += kConThreads) {
       const float a = x[e];
