@@ -381,18 +381,19 @@ def construct_bench(reps, batch=64, vocab=151936, k=10, rounds=6, m=60):
     op = torch.empty((batch, m + 1), dtype=torch.int32, device="cuda")
     ot = torch.empty_like(op)
     oc = torch.empty(batch, dtype=torch.int32, device="cuda")
-    ws = tv.alloc_workspace(256)
+    ws = tv.alloc_workspace(tv.expand_workspace_size(batch, k, k))
+    nws = ws.numel()
     lib = _lib.load()
     stream = torch.cuda.current_stream()
     P_ = ctypes.c_void_p
     ptr = lambda t: P_(t.data_ptr())
     outs = (ptr(cv), ptr(ct), ptr(cp))
     calls = [lambda: lib.tree_expand_step(batch, vocab, 1, k, ptr(root), None, cap, 0, *outs,
-                                          ptr(fr[0]), ptr(ws), P_(stream.cuda_stream))]
+                                          ptr(fr[0]), ptr(ws), nws, P_(stream.cuda_stream))]
     for d in range(rounds - 1):
         calls.append(lambda d=d: lib.tree_expand_step(
             batch, vocab, k, k, ptr(rows[d]), ptr(fr[d]), cap, k + d * k * k, *outs,
-            ptr(fr[d + 1]), ptr(ws), P_(stream.cuda_stream)))
+            ptr(fr[d + 1]), ptr(ws), nws, P_(stream.cuda_stream)))
     calls.append(lambda: lib.tree_rerank(batch, cap, cap, m, *outs, ptr(op), ptr(ot), ptr(oc),
                                          ptr(ws), P_(stream.cuda_stream)))
     for c in calls:

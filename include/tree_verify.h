@@ -304,16 +304,26 @@ tv_status tree_draw_siblings(int32_t rows, int32_t vocab, const float* draft_log
  *     below cand_offset, written at cand_offset .. cand_offset + k_in*k - 1;
  *   next_frontier [batch][k] int32 output.
  * 1 <= k, k_in <= 16, vocab >= k, cand_offset + k_in*k <= cand_capacity,
- * else TV_ERR_SHAPE. A frontier id outside [-1, cand_offset) sets
+ * else TV_ERR_SHAPE. workspace: NULL, or 256-byte aligned (else
+ * TV_ERR_WORKSPACE) with its status word at byte 0; when workspace_bytes >=
+ * tv_expand_workspace_size(batch, k_in, k), a round of fewer than 512 rows
+ * splits each row over several workgroups (partial results in the
+ * workspace), which fills the chip in the root round; the split changes
+ * only the summation order of the log-sum-exp. A frontier id outside [-1, cand_offset) sets
  * TV_DEV_TREE (the slot is expanded as the root); non-finite logits set
- * TV_DEV_LOGITS (status_workspace, if not NULL). The log-sum-exp is formed
- * in fp32 and combined in fp64, so values agree with an fp64 evaluation to
- * ~1e-6; selections can differ only where two values lie that close. */
+ * TV_DEV_LOGITS (in the workspace's status word, if any). The log-sum-exp is
+ * formed in fp32 and combined in fp64, so values agree with an fp64
+ * evaluation to ~1e-6; selections can differ only where two values lie that
+ * close. Calls that share a workspace must not overlap. */
 tv_status tree_expand_step(int32_t batch, int32_t vocab, int32_t k_in, int32_t k,
                            const float* draft_logits, const int32_t* frontier,
                            int32_t cand_capacity, int32_t cand_offset, float* cand_value,
                            int32_t* cand_token, int32_t* cand_parent, int32_t* next_frontier,
-                           void* status_workspace, hipStream_t stream);
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace with which tree_expand_step splits rounds of few rows
+ * (0 if the sizes are invalid). */
+size_t tv_expand_workspace_size(int32_t batch, int32_t k_in, int32_t k);
 
 /* Rerank: keep the m best of candidates 0 .. num_cand-1 of every request
  * (value descending, lower id on ties; a child's value never exceeds its

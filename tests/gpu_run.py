@@ -59,15 +59,16 @@ def run_sampler(inp, max_depth=None, prefix_lens=None, ws=None, replacement=Fals
                 status=st, bits=bits, max_depth=md)
 
 
-def run_construct(root, rows, k, m, num_rounds=None, bad_frontier=None):
+def run_construct(root, rows, k, m, num_rounds=None, bad_frontier=None, split=True):
     """EAGLE-2 construction on the GPU: rounds of tree_expand_step, then
-    tree_rerank. root [B][V], rows [B][R-1][k][V] (numpy fp32)."""
+    tree_rerank. root [B][V], rows [B][R-1][k][V] (numpy fp32). split: give
+    tree_expand_step the workspace with which it splits rounds of few rows."""
     import torch
     import tree_verification_verify_amd as tv
     B, V = root.shape
     R = rows.shape[1] + 1 if num_rounds is None else num_rounds
     cap = k + (R - 1) * k * k
-    ws = tv.alloc_workspace(256)
+    ws = tv.alloc_workspace(tv.expand_workspace_size(B, k, k) if split else 256)
     cv = torch.full((B, cap), float("nan"), dtype=torch.float32, device="cuda")
     ct = torch.full((B, cap), -7, dtype=torch.int32, device="cuda")
     cp = torch.full((B, cap), -7, dtype=torch.int32, device="cuda")

@@ -56,6 +56,24 @@ def test_random_shapes(V, k, R, m):
     _compare(root, rows, k, m, _run(root, rows, k, m), allow_near=1)
 
 
+@pytest.mark.parametrize("V,k,R", [(151936, 10, 3), (4099, 16, 2), (7, 3, 3)])
+def test_split_rounds_match_unsplit(V, k, R):
+    """Rows split over several workgroups (the workspace given) and unsplit
+    rows take the same decisions; values differ only in the log-sum-exp's
+    summation order."""
+    rng = np.random.default_rng(V + k)
+    root, rows = make_construct_inputs(rng, 8, V, k, R)
+    a = _run(root, rows, k, 30, split=True)
+    b = _run(root, rows, k, 30, split=False)
+    assert a["status"] == 0 and b["status"] == 0
+    for key in ("token", "parent", "out_parent", "out_token", "out_count"):
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+    for fa, fb in zip(a["frontiers"], b["frontiers"]):
+        np.testing.assert_array_equal(fa, fb)
+    np.testing.assert_allclose(a["value"], b["value"], rtol=0, atol=1e-5)
+    _compare(root, rows, k, 30, a, allow_near=1)
+
+
 def test_integer_logits_with_ties():
     """Integer logits: many exact ties inside rows (lower token id first) and
     between sibling values (lower candidate id first)."""

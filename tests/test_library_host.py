@@ -190,7 +190,7 @@ def test_construct_host_errors():
     lib = tv.library()
     P = FAKE
     exp = lambda B, V, kin, k, logits, cap, off, *outs: lib.tree_expand_step(
-        B, V, kin, k, logits, None, cap, off, *outs, None, None)
+        B, V, kin, k, logits, None, cap, off, *outs, None, 0, None)
     outs = [P, P, P, P]
     for bad in ((0, 100, 1, 4, 40, 0), (2, 3, 1, 4, 40, 0), (2, 100, 1, 17, 40, 0),
                 (2, 100, 17, 4, 400, 0), (2, 100, 2, 4, 40, 33), (2, 100, 1, 0, 40, 0),
@@ -198,6 +198,11 @@ def test_construct_host_errors():
         B, V, kin, k, cap, off = bad
         assert exp(B, V, kin, k, P, cap, off, *outs) == SHAPE, bad
     assert exp(2, 100, 1, 4, None, 40, 0, *outs) == NULL
+    misaligned = lib.tree_expand_step(2, 100, 1, 4, P, None, 40, 0, *outs,
+                                      ctypes.c_void_p(0x100010), 1 << 20, None)
+    assert misaligned == WORKSPACE
+    assert lib.tv_expand_workspace_size(64, 1, 10) > lib.tv_expand_workspace_size(2, 1, 10) > 256
+    assert lib.tv_expand_workspace_size(0, 1, 10) == 0 and lib.tv_expand_workspace_size(2, 1, 17) == 0
     for i in range(4):
         o = list(outs)
         o[i] = None

@@ -25,7 +25,7 @@ __all__ = [
     "TV_RULE_WITH_REPLACEMENT", "attn_desc",
     "sample_desc", "attn_workspace_size", "sample_workspace_size", "alloc_workspace",
     "workspace_init", "device_status", "tree_verify_attn", "tree_spec_sample",
-    "tree_accept_path", "tree_kv_commit", "tree_draw_siblings", "tree_expand_step", "tree_rerank", "tv_tree_meta", "validate_tree", "validate_pages",
+    "tree_accept_path", "tree_kv_commit", "tree_draw_siblings", "tree_expand_step", "tree_rerank", "expand_workspace_size", "tv_tree_meta", "validate_tree", "validate_pages",
     "library",
 ]
 
@@ -242,11 +242,17 @@ def tree_draw_siblings(draft_logits, counts, temperature, tokens, stream_id=0, s
         "tree_draw_siblings")
 
 
+def expand_workspace_size(batch, k_in, k):
+    return int(_lib.load().tv_expand_workspace_size(batch, k_in, k))
+
+
 def tree_expand_step(draft_logits, frontier, cand_offset, cand_value, cand_token, cand_parent,
-                     next_frontier, status_workspace=None, stream=None):
+                     next_frontier, workspace=None, stream=None):
     """One expansion round. draft_logits [B][k_in][V] fp32; frontier [B][k_in]
     int32 candidate ids or None (every slot is the root); cand_* [B][C];
-    next_frontier [B][k] int32 (k = children per node = its second size)."""
+    next_frontier [B][k] int32 (k = children per node = its second size);
+    workspace: None, or a uint8 workspace (status word; with
+    expand_workspace_size bytes, rounds of few rows are split)."""
     import torch
     _need(draft_logits, "draft_logits", torch.float32)
     _need(cand_value, "cand_value", torch.float32)
@@ -265,10 +271,12 @@ def tree_expand_step(draft_logits, frontier, cand_offset, cand_value, cand_token
     if cand_value.shape[0] != B or next_frontier.shape[0] != B or \
             tuple(cand_token.shape) != (B, C) or tuple(cand_parent.shape) != (B, C):
         raise ValueError("candidate arrays must be [B][C]")
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8)
     _check(_lib.load().tree_expand_step(
         B, V, k_in, k, _ptr(draft_logits), _ptr(frontier), C, int(cand_offset), _ptr(cand_value),
-        _ptr(cand_token), _ptr(cand_parent), _ptr(next_frontier), _ptr(status_workspace),
-        _stream(stream)), "tree_expand_step")
+        _ptr(cand_token), _ptr(cand_parent), _ptr(next_frontier), _ptr(workspace),
+        0 if workspace is None else workspace.numel(), _stream(stream)), "tree_expand_step")
 
 
 def tree_rerank(num_cand, m, cand_value, cand_token, cand_parent, out_parent, out_token,

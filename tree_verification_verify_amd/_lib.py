@@ -39,6 +39,7 @@ EXPORTS = [
     "tv_attn_workspace_size", "tv_sample_workspace_size", "tv_workspace_init",
     "tv_device_status", "tree_verify_attn", "tree_spec_sample", "tree_accept_path",
     "tree_kv_commit", "tree_draw_siblings", "tree_expand_step", "tree_rerank",
+    "tv_expand_workspace_size",
     "tv_tree_meta", "tv_validate_tree", "tv_validate_pages", "tv_status_string",
     "tv_last_hip_error", "tv_version",
 ]
@@ -71,7 +72,9 @@ def load():
         "tree_kv_commit": (st, [ctypes.POINTER(AttnDesc), I32, ctypes.c_int64] + [P] * 7
                            + [I32, P, P]),
         "tree_draw_siblings": (st, [I32, I32, P, P, P, ctypes.c_uint32, ctypes.c_uint64, P, P, P]),
-        "tree_expand_step": (st, [I32, I32, I32, I32, P, P, I32, I32, P, P, P, P, P, P]),
+        "tree_expand_step": (st, [I32, I32, I32, I32, P, P, I32, I32, P, P, P, P, P,
+                                  ctypes.c_size_t, P]),
+        "tv_expand_workspace_size": (ctypes.c_size_t, [I32, I32, I32]),
         "tree_rerank": (st, [I32, I32, I32, I32, P, P, P, P, P, P, P, P]),
         "tv_tree_meta": (st, [I32, I32] + [P] * 6 + [P, P]),
         "tv_validate_tree": (st, [I32, P, P, I32, I32]),

@@ -185,7 +185,7 @@ tv_status tree_expand_step(int32_t batch, int32_t vocab, int32_t k_in, int32_t k
                            const float* draft_logits, const int32_t* frontier,
                            int32_t cand_capacity, int32_t cand_offset, float* cand_value,
                            int32_t* cand_token, int32_t* cand_parent, int32_t* next_frontier,
-                           void* status_workspace, hipStream_t stream) {
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (batch < 1 || k < 1 || k > tv::kMaxExpand || k_in < 1 || k_in > tv::kMaxExpand ||
       vocab < k || cand_offset < 0 || cand_capacity < 1 ||
       long(cand_offset) + long(k_in) * k > long(cand_capacity) ||
@@ -193,12 +193,18 @@ tv_status tree_expand_step(int32_t batch, int32_t vocab, int32_t k_in, int32_t k
     return TV_ERR_SHAPE;
   if (!draft_logits || !cand_value || !cand_token || !cand_parent || !next_frontier)
     return TV_ERR_NULL;
+  if (workspace && !aligned256(workspace)) return TV_ERR_WORKSPACE;
   hipError_t e = tv::launch_expand_step(batch, vocab, k_in, k, draft_logits, frontier,
                                         cand_capacity, cand_offset, cand_value, cand_token,
-                                        cand_parent, next_frontier,
-                                        static_cast<uint32_t*>(status_workspace), stream);
+                                        cand_parent, next_frontier, workspace, workspace_bytes,
+                                        stream);
   if (e != hipSuccess) return hip_fail(e, "tree_expand_step");
   return TV_OK;
+}
+
+size_t tv_expand_workspace_size(int32_t batch, int32_t k_in, int32_t k) {
+  if (batch < 1 || k < 1 || k > tv::kMaxExpand || k_in < 1 || k_in > tv::kMaxExpand) return 0;
+  return tv::expand_workspace_bytes(batch, k_in, k);
 }
 
 tv_status tree_rerank(int32_t batch, int32_t num_cand, int32_t cand_capacity, int32_t m,

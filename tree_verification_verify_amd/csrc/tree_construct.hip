@@ -28,6 +28,8 @@
 // few KB per request.
 #include <math.h>
 
+#include <algorithm>
+
 #include "tv_device.hpp"
 #include "tv_internal.hpp"
 
@@ -40,6 +42,7 @@ constexpr int kConWaves = kConThreads / kWave;
 constexpr int kRrThreads = 1024;  // rerank_kernel
 constexpr int kRrWaves = kRrThreads / kWave;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr long kSplitRows = 512;  // rounds with fewer rows split them (workspace permitting)
 
 // (value, id) order of every selection: larger value first, lower id on ties.
 // Values pass through key() first: NaN (from non-finite logits, already
@@ -57,6 +60,14 @@ struct ExpandParams {
   int32_t* parent;          // [batch][cap]
   uint32_t* status;
   int V, k_in, k, cap, offset;
+  // Split rounds (S > 1): workgroup (row, seg) covers float4s (or logits)
+  // [seg * n / S, (seg + 1) * n / S) of the row and writes its k best
+  // (logit, id) and its log-sum-exp partial (max, rescaled sum) here.
+  int S;
+  float* part_v;    // [rows][S][k]
+  int32_t* part_i;  // [rows][S][k]
+  float* part_m;    // [rows][S]
+  double* part_s;   // [rows][S]
 };
 
 // The K-th largest (K <= 64) of one value per lane, by a bitonic sort across
@@ -121,7 +132,8 @@ __global__ __launch_bounds__(kConThreads) void expand_kernel(ExpandParams p) {
   __shared__ int s_i[kConWaves];
   __shared__ float s_m[kConWaves];
   __shared__ double s_s[kConWaves];
-  const int row = blockIdx.x;  // request * k_in + slot
+  const int row = blockIdx.x / p.S;  // request * k_in + slot
+  const int seg = blockIdx.x - row * p.S;
   const int b = row / p.k_in, slot = row - b * p.k_in;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const float* x = p.logits + size_t(row) * p.V;
@@ -139,7 +151,8 @@ __global__ __launch_bounds__(kConThreads) void expand_kernel(ExpandParams p) {
     // kBatch float4 loads per thread in flight before any is consumed; each
     // thread still visits its elements in ascending index.
     const float4* x4 = reinterpret_cast<const float4*>(x);
-    const int n4 = p.V >> 2;
+    const int n4 = int((long(seg + 1) * (p.V >> 2)) / p.S);  // this segment's end
+    const int lo4 = int((long(seg) * (p.V >> 2)) / p.S);
     // theta: the k-th largest of the wave's lane maxima. Those k lanes hold
     // k distinct elements >= theta, so an element below theta is not among
     // the row's k best (the lists keep K >= k entries; only k are used). A
@@ -172,7 +185,7 @@ __global__ __launch_bounds__(kConThreads) void expand_kernel(ExpandParams p) {
     // the remainder runs lane by lane without refreshing theta.
     constexpr int kBatch = 8;
     const int to_last = (kWave - 1) - lane;
-    int e = tid, nb = 0;
+    int e = lo4 + tid, nb = 0;
     for (; e + to_last + (kBatch - 1) * kConThreads < n4; e += kBatch * kConThreads) {
       float4 a[kBatch];
 #pragma unroll
@@ -184,7 +197,8 @@ __global__ __launch_bounds__(kConThreads) void expand_kernel(ExpandParams p) {
     for (; e < n4; e += kConThreads) use(x4[e], e);
     bad |= !(s - s == 0.f) | (lo == -INFINITY);
   } else {
-    for (int e = tid; e < p.V; e += kConThreads) {
+    const int hi = int((long(seg + 1) * p.V) / p.S);
+    for (int e = int((long(seg) * p.V) / p.S) + tid; e < hi; e += kConThreads) {
       const float a = x[e];
       if (a > m) {
         s *= __builtin_amdgcn_exp2f((m - a) * kLog2e);
@@ -216,14 +230,19 @@ __global__ __launch_bounds__(kConThreads) void expand_kernel(ExpandParams p) {
   const double lse = double(M) + log(S);
 
   // Frontier value (root: 0); a frontier id outside the earlier candidates
-  // is reported and taken as the root.
+  // is reported and taken as the root. (Split rounds: the merge does this.)
   int f = p.frontier ? p.frontier[size_t(b) * p.k_in + slot] : -1;
   if (f < -1 || f >= p.offset) {
-    if (tid == 0) raise_status(p.status, TV_DEV_TREE);
+    if (tid == 0 && p.S == 1) raise_status(p.status, TV_DEV_TREE);
     f = -1;
   }
   const size_t cb = size_t(b) * p.cap;
-  const double base = f < 0 ? 0.0 : double(p.value[cb + f]);
+  const double base = f < 0 || p.S > 1 ? 0.0 : double(p.value[cb + f]);
+  const size_t ps = size_t(row) * p.S + seg;  // this segment's partial slot
+  if (p.S > 1 && tid == 0) {
+    p.part_m[ps] = M;
+    p.part_s[ps] = S;
+  }
 
   // k rounds of block argmax over the list heads.
   for (int r = 0; r < p.k; ++r) {
@@ -253,7 +272,10 @@ __global__ __launch_bounds__(kConThreads) void expand_kernel(ExpandParams p) {
       }
     __syncthreads();  // every thread has read this round's winners
     if (L.i[0] == wi) L.pop();  // ids are unique across threads
-    if (tid == 0) {
+    if (tid == 0 && p.S > 1) {
+      p.part_v[ps * p.k + r] = wv;
+      p.part_i[ps * p.k + r] = wi;
+    } else if (tid == 0) {
       const size_t c = cb + size_t(p.offset) + size_t(slot) * p.k + r;
       const bool ok = wi < p.V;
       p.token[c] = ok ? wi : -1;
@@ -264,21 +286,82 @@ __global__ __launch_bounds__(kConThreads) void expand_kernel(ExpandParams p) {
 }
 
 struct SelectParams {
-  const float* value;     // [batch][cap]
+  float* value;           // [batch][cap]
+  int32_t* token;         // [batch][cap]
+  int32_t* parent;        // [batch][cap]
+  const int32_t* frontier;
   int32_t* next;          // [batch][k]
-  int cap, offset, n, k;  // candidates offset .. offset + n - 1
+  uint32_t* status;
+  int cap, offset, n, k;  // candidates offset .. offset + n - 1 (n = k_in * k)
+  int k_in, V, S;         // S > 1: first merge the segments' partials
+  const float* part_v;
+  const int32_t* part_i;
+  const float* part_m;
+  const double* part_s;
 };
 
 __global__ __launch_bounds__(kConThreads) void select_kernel(SelectParams p) {
   __shared__ float s_v[kConThreads];
+  __shared__ float s_pv[kConThreads * kMaxSplit];
+  __shared__ int s_pi[kConThreads * kMaxSplit];
+  __shared__ double s_lse[kMaxExpand], s_base[kMaxExpand];
+  __shared__ int s_f[kMaxExpand];
   const int b = blockIdx.x, t = threadIdx.x;
-  const float* v = p.value + size_t(b) * p.cap + p.offset;
-  const float mine = t < p.n ? key(v[t]) : -INFINITY;
-  s_v[t] = mine;
-  __syncthreads();
+  const size_t cb = size_t(b) * p.cap;
+  if (p.S > 1) {
+    // Merge: slot j's S * k partial entries -> its k children, and the
+    // segments' log-sum-exp partials -> the row's lse (fp64).
+    const int per_row = p.S * p.k, total = p.k_in * per_row;
+    s_v[t] = -INFINITY;  // (a row without k finite logits leaves slots unwritten)
+    const size_t row0 = size_t(b) * p.k_in;
+    for (int q = t; q < total; q += kConThreads) {
+      s_pv[q] = p.part_v[row0 * per_row + q];
+      s_pi[q] = p.part_i[row0 * per_row + q];
+    }
+    if (t < p.k_in) {
+      const size_t r = row0 + t;
+      float M = -INFINITY;
+      for (int g = 0; g < p.S; ++g) M = fmaxf(M, p.part_m[r * p.S + g]);
+      double sum = 0.0;
+      for (int g = 0; g < p.S; ++g) {
+        const double sg = p.part_s[r * p.S + g];
+        if (sg > 0.0) sum += sg * exp(double(p.part_m[r * p.S + g]) - double(M));
+      }
+      int f = p.frontier ? p.frontier[row0 + t] : -1;
+      if (f < -1 || f >= p.offset) {
+        raise_status(p.status, TV_DEV_TREE);
+        f = -1;
+      }
+      s_lse[t] = double(M) + log(sum);
+      s_base[t] = f < 0 ? 0.0 : double(p.value[cb + f]);
+      s_f[t] = f;
+    }
+    __syncthreads();
+    for (int q = t; q < total; q += kConThreads) {
+      const int j = q / per_row, e0 = j * per_row;
+      const float vq = s_pv[q];
+      const int iq = s_pi[q];
+      int rank = 0;
+      for (int e = 0; e < per_row; ++e) rank += better(s_pv[e0 + e], s_pi[e0 + e], vq, iq);
+      if (rank < p.k) {
+        const int c = j * p.k + rank;
+        const bool ok = iq < p.V;
+        const float val = ok ? float(s_base[j] + (double(vq) - s_lse[j])) : -INFINITY;
+        p.token[cb + p.offset + c] = ok ? iq : -1;
+        p.value[cb + p.offset + c] = val;
+        p.parent[cb + p.offset + c] = s_f[j];
+        s_v[c] = val;  // the selection below reads the values from LDS
+      }
+    }
+    __syncthreads();
+  } else {
+    s_v[t] = t < p.n ? p.value[cb + p.offset + t] : -INFINITY;
+    __syncthreads();
+  }
+  const float mine = t < p.n ? key(s_v[t]) : -INFINITY;
   if (t < p.n) {
     int rank = 0;
-    for (int j = 0; j < p.n; ++j) rank += better(s_v[j], j, mine, t);
+    for (int j = 0; j < p.n; ++j) rank += better(key(s_v[j]), j, mine, t);
     if (rank < p.k) p.next[size_t(b) * p.k + rank] = p.offset + t;
   }
 }
@@ -371,12 +454,37 @@ __global__ __launch_bounds__(kRrThreads) void rerank_kernel(RerankParams p) {
 
 }  // namespace
 
+size_t expand_workspace_bytes(int32_t batch, int32_t k_in, int32_t k) {
+  const size_t slots = size_t(batch) * k_in * kMaxSplit;
+  return kHeaderBytes + align256(slots * k * 4) * 2 + align256(slots * 4) + align256(slots * 8);
+}
+
 hipError_t launch_expand_step(int32_t batch, int32_t vocab, int32_t k_in, int32_t k,
                               const float* logits, const int32_t* frontier, int32_t cap,
                               int32_t offset, float* value, int32_t* token, int32_t* parent,
-                              int32_t* next, uint32_t* status, hipStream_t stream) {
-  ExpandParams e{logits, frontier, value, token, parent, status, vocab, k_in, k, cap, offset};
-  const dim3 grid(unsigned(batch) * unsigned(k_in));
+                              int32_t* next, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  uint32_t* status = static_cast<uint32_t*>(workspace);
+  // Rounds with fewer rows than kSplitRows split each row over up to
+  // kMaxSplit workgroups when the workspace holds the partials.
+  const long rows = long(batch) * k_in;
+  int S = 1;
+  if (workspace && workspace_bytes >= expand_workspace_bytes(batch, k_in, k) && rows < kSplitRows)
+    S = int(std::min<long>(kMaxSplit, std::max<long>(1, kSplitRows / rows)));
+  ExpandParams e{logits, frontier, value, token, parent, status, vocab, k_in, k, cap, offset,
+                 S, nullptr, nullptr, nullptr, nullptr};
+  if (S > 1) {
+    const size_t slots = size_t(batch) * k_in * kMaxSplit;
+    char* w = static_cast<char*>(workspace) + kHeaderBytes;
+    e.part_v = reinterpret_cast<float*>(w);
+    w += align256(slots * k * 4);
+    e.part_i = reinterpret_cast<int32_t*>(w);
+    w += align256(slots * k * 4);
+    e.part_m = reinterpret_cast<float*>(w);
+    w += align256(slots * 4);
+    e.part_s = reinterpret_cast<double*>(w);
+  }
+  const dim3 grid(static_cast<unsigned>(rows * S));
   if (k <= 4)
     hipLaunchKernelGGL(expand_kernel<4>, grid, dim3(kConThreads), 0, stream, e);
   else if (k <= 8)
@@ -387,8 +495,9 @@ hipError_t launch_expand_step(int32_t batch, int32_t vocab, int32_t k_in, int32_
     hipLaunchKernelGGL(expand_kernel<16>, grid, dim3(kConThreads), 0, stream, e);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  SelectParams s{value, next, cap, offset, k_in * k, k};
-  hipLaunchKernelGGL(select_kernel, dim3(unsigned(batch)), dim3(kConThreads), 0, stream, s);
+  SelectParams sp{value, token, parent, frontier, next, status, cap, offset, k_in * k, k,
+                  k_in, vocab, S, e.part_v, e.part_i, e.part_m, e.part_s};
+  hipLaunchKernelGGL(select_kernel, dim3(unsigned(batch)), dim3(kConThreads), 0, stream, sp);
   return hipGetLastError();
 }
 

@@ -98,10 +98,13 @@ hipError_t launch_draw_siblings(int32_t rows, int32_t vocab, const float* draft_
 // Draft-tree construction (expansion round, rerank).
 constexpr int kMaxRerank = 4096;  // candidates per request the rerank holds in LDS
 constexpr int kMaxExpand = 16;    // children per node and frontier slots per round
+constexpr int kMaxSplit = 8;      // workgroups per row in rounds with few rows
+size_t expand_workspace_bytes(int32_t batch, int32_t k_in, int32_t k);
 hipError_t launch_expand_step(int32_t batch, int32_t vocab, int32_t k_in, int32_t k,
                               const float* logits, const int32_t* frontier, int32_t cap,
                               int32_t offset, float* value, int32_t* token, int32_t* parent,
-                              int32_t* next, uint32_t* status, hipStream_t stream);
+                              int32_t* next, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
 hipError_t launch_rerank(int32_t batch, int32_t num_cand, int32_t cap, int32_t m,
                          const float* value, const int32_t* token, const int32_t* parent,
                          int32_t* out_parent, int32_t* out_token, int32_t* out_count,
