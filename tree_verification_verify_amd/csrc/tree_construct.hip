@@ -306,6 +306,8 @@ __global__ __launch_bounds__(kConThreads) void select_kernel(SelectParams p) {
   __shared__ int s_pi[kConThreads * kMaxSplit];
   __shared__ double s_lse[kMaxExpand], s_base[kMaxExpand];
   __shared__ int s_f[kMaxExpand];
+  __shared__ float s_pm[kMaxExpand * kMaxSplit];
+  __shared__ double s_ps[kMaxExpand * kMaxSplit];
   const int b = blockIdx.x, t = threadIdx.x;
   const size_t cb = size_t(b) * p.cap;
   if (p.S > 1) {
@@ -314,27 +316,35 @@ __global__ __launch_bounds__(kConThreads) void select_kernel(SelectParams p) {
     const int per_row = p.S * p.k, total = p.k_in * per_row;
     s_v[t] = -INFINITY;  // (a row without k finite logits leaves slots unwritten)
     const size_t row0 = size_t(b) * p.k_in;
+    // Every partial is staged into LDS by its own thread (one round of
+    // loads), next to the frontier nodes' ids and values.
     for (int q = t; q < total; q += kConThreads) {
       s_pv[q] = p.part_v[row0 * per_row + q];
       s_pi[q] = p.part_i[row0 * per_row + q];
     }
+    if (t < p.k_in * p.S) {
+      s_pm[t] = p.part_m[row0 * p.S + t];
+      s_ps[t] = p.part_s[row0 * p.S + t];
+    }
     if (t < p.k_in) {
-      const size_t r = row0 + t;
-      float M = -INFINITY;
-      for (int g = 0; g < p.S; ++g) M = fmaxf(M, p.part_m[r * p.S + g]);
-      double sum = 0.0;
-      for (int g = 0; g < p.S; ++g) {
-        const double sg = p.part_s[r * p.S + g];
-        if (sg > 0.0) sum += sg * exp(double(p.part_m[r * p.S + g]) - double(M));
-      }
       int f = p.frontier ? p.frontier[row0 + t] : -1;
       if (f < -1 || f >= p.offset) {
         raise_status(p.status, TV_DEV_TREE);
         f = -1;
       }
-      s_lse[t] = double(M) + log(sum);
       s_base[t] = f < 0 ? 0.0 : double(p.value[cb + f]);
       s_f[t] = f;
+    }
+    __syncthreads();
+    if (t < p.k_in) {
+      float M = -INFINITY;
+      for (int g = 0; g < p.S; ++g) M = fmaxf(M, s_pm[t * p.S + g]);
+      double sum = 0.0;
+      for (int g = 0; g < p.S; ++g) {
+        const double sg = s_ps[t * p.S + g];
+        if (sg > 0.0) sum += sg * exp(double(s_pm[t * p.S + g]) - double(M));
+      }
+      s_lse[t] = double(M) + log(sum);
     }
     __syncthreads();
     for (int q = t; q < total; q += kConThreads) {
