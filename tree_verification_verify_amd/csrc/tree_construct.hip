@@ -224,10 +224,10 @@ __global__ __launch_bounds__(kConThreads) void expand_kernel(ExpandParams p) {
   for (int o = kWave / 2; o > 0; o >>= 1) sd += shfl_xor_d(sd, o);
   if (lane == 0) s_s[wave] = sd;
   __syncthreads();
-  double S = 0.0;
+  double sum = 0.0;
 #pragma unroll
-  for (int w = 0; w < kConWaves; ++w) S += s_s[w];
-  const double lse = double(M) + log(S);
+  for (int w = 0; w < kConWaves; ++w) sum += s_s[w];
+  const double lse = double(M) + log(sum);
 
   // Frontier value (root: 0); a frontier id outside the earlier candidates
   // is reported and taken as the root. (Split rounds: the merge does this.)
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(kConThreads) void expand_kernel(ExpandParams p) {
   const size_t ps = size_t(row) * p.S + seg;  // this segment's partial slot
   if (p.S > 1 && tid == 0) {
     p.part_m[ps] = M;
-    p.part_s[ps] = S;
+    p.part_s[ps] = sum;
   }
 
   // k rounds of block argmax over the list heads.
