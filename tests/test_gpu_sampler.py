@@ -326,3 +326,32 @@ def test_monte_carlo_tv_with_replacement_on_gpu():
     tvs = [0.5 * np.abs(rng.multinomial(n, p) / n - p).sum() for _ in range(300)]
     assert tv_walk <= np.percentile(tvs, 99), (tv_walk, np.percentile(tvs, 99))
     _compare(inp, got, replacement=True)
+
+
+@pytest.mark.parametrize("replacement", [False, True])
+def test_topk_siblings_are_biased_on_gpu(replacement):
+    """The biased control ([TreeSpark §5.4, Table 9]): siblings fixed to the
+    top 3 of q instead of drawn. With q = p on a diffuse target, the first
+    candidate is always accepted, so the walk emits the argmax: its TV to p
+    is far above direct sampling's at equal n (and the GPU still matches the
+    oracle decision for decision)."""
+    rng = np.random.default_rng(23)
+    V, k, n = 16, 3, 3000
+    logits = (rng.standard_normal(V) * 0.5).astype(np.float32)
+    inp = make_sampler_inputs(rng, rng, rng, [star_tree(k + 1)] * n, V, [1.0] * n)
+    inp.target_logits[:] = logits
+    inp.draft_logits[:] = logits
+    top = np.argsort(-logits.astype(np.float64), kind="stable")[:k].astype(np.int32)
+    for r in range(n):
+        inp.tokens[r * (k + 1) + 1:(r + 1) * (k + 1)] = top
+    got = _run(inp, max_depth=1, replacement=replacement)
+    p = np.exp(logits.astype(np.float64) - logits.max())
+    p /= p.sum()
+    first = got["out_tokens"][:, 0]
+    tv_walk = 0.5 * np.abs(np.bincount(first, minlength=V) / n - p).sum()
+    tvs = [0.5 * np.abs(rng.multinomial(n, p) / n - p).sum() for _ in range(300)]
+    print(f"top-k control TV {tv_walk:.3f}, direct sampling 99th percentile "
+          f"{np.percentile(tvs, 99):.3f}, 1 - max p {1 - p.max():.3f}")
+    assert tv_walk > 5 * np.percentile(tvs, 99)
+    assert abs(tv_walk - (1 - p.max())) < 1e-9  # the argmax every time
+    _compare(inp, got, replacement=replacement)
