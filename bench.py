@@ -358,10 +358,11 @@ def siblings_bench(reps):
 
 def construct_bench(reps, batch=64, vocab=151936, k=10, rounds=6, m=60):
     """EAGLE-2 construction alone (top-k 10, depth 6, 60 kept nodes, the
-    survey's EAGLE-2 setting) for a 64-request batch over V = 151936: round 1
-    expands each root row, rounds 2..6 the 10 frontier rows of every request
-    (synthetic drafter rows resident in HBM), then the rerank. Algorithmic
-    bytes of a round: its draft rows read once (outputs are a few KB)."""
+    survey's EAGLE-2 setting) for a 64-request batch over V = 151936: the
+    first expansion round expands each root row, expansion rounds 2..6 the 10
+    frontier rows of every request (synthetic drafter rows resident in HBM),
+    then the rerank. Algorithmic bytes of an expansion round: its draft rows
+    read once (outputs are a few KB)."""
     import ctypes
     import torch
     import tree_verification_verify_amd as tv
