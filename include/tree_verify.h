@@ -192,7 +192,10 @@ tv_status tree_verify_attn(const tv_attn_desc* desc,
  *   target_logits, draft_logits [T][V] fp32; draft_logits may be NULL when
  *     every temperature is 0 (a T > 0 request then sets TV_DEV_LOGITS).
  *   tokens [T] int32 token of each node (root ignored); siblings distinct
- *     under the without-replacement rule, repeats allowed with replacement.
+ *     under the without-replacement rule, repeats allowed with replacement
+ *     for T > 0 requests only. A greedy (T == 0) request needs distinct
+ *     siblings under either rule: siblings that repeat the argmax token are
+ *     all flagged, and tree_accept_path then reports TV_DEV_PATH.
  *   node_indptr [B+1], parent [T] int32; temperature [B] fp32 >= 0;
  *   uniforms [T][2] fp32 in [0,1).
  *   accept_flag [T] int8, next_token [T] int32: outputs.

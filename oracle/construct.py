@@ -109,32 +109,43 @@ def eagle2_tree(root_row, round_rows, k, m):
     return parent, token, cands, frontiers
 
 
+def near_gap(gap, eps):
+    """A decision gap that rounding could flip: positive and below eps. An
+    exact tie (gap 0: siblings with equal logits, identical arithmetic on any
+    side) is broken by id the same way everywhere and does not count."""
+    return 0.0 < float(gap) < eps
+
+
+def order_gaps(vals, n):
+    """Gaps between consecutive values among the n+1 best (descending): the
+    order of the n best and the cut below them."""
+    s = np.sort(np.asarray(vals, dtype=np.float64))[::-1][:n + 1]
+    return s[:-1] - s[1:]
+
+
+def cut_gap(vals, n):
+    """The gap at the cut below the n best ([] when there are at most n)."""
+    s = np.sort(np.asarray(vals, dtype=np.float64))[::-1]
+    return s[n - 1:n] - s[n:n + 1] if len(s) > n else s[:0]
+
+
+def round_ranges(k, rounds):
+    """(start, count) of the candidate ids each round created: k for the
+    root round, k * k for every later round."""
+    out, start = [], 0
+    for d in range(rounds):
+        count = k if d == 0 else k * k
+        out.append((start, count))
+        start += count
+    return out
+
+
 def near_ties(cands, frontiers, k, m, eps):
     """True when a decision lies within eps of going the other way: the order
     of a round's k best values (the frontier's slot order decides which draft
-    row each slot reads next) and its cut, or the rerank cut. Exact ties
-    (siblings with equal logits: identical arithmetic on any side) are
-    broken by id and do not count."""
+    row each slot reads next) and its cut, or the rerank cut."""
     v = np.asarray(cands.value)
-
-    def close(vals, n, whole_order):
-        s = np.sort(np.asarray(vals))[::-1]
-        if len(s) <= 1:
-            return False
-        if whole_order:
-            gaps = s[:min(n + 1, len(s)) - 1] - s[1:min(n + 1, len(s))]
-        else:
-            if len(s) <= n:
-                return False
-            gaps = np.array([s[n - 1] - s[n]])
-        return bool(((gaps > 0) & (gaps < eps)).any())
-
-    # round r created ids [start_r, start_r + count_r)
-    start, count = 0, k
-    hit = close(v[start:start + count], k, True)
-    start += count
-    for _ in frontiers[1:]:
-        count = k * k
-        hit |= close(v[start:start + count], k, True)
-        start += count
-    return hit or close(v, m, False)
+    for start, count in round_ranges(k, len(frontiers)):
+        if any(near_gap(g, eps) for g in order_gaps(v[start:start + count], k)):
+            return True
+    return any(near_gap(g, eps) for g in cut_gap(v, m))

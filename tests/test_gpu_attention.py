@@ -53,28 +53,18 @@ def test_batched_full():
     _check(cfg.attn, got, st)
 
 
-def test_sequoia_sampled_rows():
+def test_sequoia_all_rows():
+    """Every one of the 768 rows (depth 12, 24 bitset words per row)."""
     cfg = make_config("sequoia", sampler=False)
     got, st, _ = _run(cfg.attn)
-    rng = np.random.default_rng(0)
-    depth = oracle.depths(cfg.trees[0])
-    picks = [(0, 0), (0, 767), (0, int(np.argmax(depth)))] + \
-            [(0, int(i)) for i in rng.choice(768, 45, replace=False)]
-    _check(cfg.attn, got, st, picks=picks)
-    assert np.isfinite(got).all()
+    _check(cfg.attn, got, st)
 
 
-def test_highload_sampled():
+def test_highload_all_rows():
+    """The benchmark's workload and launch: all 1216 rows of the 64 requests."""
     cfg = make_config("highload", sampler=False)
-    inp = cfg.attn
-    got, st, _ = _run(inp)
-    rng = np.random.default_rng(1)
-    picks = []
-    for r in rng.choice(inp.batch, 8, replace=False):
-        n = inp.nodes(int(r))
-        picks += [(int(r), int(i)) for i in rng.choice(n, min(n, 6), replace=False)]
-    _check(inp, got, st, picks=picks)
-    assert np.isfinite(got).all()
+    got, st, _ = _run(cfg.attn)
+    _check(cfg.attn, got, st)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
@@ -112,8 +102,7 @@ def test_max_nodes_tree():
     trees = [random_tree(rng, 1024, depth_cap=20)]
     inp = make_attention_inputs(rng, rng, trees, [300], 8, 2, 128, dtype="bf16")
     got, st, _ = _run(inp)
-    picks = [(0, int(i)) for i in rng.choice(1024, 40, replace=False)] + [(0, 1023)]
-    _check(inp, got, st, picks=picks)
+    _check(inp, got, st)
 
 
 def test_deterministic_and_page_placement_invariant():

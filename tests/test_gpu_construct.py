@@ -42,18 +42,22 @@ def _compare(root, rows, k, m, got, requests=None, allow_near=0):
         np.testing.assert_array_equal(got["out_token"][b, :cnt], token)
         assert (got["out_parent"][b, cnt:] == -1).all() and (got["out_token"][b, cnt:] == -1).all()
     assert near <= allow_near, near
+    total = B if requests is None else len(requests)
+    assert total - near >= total - allow_near >= 1
     return near
 
 
-@pytest.mark.parametrize("V,k,R,m", [(7, 3, 3, 8), (64, 4, 4, 20), (1000, 10, 6, 60),
-                                     (4099, 16, 3, 100), (4096, 1, 5, 10), (300, 8, 2, 1000),
-                                     (50, 2, 6, 1)])
-def test_random_shapes(V, k, R, m):
+# near: requests the oracle itself finds within EPS of a tie (counted on the
+# CPU from the oracle alone); the rest are compared.
+@pytest.mark.parametrize("V,k,R,m,near", [(7, 3, 3, 8, 0), (64, 4, 4, 20, 0), (1000, 10, 6, 60, 0),
+                                          (4099, 16, 3, 100, 1), (4096, 1, 5, 10, 0),
+                                          (300, 8, 2, 1000, 0), (50, 2, 6, 1, 0)])
+def test_random_shapes(V, k, R, m, near):
     """Scalar (V % 4 != 0) and vector rows, k from 1 to 16, m below, at and
     above the candidate count."""
     rng = np.random.default_rng(V + 7 * k + R)
     root, rows = make_construct_inputs(rng, 6, V, k, R)
-    _compare(root, rows, k, m, _run(root, rows, k, m), allow_near=1)
+    _compare(root, rows, k, m, _run(root, rows, k, m), allow_near=near)
 
 
 @pytest.mark.parametrize("V,k,R", [(151936, 10, 3), (4099, 16, 2), (7, 3, 3)])
@@ -71,7 +75,7 @@ def test_split_rounds_match_unsplit(V, k, R):
     for fa, fb in zip(a["frontiers"], b["frontiers"]):
         np.testing.assert_array_equal(fa, fb)
     np.testing.assert_allclose(a["value"], b["value"], rtol=0, atol=1e-5)
-    _compare(root, rows, k, 30, a, allow_near=1)
+    _compare(root, rows, k, 30, a, allow_near=0)
 
 
 def test_integer_logits_with_ties():
@@ -79,19 +83,18 @@ def test_integer_logits_with_ties():
     between sibling values (lower candidate id first)."""
     rng = np.random.default_rng(3)
     root, rows = make_construct_inputs(rng, 8, 257, 6, 4, integer_levels=5)
-    _compare(root, rows, 6, 40, _run(root, rows, 6, 40), allow_near=8)
+    _compare(root, rows, 6, 40, _run(root, rows, 6, 40), allow_near=1)
 
 
 def test_eagle2_shape_full_vocab():
     """The EAGLE-2 shape (top-k 10, depth 6, 60 kept nodes) over V = 151936 for
-    a 64-request batch; the oracle checks 10 sampled requests one by one (at
-    most 3 of them excluded for near ties; 4 of the 64 have one) and every
-    request's tree is checked for shape."""
+    a 64-request batch; every request is compared with the oracle (4 of the
+    64 have a near tie and are excluded) and checked for shape."""
     rng = np.random.default_rng(2024)
     B, V, k, R, m = 64, 151936, 10, 6, 60
     root, rows = make_construct_inputs(rng, B, V, k, R)
     got = _run(root, rows, k, m)
-    _compare(root, rows, k, m, got, requests=[0, 5, 9, 17, 21, 30, 38, 44, 50, 63], allow_near=3)
+    _compare(root, rows, k, m, got, allow_near=4)
     for b in range(B):
         par = got["out_parent"][b]
         assert got["out_count"][b] == m + 1 and par[0] == -1

@@ -44,6 +44,9 @@
 //  * T = 0 requests: the team splits the rows; argmax (lowest index on ties)
 //    of every row, then the exact-match flags; no draft logits are read.
 #include <math.h>
+#include <stdlib.h>
+
+#include <atomic>
 
 #include "tv_device.hpp"
 #include "tv_internal.hpp"
@@ -66,7 +69,11 @@ constexpr int kSlotWords = 8;            // 64-bit words per (member, parity) ex
 // exchange tag sequence (byte 4), exchange slots from byte 256.
 constexpr size_t kReqSlotsOff = 256;
 constexpr size_t kReqBytes = kReqSlotsOff + size_t(kMaxTeam) * 2 * kSlotWords * sizeof(uint64_t);
-constexpr uint32_t kSpinLimit = 1u << 25;
+static_assert(kReqBytes == kSampleReqBytes, "request block size is part of the workspace contract");
+// A team wait gives up after this many ticks of the 100 MHz real-time
+// counter (0.2 s; a wait that is not stalled lasts microseconds). After one
+// wait has given up, the member skips every later wait and leaves.
+constexpr uint64_t kWaitTicksDefault = 20000000ull;
 
 struct SampleParams {
   const float* t;
@@ -82,6 +89,7 @@ struct SampleParams {
   char* req;  // per-request blocks of kReqBytes
   int B, V, W, max_nodes;
   int with_replacement;  // rule (b): the stage proposal stays q
+  uint64_t wait_ticks;   // team wait limit (real-time counter ticks)
 };
 
 // ---------------------------------------------------------------------------
@@ -186,7 +194,24 @@ struct Team {
   int W;
   int member;
   uint32_t* status;
+  uint64_t wait_ticks;
+  int* s_dead;      // LDS flag: a wait of this member gave up (sticky)
 };
+
+// Bounded wait shared by the team exchange and the greedy barrier: true
+// while the caller should keep polling. Gives up (status bit, LDS flag) once
+// the wait has lasted wait_ticks, or at once when another thread of the
+// member already gave up.
+__device__ inline bool keep_waiting(uint64_t t0, uint64_t ticks, uint32_t* status, int* s_dead) {
+  if (*reinterpret_cast<volatile int*>(s_dead)) return false;
+  if (__builtin_amdgcn_s_memrealtime() - t0 > ticks) {
+    raise_status(status, TV_DEV_TIMEOUT);
+    *reinterpret_cast<volatile int*>(s_dead) = 1;
+    return false;
+  }
+  __builtin_amdgcn_s_sleep(1);
+  return true;
+}
 
 // Word k of this member's payload for the next exchange. Stored
 // device-coherent (agent scope): readers on other CUs poll it.
@@ -204,28 +229,24 @@ __device__ inline void ll_put(Team& tm, int k, uint32_t payload, uint32_t* s_wor
 // (one polling thread per word; bounded spin). A member two exchanges ahead
 // cannot overwrite a slot still being read: it must first have read this
 // member's next words, which are published only after this gather.
-__device__ void ll_gather(Team& tm, int K, uint32_t* s_words) {
-  if (tm.W > 1) {
+__device__ bool ll_gather(Team& tm, int K, uint32_t* s_words) {
+  if (tm.W > 1 && !*reinterpret_cast<volatile int*>(tm.s_dead)) {
     const uint32_t tag = tm.seq + uint32_t(tm.phase) + 1u;
     const int par = (tm.phase + 1) & 1;
     for (int i = threadIdx.x; i < tm.W * K; i += blockDim.x) {
       const int w = i / K;
       const uint64_t* a = tm.slots + (size_t(w) * 2 + par) * kSlotWords + (i - w * K);
       uint64_t x = __hip_atomic_load(const_cast<uint64_t*>(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      uint32_t spins = 0;
-      while (uint32_t(x >> 32) != tag) {
-        if (++spins > kSpinLimit) {
-          raise_status(tm.status, TV_DEV_TIMEOUT);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (uint32_t(x >> 32) != tag && keep_waiting(t0, tm.wait_ticks, tm.status, tm.s_dead))
         x = __hip_atomic_load(const_cast<uint64_t*>(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
       s_words[i] = uint32_t(x);
     }
   }
   __syncthreads();
   tm.phase++;
+  // Uniform over the workgroup: every thread reads the flag after the barrier.
+  return !*reinterpret_cast<volatile int*>(tm.s_dead);
 }
 
 __device__ inline double words_to_double(uint32_t lo, uint32_t hi) {
@@ -250,25 +271,25 @@ struct Barrier {
   uint32_t target;
   int W;
   uint32_t* status;
+  uint64_t wait_ticks;
+  int* s_dead;
 };
 
-__device__ void barrier_sync(Barrier& b) {
+// False (for the whole workgroup) when a wait of this member gave up.
+__device__ bool barrier_sync(Barrier& b) {
   __syncthreads();
   if (b.W > 1) {
     b.target += uint32_t(b.W);
     if (threadIdx.x == 0) {
       __hip_atomic_fetch_add(b.ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-      uint32_t spins = 0;
-      while (__hip_atomic_load(b.ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < b.target) {
-        __builtin_amdgcn_s_sleep(1);
-        if (++spins > kSpinLimit) {
-          raise_status(b.status, TV_DEV_TIMEOUT);
-          break;
-        }
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (__hip_atomic_load(b.ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < b.target &&
+             keep_waiting(t0, b.wait_ticks, b.status, b.s_dead)) {
       }
     }
     __syncthreads();
   }
+  return !*reinterpret_cast<volatile int*>(b.s_dead);
 }
 
 // No member waits after this point, so the reset cannot strand anyone.
@@ -845,7 +866,7 @@ __device__ __attribute__((always_inline)) inline void walk(
                                  : (j == 1 ? uint32_t(__double2loint(dv)) : uint32_t(__double2hiint(dv)));
       ll_put(tm, int(k), wv, L.s_words);
     }
-    ll_gather(tm, 6, L.s_words);
+    if (!ll_gather(tm, 6, L.s_words)) return;  // a wait gave up (status bit set)
     const int nkk = __builtin_amdgcn_readfirstlane(*L.s_nk);
 
     // Team totals, member w in lane w of the first row of every wave (the
@@ -933,7 +954,7 @@ __device__ __attribute__((always_inline)) inline void walk(
       if (threadIdx.x < 2)
         ll_put(tm, int(threadIdx.x),
                threadIdx.x == 0 ? uint32_t(__double2loint(part)) : uint32_t(__double2hiint(part)), L.s_words);
-      ll_gather(tm, 2, L.s_words);
+      if (!ll_gather(tm, 2, L.s_words)) return;
       const double pw = lane < tm.W ? words_to_double(L.s_words[2 * lane], L.s_words[2 * lane + 1]) : 0.0;
       const double F = lane_d(row_sum(pw), 0);
       if (F > 0.0) {
@@ -1116,7 +1137,7 @@ __device__ __attribute__((always_inline)) inline void greedy_rows(const SamplePa
       for (int k = 1; k < 4; ++k) wv = threadIdx.x == k ? w4[k] : wv;
       ll_put(tm, int(threadIdx.x), wv, s_words);
     }
-    ll_gather(tm, 4, s_words);
+    if (!ll_gather(tm, 4, s_words)) return;
     if (last_shared && g0 <= (long long)row_last * C && threadIdx.x == 0) {
       // This member holds the first unit of its last row: fold in the later
       // members that start inside that row.
@@ -1146,7 +1167,7 @@ __global__ __launch_bounds__(kThreads, 4) void sample_kernel(SampleParams p) {
   __shared__ float4 s_res[2 * kLdsCh * kThreads];
   __shared__ float shv[kWaves];
   __shared__ int shi[kWaves];
-  __shared__ int s_nk, s_int;
+  __shared__ int s_nk, s_int, s_dead;
 
   // Team placement: block b runs on XCD b % 8; the W members of a team are
   // consecutive slots of one XCD.
@@ -1156,6 +1177,7 @@ __global__ __launch_bounds__(kThreads, 4) void sample_kernel(SampleParams p) {
   const int member = slot - (slot / p.W) * p.W;
   if (r >= p.B) return;  // padding block: belongs to no team
 
+  if (threadIdx.x == 0) s_dead = 0;
   for (int j = threadIdx.x; j < 64; j += kThreads) tbl[j] = exp2(double(j) / 64.0);
   for (int j = threadIdx.x; j < kZTable; j += kThreads) tblz[j] = exp2(double(j) / double(kZTable));
 
@@ -1199,9 +1221,11 @@ __global__ __launch_bounds__(kThreads, 4) void sample_kernel(SampleParams p) {
   tm.W = p.W;
   tm.member = member;
   tm.status = p.status;
+  tm.wait_ticks = p.wait_ticks;
+  tm.s_dead = &s_dead;
 
   if (T == 0.f) {
-    Barrier bar{reinterpret_cast<uint32_t*>(rq), 0u, p.W, p.status};
+    Barrier bar{reinterpret_cast<uint32_t*>(rq), 0u, p.W, p.status, p.wait_ticks, &s_dead};
     // Greedy exact match: argmax of every row, then the match flags.
     if (vec4) greedy_rows(p, tm, nbeg, N, shv, shi, s_words);
     for (int i = member; !vec4 && i < N; i += p.W) {
@@ -1238,7 +1262,7 @@ __global__ __launch_bounds__(kThreads, 4) void sample_kernel(SampleParams p) {
       }
       __syncthreads();
     }
-    barrier_sync(bar);
+    if (!barrier_sync(bar)) return;  // a wait gave up (status bit set)
     for (int i = member * kThreads + threadIdx.x; i < N; i += p.W * kThreads) {
       int8_t f = 0;
       if (i == 0) {
@@ -1306,29 +1330,68 @@ bool plan_sample(const tv_sample_desc& d, SamplePlan* out) {
 }
 
 namespace {
-int g_coop_blocks_per_cu = -1;
-int g_num_cus = -1;
+
+// Launch facts of one device (resident sample_kernel workgroups per CU, CU
+// count), looked up on the first call made with that device current and
+// kept per device; concurrent first calls compute the same values.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_blocks_per_cu[kMaxDevices];
+std::atomic<int> g_num_cus[kMaxDevices];
+
+hipError_t device_facts(int* blocks_per_cu, int* num_cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int b = g_blocks_per_cu[dev].load(std::memory_order_acquire);
+    const int c = g_num_cus[dev].load(std::memory_order_acquire);
+    if (b > 0 && c > 0) {
+      *blocks_per_cu = b;
+      *num_cus = c;
+      return hipSuccess;
+    }
+  }
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  int per = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, reinterpret_cast<const void*>(sample_kernel),
+                                                   kThreads, 0);
+  if (e != hipSuccess) return e;
+  if (per < 1 || cus < 1) return hipErrorInvalidDevice;
+  if (dev >= 0 && dev < kMaxDevices) {
+    g_blocks_per_cu[dev].store(per, std::memory_order_release);
+    g_num_cus[dev].store(cus, std::memory_order_release);
+  }
+  *blocks_per_cu = per;
+  *num_cus = cus;
+  return hipSuccess;
+}
+
+// Team wait limit: kWaitTicksDefault, or TREEVERIFY_TEAM_WAIT_US
+// microseconds when that variable is set (read once per process).
+uint64_t wait_ticks() {
+  static const uint64_t ticks = []() -> uint64_t {
+    const char* v = getenv("TREEVERIFY_TEAM_WAIT_US");
+    if (!v || !*v) return kWaitTicksDefault;
+    char* end = nullptr;
+    const unsigned long long us = strtoull(v, &end, 10);
+    return (end && *end == 0) ? uint64_t(us) * 100ull : kWaitTicksDefault;
+  }();
+  return ticks;
+}
+
 }  // namespace
 
-hipError_t launch_sample(const tv_sample_desc& d, const SamplePlan& pl, const SampleArgs& a,
-                         hipStream_t stream) {
-  if (g_num_cus < 0) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    hipDeviceProp_t prop;
-    e = hipGetDeviceProperties(&prop, dev);
-    if (e != hipSuccess) return e;
-    int per = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, reinterpret_cast<const void*>(sample_kernel),
-                                                     kThreads, 0);
-    if (e != hipSuccess) return e;
-    g_coop_blocks_per_cu = per;
-    g_num_cus = prop.multiProcessorCount;
-  }
+// One launch of the walk with its status word and per-request blocks given.
+hipError_t launch_sample_core(const tv_sample_desc& d, const SampleArgs& a, uint32_t* status,
+                              char* req, hipStream_t stream) {
+  int per = 0, cus = 0;
+  hipError_t e = device_facts(&per, &cus);
+  if (e != hipSuccess) return e;
   // Team size: as many workgroups per request as stay resident (the
   // launch is cooperative), at most kMaxTeam; a team lives on one XCD.
-  const long resident = long(g_coop_blocks_per_cu) * g_num_cus;
+  const long resident = long(per) * cus;
   int W = int(resident / ((d.batch + 7) / 8 * 8));
   if (W > kMaxTeam) W = kMaxTeam;
   if (W < 1) W = 1;
@@ -1344,14 +1407,14 @@ hipError_t launch_sample(const tv_sample_desc& d, const SamplePlan& pl, const Sa
   p.uniforms = a.uniforms;
   p.flag = a.flag;
   p.next_token = a.next_token;
-  char* ws = static_cast<char*>(a.workspace);
-  p.status = reinterpret_cast<uint32_t*>(ws);
-  p.req = ws + pl.off_req;
+  p.status = status;
+  p.req = req;
   p.B = d.batch;
   p.V = d.vocab;
   p.W = W;
   p.max_nodes = d.max_nodes;
   p.with_replacement = d.rule == TV_RULE_WITH_REPLACEMENT;
+  p.wait_ticks = wait_ticks();
   const dim3 grid(unsigned(grid_for(W))), block(kThreads);
   if (W == 1) {
     hipLaunchKernelGGL(sample_kernel, grid, block, 0, stream, p);
@@ -1360,6 +1423,12 @@ hipError_t launch_sample(const tv_sample_desc& d, const SamplePlan& pl, const Sa
   void* args[] = {&p};
   return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(sample_kernel), grid, block,
                                     args, 0, stream);
+}
+
+hipError_t launch_sample(const tv_sample_desc& d, const SamplePlan& pl, const SampleArgs& a,
+                         hipStream_t stream) {
+  char* ws = static_cast<char*>(a.workspace);
+  return launch_sample_core(d, a, reinterpret_cast<uint32_t*>(ws), ws + pl.off_req, stream);
 }
 
 }  // namespace tv

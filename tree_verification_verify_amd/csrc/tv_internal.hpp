@@ -71,6 +71,13 @@ struct SampleArgs {
 
 hipError_t launch_sample(const tv_sample_desc& d, const SamplePlan& plan, const SampleArgs& a,
                          hipStream_t stream);
+// Bytes of one request's block of sampler synchronisation state (greedy
+// barrier counter, exchange tag sequence, exchange words).
+constexpr size_t kSampleReqBytes = 2304;
+// One launch of the walk with its status word and per-request blocks given
+// (a.workspace unused).
+hipError_t launch_sample_core(const tv_sample_desc& d, const SampleArgs& a, uint32_t* status,
+                              char* req, hipStream_t stream);
 
 hipError_t launch_accept_path(int32_t batch, int32_t max_depth, const int32_t* node_indptr,
                               const int32_t* parent, const int32_t* tokens,
