@@ -1369,16 +1369,14 @@ hipError_t device_facts(int* blocks_per_cu, int* num_cus) {
 }
 
 // Team wait limit: kWaitTicksDefault, or TREEVERIFY_TEAM_WAIT_US
-// microseconds when that variable is set (read once per process).
+// microseconds when that variable is set (a diagnostic: read at every launch,
+// so a test can force waits to give up from the host).
 uint64_t wait_ticks() {
-  static const uint64_t ticks = []() -> uint64_t {
-    const char* v = getenv("TREEVERIFY_TEAM_WAIT_US");
-    if (!v || !*v) return kWaitTicksDefault;
-    char* end = nullptr;
-    const unsigned long long us = strtoull(v, &end, 10);
-    return (end && *end == 0) ? uint64_t(us) * 100ull : kWaitTicksDefault;
-  }();
-  return ticks;
+  const char* v = getenv("TREEVERIFY_TEAM_WAIT_US");
+  if (!v || !*v) return kWaitTicksDefault;
+  char* end = nullptr;
+  const unsigned long long us = strtoull(v, &end, 10);
+  return (end && *end == 0) ? uint64_t(us) * 100ull : kWaitTicksDefault;
 }
 
 }  // namespace
