@@ -14,8 +14,10 @@
  *   - Array arguments are DEVICE pointers unless the name ends in _host.
  *   - The caller owns every buffer, the workspace included. The library never
  *     allocates device memory, never synchronises (tv_device_status aside)
- *     and keeps no per-call state outside the workspace. Host-side argument
- *     errors are returned before anything is launched.
+ *     and keeps no per-call state outside the workspace (the one exception,
+ *     tree_spec_sample_noalloc, uses a fixed device array of the library's
+ *     own). Host-side argument errors are returned before anything is
+ *     launched.
  *   - Calls are stream-ordered and re-entrant; concurrent streams need
  *     distinct workspaces. A workspace must be zero-filled once
  *     (tv_workspace_init) before its first use and then belongs to one
@@ -208,6 +210,30 @@ tv_status tree_spec_sample(const tv_sample_desc* desc,
                            const float* uniforms, int8_t* accept_flag,
                            int32_t* next_token,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* tree_spec_sample for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same computation, arguments and outputs as tree_spec_sample,
+ * without the workspace: the walk's per-request exchange blocks (2304 bytes
+ * each) live in a device array the library owns, sized for
+ * TV_SAMPLE_STATIC_MAX_BATCH requests (2.25 MiB, one copy per GPU, held until
+ * the process ends). Every call first clears the blocks it uses and *status
+ * with a fill kernel; nothing is allocated and nothing is synchronised.
+ *   status: caller-owned device word (4-byte aligned) that receives the
+ *     TV_DEV_* bits of this call. It can be read with tv_device_status
+ *     (passed as the workspace) and passed to tree_accept_path as its
+ *     status_workspace.
+ * desc->batch > TV_SAMPLE_STATIC_MAX_BATCH returns TV_ERR_SHAPE before any
+ * launch. Every call on one GPU uses that GPU's one array: calls that
+ * overlap on one GPU (several streams, or several host threads) race and
+ * their results are undefined; order them on one stream. */
+#define TV_SAMPLE_STATIC_MAX_BATCH 1024
+tv_status tree_spec_sample_noalloc(const tv_sample_desc* desc,
+                                   const float* target_logits, const float* draft_logits,
+                                   const int32_t* tokens, const int32_t* node_indptr,
+                                   const int32_t* parent, const float* temperature,
+                                   const float* uniforms, int8_t* accept_flag,
+                                   int32_t* next_token, uint32_t* status, hipStream_t stream);
 
 /* Longest accepted path ([TreeSpark] §3.2 step 3: commit the longest
  * surviving root path plus one correction/bonus token; §5.1: tau = accepted

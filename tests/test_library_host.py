@@ -215,3 +215,20 @@ def test_construct_host_errors():
         p = list(ptrs)
         p[i] = None
         assert rr(2, 10, 10, 5, *p) == NULL, i
+
+
+def test_noalloc_sampler_host_errors():
+    """Rejected before any launch: a batch above the static array, NULL
+    arguments, a misaligned status word."""
+    lib = tv.library()
+    ptrs = [FAKE] * 9
+    big = tv.sample_desc(_lib.TV_SAMPLE_STATIC_MAX_BATCH + 1, 1000, 8, 4)
+    assert lib.tree_spec_sample_noalloc(ctypes.byref(big), *ptrs, FAKE, None) == SHAPE
+    d = tv.sample_desc(4, 1000, 8, 4)
+    assert lib.tree_spec_sample_noalloc(ctypes.byref(d), *ptrs, None, None) == NULL
+    bad = list(ptrs)
+    bad[0] = None
+    assert lib.tree_spec_sample_noalloc(ctypes.byref(d), *bad, FAKE, None) == NULL
+    assert lib.tree_spec_sample_noalloc(ctypes.byref(d), *ptrs, ctypes.c_void_p(0x100002),
+                                        None) == WORKSPACE
+    assert lib.tree_spec_sample_noalloc(None, *ptrs, FAKE, None) == NULL

@@ -172,6 +172,30 @@ def tree_spec_sample(desc, target_logits, draft_logits, tokens, node_indptr, par
         "tree_spec_sample")
 
 
+def tree_spec_sample_noalloc(desc, target_logits, draft_logits, tokens, node_indptr, parent,
+                             temperature, uniforms, accept_flag, next_token, status, stream=None):
+    """tree_spec_sample with its synchronisation blocks in the library's own
+    device array (no workspace); status is a caller-owned device int32/uint32
+    word that receives the TV_DEV_* bits."""
+    import torch
+    _need(target_logits, "target_logits", torch.float32)
+    if draft_logits is not None:
+        _need(draft_logits, "draft_logits", torch.float32)
+    for t, n in ((tokens, "tokens"), (node_indptr, "node_indptr"), (parent, "parent"),
+                 (next_token, "next_token")):
+        _need(t, n, torch.int32)
+    _need(temperature, "temperature", torch.float32)
+    _need(uniforms, "uniforms", torch.float32)
+    _need(accept_flag, "accept_flag", torch.int8)
+    _need(status, "status", None)
+    if target_logits.dim() != 2 or target_logits.shape[1] != desc.vocab:
+        raise ValueError("target_logits must be [T][V]")
+    _check(_lib.load().tree_spec_sample_noalloc(
+        ctypes.byref(desc), _ptr(target_logits), _ptr(draft_logits), _ptr(tokens),
+        _ptr(node_indptr), _ptr(parent), _ptr(temperature), _ptr(uniforms), _ptr(accept_flag),
+        _ptr(next_token), _ptr(status), _stream(stream)), "tree_spec_sample_noalloc")
+
+
 def tree_accept_path(batch, max_depth, node_indptr, parent, tokens, accept_flag, next_token,
                      prefix_len, path_nodes, out_tokens, out_len, kv_keep,
                      status_workspace=None, stream=None):

@@ -33,11 +33,13 @@ class SampleDesc(ctypes.Structure):
 
 TV_RULE_WITHOUT_REPLACEMENT = 0
 TV_RULE_WITH_REPLACEMENT = 1
+TV_SAMPLE_STATIC_MAX_BATCH = 1024
 
 
 EXPORTS = [
     "tv_attn_workspace_size", "tv_sample_workspace_size", "tv_workspace_init",
-    "tv_device_status", "tree_verify_attn", "tree_spec_sample", "tree_accept_path",
+    "tv_device_status", "tree_verify_attn", "tree_spec_sample", "tree_spec_sample_noalloc",
+    "tree_accept_path",
     "tree_kv_commit", "tree_draw_siblings", "tree_expand_step", "tree_rerank",
     "tv_expand_workspace_size",
     "tv_tree_meta", "tv_validate_tree", "tv_validate_pages", "tv_status_string",
@@ -68,6 +70,7 @@ def load():
         "tv_device_status": (st, [P, P, ctypes.POINTER(ctypes.c_uint32)]),
         "tree_verify_attn": (st, [ctypes.POINTER(AttnDesc)] + [P] * 9 + [P, S, P]),
         "tree_spec_sample": (st, [ctypes.POINTER(SampleDesc)] + [P] * 9 + [P, S, P]),
+        "tree_spec_sample_noalloc": (st, [ctypes.POINTER(SampleDesc)] + [P] * 9 + [P, P]),
         "tree_accept_path": (st, [I32, I32] + [P] * 10 + [P, P]),
         "tree_kv_commit": (st, [ctypes.POINTER(AttnDesc), I32, ctypes.c_int64] + [P] * 7
                            + [I32, P, P]),

@@ -124,6 +124,27 @@ tv_status tree_spec_sample(const tv_sample_desc* desc, const float* target_logit
   return TV_OK;
 }
 
+tv_status tree_spec_sample_noalloc(const tv_sample_desc* desc, const float* target_logits,
+                                   const float* draft_logits, const int32_t* tokens,
+                                   const int32_t* node_indptr, const int32_t* parent,
+                                   const float* temperature, const float* uniforms,
+                                   int8_t* accept_flag, int32_t* next_token, uint32_t* status,
+                                   hipStream_t stream) {
+  if (!desc) return TV_ERR_NULL;
+  tv::SamplePlan pl;
+  if (!tv::plan_sample(*desc, &pl)) return TV_ERR_SHAPE;
+  if (desc->batch > TV_SAMPLE_STATIC_MAX_BATCH) return TV_ERR_SHAPE;
+  if (!target_logits || !tokens || !node_indptr || !parent || !temperature || !uniforms ||
+      !accept_flag || !next_token || !status)
+    return TV_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(status) & 3u) != 0) return TV_ERR_WORKSPACE;
+  tv::SampleArgs a{target_logits, draft_logits, tokens, node_indptr, parent, temperature,
+                   uniforms, accept_flag, next_token, nullptr};
+  hipError_t e = tv::launch_sample_static(*desc, a, status, stream);
+  if (e != hipSuccess) return hip_fail(e, "tree_spec_sample_noalloc");
+  return TV_OK;
+}
+
 tv_status tree_accept_path(int32_t batch, int32_t max_depth, const int32_t* node_indptr,
                            const int32_t* parent, const int32_t* tokens,
                            const int8_t* accept_flag, const int32_t* next_token,

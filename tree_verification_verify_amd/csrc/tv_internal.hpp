@@ -78,6 +78,10 @@ constexpr size_t kSampleReqBytes = 2304;
 // (a.workspace unused).
 hipError_t launch_sample_core(const tv_sample_desc& d, const SampleArgs& a, uint32_t* status,
                               char* req, hipStream_t stream);
+// The walk with its per-request blocks in the library's static device array
+// (cleared first) and its status bits in *status.
+hipError_t launch_sample_static(const tv_sample_desc& d, const SampleArgs& a, uint32_t* status,
+                                hipStream_t stream);
 
 hipError_t launch_accept_path(int32_t batch, int32_t max_depth, const int32_t* node_indptr,
                               const int32_t* parent, const int32_t* tokens,
