@@ -4,7 +4,9 @@ Plain, slow, obviously-correct NumPy (fp64) definitions of what the hot path
 computes: tree metadata, tree-masked attention over a paged prefix, the
 multi-step speculative-sampling walk with siblings drawn without replacement,
 longest-accepted-path selection, the commit of the accepted path's K/V, and
-the draw of a node's children without replacement (Gumbel-top-k). Each function cites the passage of the
+the draw of a node's children without replacement (Gumbel-top-k), and
+the draft-tree constructions (EAGLE-2 expansion and rerank; TreeSpark's
+best-first expansion with the calibrated theta stop). Each function cites the passage of the
 source pages it follows:
 
   [survey]    "Tree-based speculative decoding: draft trees win latency, lose
@@ -27,6 +29,7 @@ from .commit import BadKeepList, check_keep, kv_commit_layer, kv_commit
 from .siblings import philox4x32_10, draw_children, tree_draw_siblings
 from .enumerate import enumerate_node_laws
 from . import construct
+from . import treespark
 
 __all__ = [
     "check_tree", "depths", "ancestors_or_self", "children", "ancestor_bitsets",
@@ -36,5 +39,5 @@ __all__ = [
     "tree_spec_sample", "accept_path_request", "tree_accept_path",
     "BadKeepList", "check_keep", "kv_commit_layer", "kv_commit",
     "philox4x32_10", "draw_children", "tree_draw_siblings",
-    "enumerate_node_laws", "construct",
+    "enumerate_node_laws", "construct", "treespark",
 ]

@@ -13,7 +13,7 @@ from .trees import (expansion_vector_tree, random_tree, chain_tree, star_tree,
                     relabel_dfs, tree_depths)
 from .inputs import (make_attention_inputs, make_sampler_inputs, make_construct_inputs,
                      gumbel_topk_tokens, independent_draw_tokens, AttentionInputs,
-                     SamplerInputs)
+                     SamplerInputs, SparkInputs, make_spark_inputs)
 from .configs import CONFIGS, make_config, Config
 
 __all__ = [
@@ -22,5 +22,6 @@ __all__ = [
     "eagle2_tree", "bfs_renumber", "relabel_random_topological", "relabel_dfs",
     "tree_depths", "make_attention_inputs", "make_sampler_inputs", "make_construct_inputs",
     "gumbel_topk_tokens", "independent_draw_tokens", "AttentionInputs", "SamplerInputs",
+    "SparkInputs", "make_spark_inputs",
     "CONFIGS", "make_config", "Config",
 ]

@@ -260,3 +260,59 @@ def make_construct_inputs(rng, batch, vocab, k, rounds, sigma=2.0, integer_level
         root = _normal_f32(rng, (batch, vocab), scale=sigma)
         rows = _normal_f32(rng, shape_rows, scale=sigma)
     return root, rows
+
+
+@dataclass
+class SparkInputs:
+    """Inputs of TreeSpark's best-first construction (one drafter backbone
+    pass per request plus the shared Markov head)."""
+    base_logits: np.ndarray   # float32 [B][depths][V]: U_1..U_b of each request
+    w1: np.ndarray            # uint16 bf16 bits [V][r]
+    w2: np.ndarray            # uint16 bf16 bits [V][r]
+    anchor: np.ndarray        # int32 [B]: the root (last committed) token
+    temperature: np.ndarray   # float32 [B]
+    theta: np.ndarray         # float32 [B]
+
+    @property
+    def batch(self):
+        return self.base_logits.shape[0]
+
+    @property
+    def depths(self):
+        return self.base_logits.shape[1]
+
+    @property
+    def vocab(self):
+        return self.base_logits.shape[2]
+
+    @property
+    def rank(self):
+        return self.w1.shape[1]
+
+
+def make_spark_inputs(rng, batch, vocab=151936, depths=7, rank=256, temperatures=0.0,
+                      thetas=0.05, scale_range=(4.0, 8.0), w_sigma=0.3):
+    """Synthetic drafter output of TreeSpark's shape (block of b = 7 depths,
+    Markov head of rank r = 256 over V = 151936): base logits
+    U ~ s_r N(0, 1) with a per-request scale s_r ~ U(scale_range) (confident
+    and diffuse rounds side by side), Markov factors W1, W2 ~ N(0, w_sigma)
+    stored as bf16. temperatures / thetas: a value for every request or a
+    per-request sequence."""
+    V, r = int(vocab), int(rank)
+    scales = rng.uniform(scale_range[0], scale_range[1], size=batch).astype(np.float32)
+    U = _normal_f32(rng, (batch, depths, V))
+    U *= scales[:, None, None]
+    w1 = _normal_bf16_scaled(rng, (V, r), w_sigma)
+    w2 = _normal_bf16_scaled(rng, (V, r), w_sigma)
+    anchor = rng.integers(0, V, size=batch).astype(np.int32)
+    temps = np.broadcast_to(np.asarray(temperatures, np.float32), (batch,)).copy()
+    ths = np.broadcast_to(np.asarray(thetas, np.float32), (batch,)).copy()
+    return SparkInputs(base_logits=U, w1=w1, w2=w2, anchor=anchor, temperature=temps, theta=ths)
+
+
+def _normal_bf16_scaled(rng, shape, sigma, chunk=1 << 24):
+    out = np.empty(int(np.prod(shape)), dtype=np.uint16)
+    for s in range(0, out.size, chunk):
+        e = min(out.size, s + chunk)
+        out[s:e] = f32_to_bf16_bits(rng.standard_normal(e - s, dtype=np.float32) * np.float32(sigma))
+    return out.reshape(shape)
