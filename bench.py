@@ -432,6 +432,65 @@ def construct_bench(reps, batch=64, vocab=151936, k=10, rounds=6, m=60):
         "trees_per_s": batch / (total * 1e-6)}), flush=True)
 
 
+def spark_bench(reps, batch=64, vocab=151936, rank=256, depths=7, N=64, K=8, theta=0.05,
+                temps=("mixed",)):
+    """TreeSpark's best-first construction alone (tree_spark_build): the pages'
+    drafter shape (b = 7, r = 256, V = 151936, K = 8, node cap 64) for a
+    64-request batch at theta, with synthetic backbone logits and Markov
+    factors resident in HBM. Algorithmic bytes per call: w2 once per round
+    (V r 2 B) plus, per expansion, its base-logit row (4 V B) and w1 row;
+    the logits row each expansion writes and reads back is not counted."""
+    import torch
+    import tree_verification_verify_amd as tv
+    from workloads import make_spark_inputs
+    for tsel in temps:
+        rng = np.random.default_rng(4242)
+        t = [0.0, 0.5, 1.0] * (batch // 3 + 1) if tsel == "mixed" else [float(tsel)] * batch
+        inp = make_spark_inputs(rng, batch, vocab=vocab, depths=depths, rank=rank,
+                                temperatures=np.asarray(t[:batch], np.float32), thetas=theta)
+        dev = "cuda"
+        desc = tv.spark_desc(batch, vocab, rank, depths, N, K)
+        ws = tv.alloc_workspace(tv.spark_workspace_size(desc))
+        U = torch.from_numpy(inp.base_logits).to(dev)
+        w1 = torch.from_numpy(inp.w1.view(np.int16)).to(dev).view(torch.bfloat16)
+        w2 = torch.from_numpy(inp.w2.view(np.int16)).to(dev).view(torch.bfloat16)
+        anchor = torch.from_numpy(inp.anchor).to(dev)
+        temp = torch.from_numpy(inp.temperature).to(dev)
+        th = torch.from_numpy(inp.theta).to(dev)
+        par = torch.empty((batch, N + 1), dtype=torch.int32, device=dev)
+        tok = torch.empty_like(par)
+        cnt = torch.empty(batch, dtype=torch.int32, device=dev)
+        call = lambda: tv.tree_spark_build(desc, U, w1, w2, anchor, temp, th, par, tok, cnt, ws,
+                                           seed=7)
+        call()
+        torch.cuda.synchronize()
+        status, bits = tv.device_status(ws)
+        if status != 0:
+            raise SystemExit(f"device status {status} bits {bits}")
+        diag = ws[8:16].view(torch.int32).cpu().numpy()
+        rounds, expanded = int(diag[0]), int(diag[1])
+        stream = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            call()
+            b.record(stream)
+        torch.cuda.synchronize()
+        us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+        nodes = int(cnt.sum().item()) - batch
+        abytes = rounds * vocab * rank * 2 + expanded * (vocab * 4 + rank * 2)
+        print(json.dumps({
+            "kernel": "tree_spark_build (spark_kernel: select, bf16 MFMA logits, statistics)",
+            "workload": f"TreeSpark construction: {batch} requests, T {tsel}, theta {theta}, "
+                        f"b {depths}, r {rank}, V {vocab}, K {K}, cap {N}",
+            "us_median": us, "reps": reps, "rounds": rounds, "expanded_rows": expanded,
+            "drafted_nodes": nodes, "trees_per_s": batch / (us * 1e-6),
+            "nodes_per_s": nodes / (us * 1e-6), "us_per_round": us / max(rounds, 1),
+            "algorithmic_bytes": abytes, "hbm_GBs": abytes / (us * 1e-6) / 1e9,
+            "hbm_frac": abytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -453,6 +512,8 @@ def main():
                          "the with-replacement rule")
     ap.add_argument("--construct-bench", action="store_true",
                     help="time the EAGLE-2 construction (expansion rounds + rerank) alone")
+    ap.add_argument("--spark-bench", action="store_true",
+                    help="time TreeSpark's best-first construction alone")
     ap.add_argument("--siblings-bench", action="store_true",
                     help="time tree_draw_siblings alone on the highload trees' expansions")
     ap.add_argument("--commit-bench", type=int, default=0, metavar="LAYERS",
@@ -466,6 +527,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.spark_bench:
+        spark_bench(max(1, args.steps), temps=("0", "1", "mixed"))
+        return
     if args.siblings_bench:
         siblings_bench(max(1, args.steps))
         return

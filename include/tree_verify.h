@@ -369,6 +369,59 @@ tv_status tree_rerank(int32_t batch, int32_t num_cand, int32_t cand_capacity, in
                       const int32_t* cand_parent, int32_t* out_parent, int32_t* out_token,
                       int32_t* out_count, void* status_workspace, hipStream_t stream);
 
+/* TreeSpark's best-first draft-tree construction with the calibrated theta
+ * stop ([TreeSpark] §3.1-§3.5). The drafter's backbone gives each request
+ * base logits U_1..U_b (one row per depth) and a shared rank-r Markov head
+ * B(x, v) = <w1[x], w2[v]>; a node at depth d carrying token x has children
+ * from q0 = softmax(U_{d+1} + B(x, .)) (§3.2 step 1). Slots (a node's next
+ * child) are keyed by calibrated path survival, the sum of
+ * log p_hat(q0) = log sigma(a logit(q0) + b) along the root path (§1, §3.4):
+ * the most probable unused token at T == 0; at T > 0 the slot is keyed by
+ * the admissible pre-draw bound S(v) p_hat(max unused q0) and its token is
+ * the node's next draw without replacement from q_T = softmax(l / T)
+ * (Gumbel-top-k with the Philox4x32-10 noise of tree_draw_siblings, counter
+ * (y/4, request * (max_nodes+1) + node, stream_id, 0), key seed). The best
+ * slot is materialised first (ties: the lower node index); a node opens its
+ * first-child slot (below depth b) and its parent's next-sibling slot (up to
+ * max_siblings children); expansion stops when the best key falls below
+ * log theta[r] (theta 0: never) or the tree holds max_nodes drafted nodes
+ * (§3.5). The result equals one-slot-at-a-time best-first expansion.
+ *   base_logits [B][depths][V] fp32; w1, w2 [V][rank] bf16 (row-major);
+ *   anchor [B] int32 (the root's token); temperature, theta [B] fp32.
+ *   out_parent, out_token [B][max_nodes+1] int32: the root (parent -1,
+ *     token -1) then the nodes in materialisation order (topological,
+ *     siblings in draw order), -1 past out_count[b] = 1 + drafted nodes;
+ *     out_logsurv [B][max_nodes+1] fp32 log path survival (may be NULL).
+ *   workspace: tv_spark_workspace_size bytes, 256-byte aligned, zero-filled
+ *     once (tv_workspace_init); it holds the status word and the state kept
+ *     between calls; calls that share it must not overlap. After a call,
+ *     its uint32 words 2 and 3 hold the rounds run and the rows expanded
+ *     (each round reads w2 once and the base-logit row of every expansion).
+ * Logits are formed by bf16 matrix products with fp32 accumulation, the
+ * log-sum-exp in fp32 combined in fp64, the calibration in fp64: decisions
+ * agree with an fp64 evaluation except where two keys, two logits or two
+ * draw scores lie within ~1e-5. Non-finite logits set TV_DEV_LOGITS, an
+ * anchor outside [0, V) TV_DEV_SHAPE. */
+typedef struct {
+  int32_t batch;         /* B, 1..256 */
+  int32_t vocab;         /* V >= max_siblings + 1 */
+  int32_t rank;          /* r: a multiple of 32, at most 256 */
+  int32_t depths;        /* b: base-logit rows per request, 1..16 */
+  int32_t max_nodes;     /* N: drafted nodes per tree, 1..64 */
+  int32_t max_siblings;  /* K: children per node, 1..16 */
+  float calib_a;         /* p_hat = sigma(calib_a logit(q0) + calib_b); */
+  float calib_b;         /* the pages' fit: 0.67, -0.46 */
+} tv_spark_desc;
+
+size_t tv_spark_workspace_size(const tv_spark_desc* desc);
+
+tv_status tree_spark_build(const tv_spark_desc* desc, const float* base_logits,
+                           const void* w1, const void* w2, const int32_t* anchor,
+                           const float* temperature, const float* theta,
+                           uint32_t stream_id, uint64_t seed, int32_t* out_parent,
+                           int32_t* out_token, int32_t* out_count, float* out_logsurv,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Tree metadata ([TreeSpark] §3.2 step 3 and §4: per-depth position ids and
  * ancestor bitmasks). For every row: depth (edges from the root),
  * anc_bits [T][ceil(max_nodes/32)] (bit j of word j/32 set iff j is an

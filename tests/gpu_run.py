@@ -96,3 +96,33 @@ def run_construct(root, rows, k, m, num_rounds=None, bad_frontier=None, split=Tr
                 frontiers=[f.cpu().numpy() for f in frontiers], out_parent=op.cpu().numpy(),
                 out_token=ot.cpu().numpy(), out_count=oc.cpu().numpy(), status=st, bits=bits,
                 num_cand=off)
+
+
+def run_spark(inp, N, K, stream_id=0, seed=0, ws=None, repeat=1, a=0.67, b=-0.46):
+    """TreeSpark construction on the GPU; returns dict of numpy outputs."""
+    import torch
+    import tree_verification_verify_amd as tv
+    dev = "cuda"
+    B = inp.batch
+    desc = tv.spark_desc(B, inp.vocab, inp.rank, inp.depths, N, K, a, b)
+    if ws is None:
+        ws = tv.alloc_workspace(tv.spark_workspace_size(desc))
+    U = torch.from_numpy(np.ascontiguousarray(inp.base_logits)).to(dev)
+    w1 = torch.from_numpy(inp.w1.view(np.int16)).to(dev).view(torch.bfloat16)
+    w2 = torch.from_numpy(inp.w2.view(np.int16)).to(dev).view(torch.bfloat16)
+    anchor = torch.from_numpy(inp.anchor).to(dev)
+    temp = torch.from_numpy(inp.temperature).to(dev)
+    theta = torch.from_numpy(inp.theta).to(dev)
+    outs = []
+    for _ in range(repeat):
+        par = torch.full((B, N + 1), -7, dtype=torch.int32, device=dev)
+        tok = torch.full_like(par, -7)
+        cnt = torch.full((B,), -7, dtype=torch.int32, device=dev)
+        logs = torch.full((B, N + 1), float("nan"), dtype=torch.float32, device=dev)
+        tv.tree_spark_build(desc, U, w1, w2, anchor, temp, theta, par, tok, cnt, ws,
+                            out_logsurv=logs, stream_id=stream_id, seed=seed)
+        outs.append(dict(parent=par.cpu().numpy(), token=tok.cpu().numpy(),
+                         count=cnt.cpu().numpy(), logS=logs.cpu().numpy()))
+    st, bits = tv.device_status(ws)
+    res = outs if repeat > 1 else outs[0]
+    return res, st, bits

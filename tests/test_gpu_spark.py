@@ -1,0 +1,106 @@
+"""GPU parity: tree_spark_build (TreeSpark's best-first construction with the
+calibrated theta stop, HIP, via the C ABI) against the fp64 oracle. Trees
+(parents, tokens, node counts) are compared exactly and log survivals within
+1e-4; a request whose oracle has a decision within EPS (a key against the
+runner-up or theta, or a token order among an expanded node's K+1 best) is
+excluded and counted against an allowance equal to the oracle's own count."""
+import numpy as np
+import pytest
+
+import oracle.treespark as TS
+from workloads import make_spark_inputs
+
+pytestmark = pytest.mark.gpu
+
+EPS = 1e-4
+
+
+def _run(*a, **kw):
+    from gpu_run import run_spark
+    return run_spark(*a, **kw)
+
+
+def _compare(inp, got, N, K, seed=0, stream_id=0, requests=None, a=0.67, b=-0.46):
+    res = TS.build_batch(inp.base_logits, inp.w1, inp.w2, inp.anchor, inp.temperature, inp.theta,
+                         N, K, a, b, seed=seed, stream=stream_id, requests=requests)
+    near = 0
+    for idx, ref in zip(requests if requests is not None else range(inp.batch), res):
+        if TS.near(ref["log"], EPS):
+            near += 1
+            continue
+        n = len(ref["parent"])
+        assert got["count"][idx] == n, (idx, got["count"][idx], n)
+        np.testing.assert_array_equal(got["parent"][idx, :n], ref["parent"], err_msg=f"request {idx}")
+        np.testing.assert_array_equal(got["token"][idx, :n], ref["token"], err_msg=f"request {idx}")
+        np.testing.assert_allclose(got["logS"][idx, :n], ref["logS"], rtol=0, atol=1e-4)
+        assert (got["parent"][idx, n:] == -1).all() and (got["token"][idx, n:] == -1).all()
+    total = len(res)
+    return near, total
+
+
+@pytest.mark.parametrize("V,r,depths,N,K,temps,thetas", [
+    (64, 32, 3, 10, 4, 0.0, 0.0),
+    (1001, 64, 4, 30, 3, [0.0, 0.5, 1.0, 2.0], 0.02),
+    (4099, 256, 7, 64, 8, [0.0, 1.0], [0.0, 0.05, 0.15]),
+    (4096, 128, 1, 16, 16, 1.0, 0.0),
+    (2048, 256, 7, 64, 1, [0.0, 0.5], 0.01),
+    (300, 32, 5, 1, 4, 0.7, 0.0),
+])
+def test_random_shapes(V, r, depths, N, K, temps, thetas):
+    rng = np.random.default_rng(V + N + K)
+    B = 6
+    t = np.resize(np.asarray(temps, np.float32), B)
+    th = np.resize(np.asarray(thetas, np.float32), B)
+    inp = make_spark_inputs(rng, B, vocab=V, depths=depths, rank=r, temperatures=t, thetas=th,
+                            scale_range=(2.0, 6.0))
+    got, st, bits = _run(inp, N, K, seed=11, stream_id=3)
+    assert st == 0, (st, bits)
+    near, total = _compare(inp, got, N, K, seed=11, stream_id=3)
+    assert near == 0, near   # the oracle finds no near decision in these inputs
+
+
+@pytest.mark.parametrize("T,near_seen", [(0.0, 1), (1.0, 0)])
+def test_full_vocab_batch(T, near_seen):
+    """The pages' drafter shape (b = 7, r = 256, V = 151936, K = 8, node cap
+    64) for a 64-request batch at theta = 0.05; every request compared (the
+    oracle finds near_seen near decisions among them)."""
+    rng = np.random.default_rng(77 + int(T))
+    inp = make_spark_inputs(rng, 64, temperatures=T, thetas=0.05)
+    got, st, bits = _run(inp, 64, 8, seed=5)
+    assert st == 0, (st, bits)
+    near, total = _compare(inp, got, 64, 8, seed=5)
+    assert near == near_seen, near
+    assert (got["count"] >= 1).all() and (got["count"] <= 65).all()
+
+
+def test_full_vocab_fixed_budget():
+    """theta = 0: every tree grows to the 64-node cap (the most rounds), T
+    mixed over the batch."""
+    rng = np.random.default_rng(91)
+    inp = make_spark_inputs(rng, 12, temperatures=[0.0, 0.5, 1.0] * 4, thetas=0.0)
+    got, st, bits = _run(inp, 64, 8, seed=8, stream_id=1)
+    assert st == 0, (st, bits)
+    assert (got["count"] == 65).all()
+    near, total = _compare(inp, got, 64, 8, seed=8, stream_id=1)
+    assert near == 2, near   # the oracle's own count for these inputs
+
+
+def test_repeat_and_workspace_reuse_are_identical():
+    rng = np.random.default_rng(5)
+    inp = make_spark_inputs(rng, 8, vocab=8192, temperatures=[0.0, 1.0] * 4, thetas=0.02)
+    (a, b), st, bits = _run(inp, 40, 6, repeat=2, seed=2)
+    assert st == 0, (st, bits)
+    for k in ("parent", "token", "count"):
+        np.testing.assert_array_equal(a[k], b[k])
+
+
+def test_bad_anchor_and_nonfinite_logits_are_reported():
+    rng = np.random.default_rng(6)
+    inp = make_spark_inputs(rng, 3, vocab=512, rank=32, temperatures=0.0, thetas=0.0)
+    inp.anchor[1] = 100000
+    _, st, bits = _run(inp, 8, 4)
+    assert bits & (1 << 5)
+    inp = make_spark_inputs(rng, 3, vocab=512, rank=32, temperatures=1.0, thetas=0.0)
+    inp.base_logits[0, 0, 7] = np.nan
+    _, st, bits = _run(inp, 8, 4)
+    assert bits & (1 << 2)

@@ -323,6 +323,47 @@ def tree_rerank(num_cand, m, cand_value, cand_token, cand_parent, out_parent, ou
         _stream(stream)), "tree_rerank")
 
 
+def spark_desc(batch, vocab, rank, depths, max_nodes, max_siblings, calib_a=0.67, calib_b=-0.46):
+    return _lib.SparkDesc(batch, vocab, rank, depths, max_nodes, max_siblings, calib_a, calib_b)
+
+
+def spark_workspace_size(desc):
+    n = _lib.load().tv_spark_workspace_size(ctypes.byref(desc))
+    if n == 0:
+        raise TVError(2, "tv_spark_workspace_size")
+    return n
+
+
+def tree_spark_build(desc, base_logits, w1, w2, anchor, temperature, theta, out_parent, out_token,
+                     out_count, workspace, out_logsurv=None, stream_id=0, seed=0, stream=None):
+    """TreeSpark best-first construction; w1, w2 are bf16 [V][rank]."""
+    import torch
+    _need(base_logits, "base_logits", torch.float32)
+    _need(w1, "w1", torch.bfloat16)
+    _need(w2, "w2", torch.bfloat16)
+    for t, n in ((anchor, "anchor"), (out_parent, "out_parent"), (out_token, "out_token"),
+                 (out_count, "out_count")):
+        _need(t, n, torch.int32)
+    _need(temperature, "temperature", torch.float32)
+    _need(theta, "theta", torch.float32)
+    _need(workspace, "workspace", torch.uint8)
+    if out_logsurv is not None:
+        _need(out_logsurv, "out_logsurv", torch.float32)
+    B, W = desc.batch, desc.max_nodes + 1
+    if tuple(base_logits.shape) != (B, desc.depths, desc.vocab):
+        raise ValueError("base_logits must be [B][depths][V]")
+    if tuple(w1.shape) != (desc.vocab, desc.rank) or tuple(w2.shape) != (desc.vocab, desc.rank):
+        raise ValueError("w1, w2 must be [V][rank]")
+    for t in (out_parent, out_token) + ((out_logsurv,) if out_logsurv is not None else ()):
+        if t.numel() != B * W:
+            raise ValueError("tree outputs must be [B][max_nodes+1]")
+    _check(_lib.load().tree_spark_build(
+        ctypes.byref(desc), _ptr(base_logits), _ptr(w1), _ptr(w2), _ptr(anchor),
+        _ptr(temperature), _ptr(theta), ctypes.c_uint32(stream_id), ctypes.c_uint64(seed),
+        _ptr(out_parent), _ptr(out_token), _ptr(out_count), _ptr(out_logsurv),
+        _ptr(workspace), workspace.numel(), _stream(stream)), "tree_spark_build")
+
+
 def tv_tree_meta(batch, max_nodes, node_indptr, parent, depth=None, anc_bits=None,
                  first_child=None, next_sibling=None, status_workspace=None, stream=None):
     import torch

@@ -31,6 +31,13 @@ class SampleDesc(ctypes.Structure):
                 ("rule", ctypes.c_int32)]
 
 
+class SparkDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("vocab", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("depths", ctypes.c_int32), ("max_nodes", ctypes.c_int32),
+                ("max_siblings", ctypes.c_int32), ("calib_a", ctypes.c_float),
+                ("calib_b", ctypes.c_float)]
+
+
 TV_RULE_WITHOUT_REPLACEMENT = 0
 TV_RULE_WITH_REPLACEMENT = 1
 TV_SAMPLE_STATIC_MAX_BATCH = 1024
@@ -41,7 +48,7 @@ EXPORTS = [
     "tv_device_status", "tree_verify_attn", "tree_spec_sample", "tree_spec_sample_noalloc",
     "tree_accept_path",
     "tree_kv_commit", "tree_draw_siblings", "tree_expand_step", "tree_rerank",
-    "tv_expand_workspace_size",
+    "tv_expand_workspace_size", "tv_spark_workspace_size", "tree_spark_build",
     "tv_tree_meta", "tv_validate_tree", "tv_validate_pages", "tv_status_string",
     "tv_last_hip_error", "tv_version",
 ]
@@ -80,6 +87,9 @@ def load():
         "tv_expand_workspace_size": (ctypes.c_size_t, [I32, I32, I32]),
         "tree_rerank": (st, [I32, I32, I32, I32, P, P, P, P, P, P, P, P]),
         "tv_tree_meta": (st, [I32, I32] + [P] * 6 + [P, P]),
+        "tv_spark_workspace_size": (S, [ctypes.POINTER(SparkDesc)]),
+        "tree_spark_build": (st, [ctypes.POINTER(SparkDesc)] + [P] * 6
+                             + [ctypes.c_uint32, ctypes.c_uint64] + [P] * 4 + [P, S, P]),
         "tv_validate_tree": (st, [I32, P, P, I32, I32]),
         "tv_validate_pages": (st, [I32, P, P, P, P, I32, I32]),
         "tv_status_string": (ctypes.c_char_p, [st]),

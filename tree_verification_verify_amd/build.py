@@ -15,7 +15,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libtreeverify.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["tree_attn.hip", "tree_sample.hip", "tree_sample_noalloc.hip", "tree_path.hip", "tree_commit.hip", "tree_siblings.hip",
-           "tree_construct.hip", "api.cpp"]
+           "tree_construct.hip", "tree_spark.hip", "api.cpp"]
 ARCH = "gfx950"
 # Per-source extra flags. The attention kernels are scheduled for ILP (LDS
 # operand loads batched ahead of their MFMAs); their occupancy is fixed by

@@ -244,6 +244,44 @@ tv_status tree_rerank(int32_t batch, int32_t num_cand, int32_t cand_capacity, in
   return TV_OK;
 }
 
+namespace {
+bool spark_desc_ok(const tv_spark_desc& d) {
+  return d.batch >= 1 && d.batch <= tv::kSparkMaxBatch && d.max_siblings >= 1 &&
+         d.max_siblings <= tv::kSparkMaxSiblings && d.vocab >= d.max_siblings + 1 && d.rank >= 32 &&
+         d.rank <= 256 && d.rank % 32 == 0 && d.depths >= 1 && d.depths <= tv::kSparkMaxDepths &&
+         d.max_nodes >= 1 && d.max_nodes <= tv::kSparkMaxNodes && d.calib_a == d.calib_a &&
+         d.calib_b == d.calib_b;
+}
+}  // namespace
+
+size_t tv_spark_workspace_size(const tv_spark_desc* desc) {
+  if (!desc || !spark_desc_ok(*desc)) return 0;
+  return tv::spark_workspace_bytes(*desc);
+}
+
+tv_status tree_spark_build(const tv_spark_desc* desc, const float* base_logits, const void* w1,
+                           const void* w2, const int32_t* anchor, const float* temperature,
+                           const float* theta, uint32_t stream_id, uint64_t seed,
+                           int32_t* out_parent, int32_t* out_token, int32_t* out_count,
+                           float* out_logsurv, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  if (!desc) return TV_ERR_NULL;
+  if (!spark_desc_ok(*desc)) return TV_ERR_SHAPE;
+  if (!base_logits || !w1 || !w2 || !anchor || !temperature || !theta || !out_parent ||
+      !out_token || !out_count || !workspace)
+    return TV_ERR_NULL;
+  if (workspace_bytes < tv::spark_workspace_bytes(*desc) || !aligned256(workspace))
+    return TV_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(w1) & 15u) || (reinterpret_cast<uintptr_t>(w2) & 15u) ||
+      (reinterpret_cast<uintptr_t>(base_logits) & 15u))
+    return TV_ERR_SHAPE;
+  tv::SparkArgs a{base_logits, w1, w2, anchor, temperature, theta, stream_id, seed,
+                  out_parent, out_token, out_count, out_logsurv, workspace};
+  hipError_t e = tv::launch_spark(*desc, a, stream);
+  if (e != hipSuccess) return hip_fail(e, "tree_spark_build");
+  return TV_OK;
+}
+
 tv_status tv_tree_meta(int32_t batch, int32_t max_nodes, const int32_t* node_indptr,
                        const int32_t* parent, int32_t* depth, uint32_t* anc_bits,
                        int32_t* first_child, int32_t* next_sibling, void* status_workspace,

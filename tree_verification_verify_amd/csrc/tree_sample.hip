@@ -283,9 +283,12 @@ __device__ bool barrier_sync(Barrier& b) {
     if (threadIdx.x == 0) {
       __hip_atomic_fetch_add(b.ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
       const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-      while (__hip_atomic_load(b.ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < b.target &&
+      // Poll with relaxed loads (an acquire load invalidates the XCD's L2 on
+      // every poll, evicting the other teams' rows); one acquire fence after.
+      while (__hip_atomic_load(b.ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < b.target &&
              keep_waiting(t0, b.wait_ticks, b.status, b.s_dead)) {
       }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     __syncthreads();
   }

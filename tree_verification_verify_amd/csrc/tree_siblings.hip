@@ -25,6 +25,7 @@
 // by k rounds of a block argmax.
 #include "tv_device.hpp"
 #include "tv_internal.hpp"
+#include "tv_philox.hpp"
 
 namespace tv {
 
@@ -42,21 +43,6 @@ struct SibParams {
   int rows, vocab;
   uint32_t stream, key0, key1;
 };
-
-__device__ inline uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
-#pragma unroll
-  for (int i = 0; i < 10; ++i) {
-    if (i) {
-      k0 += 0x9E3779B9u;
-      k1 += 0xBB67AE85u;
-    }
-    const uint64_t p0 = uint64_t(0xD2511F53u) * c.x;
-    const uint64_t p1 = uint64_t(0xCD9E8D57u) * c.z;
-    c = make_uint4(uint32_t(p1 >> 32) ^ c.y ^ k0, uint32_t(p1), uint32_t(p0 >> 32) ^ c.w ^ k1,
-                   uint32_t(p0));
-  }
-  return c;
-}
 
 // (a, ia) ranks before (b, ib): larger score, then lower id.
 __device__ inline bool before(float a, int ia, float b, int ib) {

@@ -1,0 +1,885 @@
+// TreeSpark's best-first draft-tree construction with the calibrated theta
+// stop (TreeSpark: Markov-conditioned draft trees, §3.1-§3.5).
+//
+// The drafter gives, per request, base logits U_1..U_b (one row per depth)
+// and shares a rank-r Markov head B(x, v) = <W1[x], W2[v]> (§3.1). A node at
+// depth d carrying token x has children drawn from q0 = softmax(U_{d+1} +
+// B(x, .)) (§3.2 step 1). A max-heap of child slots is keyed by calibrated
+// path survival: the sum of log p_hat along the root path with
+// p_hat = sigma(a logit(q0) + b) on the unscaled q0 (§1, §3.4). A node's slot
+// is its next child: the most probable unused token at T = 0, the next
+// without-replacement draw from q_T at T > 0, where the slot is keyed by the
+// admissible pre-draw bound S(v) p_hat(max unused q0) (§3.2). Materialising a
+// node opens its first-child slot and its parent's next-sibling slot (up to
+// K siblings); expansion stops when the best key falls below log theta or
+// the tree holds N drafted nodes (§3.5).
+//
+// GPU design: one persistent cooperative kernel runs every round, phases
+// separated by grid barriers (bounded waits):
+//  A select   one workgroup per request merges the statistics of the nodes
+//             expanded last round, then pops slots while the best exact key
+//             exceeds every pending node's bound (a node not yet expanded can
+//             only open slots keyed at or below its own survival), so the
+//             pops are exactly those of the one-at-a-time heap. It then lists
+//             the nodes that need their conditional (at most kRows per round).
+//             The request's state is kept as arrays (one entry per node), so
+//             lanes reading their own node hit distinct LDS banks.
+//  B logits   the listed nodes' W1 rows are staged in LDS 64 at a time (rows
+//             padded so an operand read is conflict-free); every wave takes
+//             16-token tiles of W2 as the A operand of
+//             v_mfma_f32_16x16x32_bf16 (the next tile's loads in flight while
+//             the current one is used), against the four 16-row tiles of the
+//             group, adds U (loaded before the products) and writes
+//             l = U + B for every listed row: W2 is read once per row group.
+//  C stats    (row, segment) items stream l once, eight 16-byte loads per
+//             thread in flight: fp32 online log-sum-exp, the row's K+1 best
+//             logits, and at T > 0 its K best Gumbel scores l/T - ln(-ln u)
+//             (u from Philox4x32-10 at counter (y/4, request * (N+1) + node,
+//             stream, 0)), kept in per-thread lists behind a wave threshold,
+//             merged per wave by shuffles and across waves in LDS.
+// Grid barriers poll with relaxed loads and take one acquire fence after: an
+// acquire load invalidates the XCD's L2 on every poll, which would evict the
+// lines the working waves of that XCD are using. Rounds end when no request
+// lists a node.
+#include <math.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "tv_device.hpp"
+#include "tv_internal.hpp"
+#include "tv_philox.hpp"
+#include "tv_topk.hpp"
+
+namespace tv {
+
+namespace {
+
+constexpr int kSpThreads = 256;
+constexpr int kSpWaves = kSpThreads / kWave;
+constexpr int kNodes = kSparkMaxNodes + 1;    // root + drafted nodes
+constexpr int kList = kSparkMaxSiblings + 1;  // K + 1 entries per list
+constexpr int kRows = kSparkRowsPerRound;
+constexpr int kMaxSeg = kSparkMaxSeg;
+constexpr int kMaxRank = 256;
+constexpr int kGroupRows = 64;                // W1 rows staged per group
+constexpr int kW1Stride = kMaxRank + 8;       // bf16 per staged row (528 B: 16-byte shift per row)
+constexpr int kStatBatch = 8;                 // float4 loads per thread in flight (stats)
+constexpr uint64_t kSpWaitTicks = 20000000ull;  // 0.2 s of the 100 MHz counter
+
+// A request's tree, one entry per node (workspace and LDS).
+struct ReqState {
+  double logS[kNodes];       // log path survival
+  double lse[kNodes];        // log-sum-exp of the node's child logits
+  int tok[kNodes], par[kNodes], dep[kNodes], nch[kNodes];
+  int state[kNodes];         // 0 not expanded, 1 listed for expansion, 2 expanded
+  int top_id[kNodes][kList]; // K+1 largest child logits, best first
+  float top_l[kNodes][kList];
+  int drw_id[kNodes][kList]; // T > 0: the K first without-replacement draws
+  float drw_l[kNodes][kList];
+  int pad[3];
+};
+static_assert(sizeof(ReqState) % 16 == 0, "state is copied in 16-byte units");
+
+// Statistics of one (row, segment).
+struct Part {
+  float m;
+  float pad;
+  double s;                  // sum exp(l - m)
+  float tv[kList];           // best logits
+  int ti[kList];
+  float gv[kList];           // best Gumbel scores
+  int gi[kList];
+};
+
+struct ReqHead {
+  int done, count, pad[6];
+};
+
+struct SparkParams {
+  const float* U;          // [B][depths][V]
+  const uint16_t* w1;      // [V][r] bf16
+  const uint16_t* w2;      // [V][r] bf16
+  const int32_t* anchor;
+  const float* temperature;
+  const float* theta;
+  int32_t* out_parent;     // [B][N+1]
+  int32_t* out_token;
+  int32_t* out_count;
+  float* out_logs;         // optional
+  uint32_t* status;
+  uint32_t* bar;           // [0] arrivals, [1] generation
+  ReqHead* head;           // [B]
+  ReqState* state;         // [B]
+  int* rows;               // [2][B][kRows]
+  int* cnt;                // [2][B]
+  float* ell;              // [B * kRows][V]
+  Part* part;              // [B * kRows][kMaxSeg]
+  int B, V, r, depths, N, K, nwg;
+  float a, b;
+  uint32_t stream, key0, key1;
+};
+
+// Phase-local LDS: the select phase's request state, or the logits phase's
+// staged W1 rows, or the statistics merge lists.
+constexpr size_t kSelectBytes = sizeof(ReqState);
+constexpr size_t kW1Bytes = size_t(kGroupRows) * kW1Stride * 2;
+constexpr size_t kMergeBytes = size_t(kSpWaves) * kList * 8 * 2;
+constexpr size_t kPhaseBytes =
+    kSelectBytes > kW1Bytes ? (kSelectBytes > kMergeBytes ? kSelectBytes : kMergeBytes)
+                            : (kW1Bytes > kMergeBytes ? kW1Bytes : kMergeBytes);
+
+// ---------------------------------------------------------------------------
+// Grid barrier: arrivals counted at agent scope; the last arrival resets the
+// count and bumps the generation the others wait for (bounded by time; after
+// a timeout the workgroup is dead and every later barrier returns false).
+
+__device__ bool grid_sync(const SparkParams& p, uint32_t& gen, int* s_dead) {
+  __syncthreads();
+  if (threadIdx.x == 0 && !*s_dead) {
+    const uint32_t old = __hip_atomic_fetch_add(p.bar, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == uint32_t(p.nwg) - 1u) {
+      __hip_atomic_store(p.bar, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p.bar + 1, gen + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (__hip_atomic_load(p.bar + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpWaitTicks) {
+          raise_status(p.status, TV_DEV_TIMEOUT);
+          *s_dead = 1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+  }
+  gen += 1u;
+  __syncthreads();
+  return !*reinterpret_cast<volatile int*>(s_dead);
+}
+
+// ---------------------------------------------------------------------------
+// Calibration and keys (fp64).
+
+// log sigma(a logit(q) + b), in the stable form log sigma(z) = -softplus(-z).
+__device__ inline double log_p_hat(double q, double a, double b) {
+  if (!(q > 0.0)) return -INFINITY;
+  if (q >= 1.0) return 0.0;
+  const double z = a * (log(q) - log1p(-q)) + b;
+  return z < 0.0 ? z - log1p(exp(z)) : -log1p(exp(-z));
+}
+
+__device__ inline bool rank_before(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+// Largest q0 among node i's tokens not yet used as its children.
+__device__ inline double max_unused_q0(const ReqState& st, int i, bool sampled) {
+  const int nch = st.nch[i];
+  int e = nch;  // greedy: the children are the first nch of the logit order
+  if (sampled) {
+    e = 0;
+    for (; e < kList; ++e) {
+      bool used = false;
+      for (int j = 0; j < nch; ++j) used |= st.drw_id[i][j] == st.top_id[i][e];
+      if (!used) break;
+    }
+  }
+  return exp(double(st.top_l[i][e]) - st.lse[i]);
+}
+
+// Wave argmax over (value, id) candidates, larger value then lower id; every
+// lane returns the winner.
+__device__ inline void wave_best(float& v, int& id) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(v, o, kWave);
+    const int oi = __shfl_xor(id, o, kWave);
+    if (rank_before(ov, oi, v, id)) {
+      v = ov;
+      id = oi;
+    }
+  }
+}
+
+// n rounds of a wave argmax over kC candidates per lane; the k-th winner goes
+// to (dv[k], di[k]) through lane 0.
+template <int kC>
+__device__ inline void wave_top(float (&cv)[kC], int (&ci)[kC], int n, float* dv, int* di) {
+  const int lane = threadIdx.x & (kWave - 1);
+  for (int k = 0; k < n; ++k) {
+    float bv = cv[0];
+    int bi = ci[0];
+#pragma unroll
+    for (int u = 1; u < kC; ++u)
+      if (rank_before(cv[u], ci[u], bv, bi)) {
+        bv = cv[u];
+        bi = ci[u];
+      }
+    wave_best(bv, bi);
+#pragma unroll
+    for (int u = 0; u < kC; ++u)
+      if (ci[u] == bi) {
+        cv[u] = -INFINITY;
+        ci[u] = 0x7fffffff;
+      }
+    if (lane == 0) {
+      dv[k] = bv;
+      di[k] = bi;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Phase A: one request.
+
+__device__ void select_request(const SparkParams& p, int r, int round, ReqState& st, int* s_misc) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int N = p.N, K = p.K;
+  const int cur = round & 1, prev = cur ^ 1;
+  const float T = p.temperature[r];
+  const bool sampled = T > 0.f;
+  const float th = p.theta[r];
+  const double logth = th > 0.f ? log(double(th)) : -INFINITY;
+  ReqHead* hd = p.head + r;
+  int* my_rows = p.rows + (size_t(cur) * p.B + r) * kRows;
+  constexpr int kWords = int(sizeof(ReqState) / 16);
+
+  if (round == 0) {
+    for (int i = tid; i <= N; i += kSpThreads) {
+      p.out_parent[size_t(r) * (N + 1) + i] = -1;
+      p.out_token[size_t(r) * (N + 1) + i] = -1;
+      if (p.out_logs) p.out_logs[size_t(r) * (N + 1) + i] = i == 0 ? 0.f : -INFINITY;
+    }
+    if (tid == 0) {
+      int a = p.anchor[r];
+      if (a < 0 || a >= p.V) {
+        raise_status(p.status, TV_DEV_SHAPE);
+        a = 0;
+      }
+      if (!(T >= 0.f) || !(th >= 0.f)) raise_status(p.status, TV_DEV_LOGITS);  // read as 0
+      st.tok[0] = a;
+      st.par[0] = -1;
+      st.dep[0] = 0;
+      st.nch[0] = 0;
+      st.state[0] = 0;
+      st.logS[0] = 0.0;
+      st.lse[0] = 0.0;
+      s_misc[0] = 0;  // done
+      s_misc[1] = 0;  // drafted nodes
+    }
+  } else {
+    if (tid == 0) {
+      s_misc[0] = hd->done;
+      s_misc[1] = hd->count;
+    }
+    __syncthreads();
+    if (!s_misc[0]) {  // request state into LDS
+      const uint4* src = reinterpret_cast<const uint4*>(p.state + r);
+      uint4* dst = reinterpret_cast<uint4*>(&st);
+      for (int i = tid; i < kWords; i += kSpThreads) dst[i] = src[i];
+    }
+  }
+  __syncthreads();
+  if (s_misc[0]) {
+    if (tid == 0) p.cnt[size_t(cur) * p.B + r] = 0;
+    return;
+  }
+  const int count0 = s_misc[1];
+
+  if (tid < kWave) {
+    // --- merge last round's statistics of this request's listed nodes
+    if (round > 0) {
+      int nprev = 0, pre = 0;
+      for (int q = lane; q < p.B; q += kWave) {
+        const int c = p.cnt[size_t(prev) * p.B + q];
+        nprev += c;
+        pre += q < r ? c : 0;
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        nprev += __shfl_xor(nprev, o, kWave);
+        pre += __shfl_xor(pre, o, kWave);
+      }
+      const int S = spark_segments(nprev, p.nwg);
+      const int mine = p.cnt[size_t(prev) * p.B + r];
+      for (int j = 0; j < mine; ++j) {
+        const int i = p.rows[(size_t(prev) * p.B + r) * kRows + j];
+        const size_t g = size_t(pre + j);
+        const Part* pp = p.part + g * kMaxSeg;
+        // log-sum-exp of the segments
+        double M = lane < S ? double(pp[lane].m) : -INFINITY;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) M = fmax(M, __shfl_xor(M, o, kWave));
+        double t = lane < S && pp[lane].m != -INFINITY ? pp[lane].s * exp(double(pp[lane].m) - M) : 0.0;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, kWave);
+        // the K+1 best logits and (T > 0) the K best scores over the
+        // segments: candidates c = seg * kList + e, up to nine per lane
+        constexpr int kC = (kMaxSeg * kList + kWave - 1) / kWave;
+        const int nl = K + 1;
+        float cv[kC], gv[kC];
+        int ci[kC], gi[kC];
+#pragma unroll
+        for (int u = 0; u < kC; ++u) {
+          const int c = lane + u * kWave, sg = c / kList, e = c - sg * kList;
+          const bool ok = sg < S && e < nl;
+          cv[u] = ok ? pp[sg].tv[e] : -INFINITY;
+          ci[u] = ok ? pp[sg].ti[e] : 0x7fffffff;
+          const bool okg = sampled && sg < S && e < K;
+          gv[u] = okg ? pp[sg].gv[e] : -INFINITY;
+          gi[u] = okg ? pp[sg].gi[e] : 0x7fffffff;
+        }
+        wave_top(cv, ci, nl, st.top_l[i], st.top_id[i]);
+        if (sampled) wave_top(gv, gi, K, st.drw_l[i], st.drw_id[i]);
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        // fewer than K+1 candidates only with non-finite logits (already
+        // reported): keep every id a valid row of W1; the drawn tokens'
+        // logits are read back from the row, all at once
+        const float* row = p.ell + g * size_t(p.V);
+        if (lane < nl) {
+          const int y = st.top_id[i][lane];
+          if (y < 0 || y >= p.V) {
+            raise_status(p.status, TV_DEV_LOGITS);
+            st.top_id[i][lane] = 0;
+          }
+        }
+        if (sampled && lane < K) {
+          int y = st.drw_id[i][lane];
+          if (y < 0 || y >= p.V) y = 0;
+          st.drw_id[i][lane] = y;
+          st.drw_l[i][lane] = row[y];
+        }
+        if (lane == 0) {
+          st.lse[i] = M + log(t);
+          st.state[i] = 2;
+          if (!(t > 0.0) || !isfinite(st.lse[i])) raise_status(p.status, TV_DEV_LOGITS);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
+
+    // --- pops
+    int count = count0;
+    int done = 0;
+    const double ca = p.a, cb = p.b;
+    while (true) {
+      if (count >= N) {
+        done = 1;
+        break;
+      }
+      double bk = -INFINITY;
+      int bi = 0x7fffffff, npend = 0;
+      double pb = -INFINITY;
+      for (int i = lane; i <= count; i += kWave) {
+        if (st.dep[i] >= p.depths) continue;
+        if (st.state[i] == 2) {
+          if (st.nch[i] < K) {
+            const double key = st.logS[i] + log_p_hat(max_unused_q0(st, i, sampled), ca, cb);
+            if (key > bk || (key == bk && i < bi)) {
+              bk = key;
+              bi = i;
+            }
+          }
+        } else if (st.logS[i] >= logth) {
+          pb = fmax(pb, st.logS[i]);
+          ++npend;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const double ok = __shfl_xor(bk, o, kWave);
+        const int oi = __shfl_xor(bi, o, kWave);
+        if (ok > bk || (ok == bk && oi < bi)) {
+          bk = ok;
+          bi = oi;
+        }
+        pb = fmax(pb, __shfl_xor(pb, o, kWave));
+        npend += __shfl_xor(npend, o, kWave);
+      }
+      if (npend > 0 && (bi == 0x7fffffff || pb >= bk)) break;  // expand first
+      if (bi == 0x7fffffff || bk < logth) {
+        done = 1;
+        break;
+      }
+      if (npend >= kRows) break;
+      // pop the slot of node v
+      const int v = __builtin_amdgcn_readfirstlane(bi);
+      const int j = st.nch[v];
+      const int x = sampled ? st.drw_id[v][j] : st.top_id[v][j];
+      const float lx = sampled ? st.drw_l[v][j] : st.top_l[v][j];
+      const double lS = st.logS[v] + log_p_hat(exp(double(lx) - st.lse[v]), ca, cb);
+      const int c = count + 1;
+      const int dv = st.dep[v];
+      __builtin_amdgcn_wave_barrier();
+      if (lane == 0) {
+        st.tok[c] = x;
+        st.par[c] = v;
+        st.dep[c] = dv + 1;
+        st.nch[c] = 0;
+        st.state[c] = 0;
+        st.logS[c] = lS;
+        st.lse[c] = 0.0;
+        st.nch[v] = j + 1;
+        const size_t o = size_t(r) * (N + 1) + c;
+        p.out_parent[o] = v;
+        p.out_token[o] = x;
+        if (p.out_logs) p.out_logs[o] = float(lS);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      count = c;
+    }
+    // --- list the nodes to expand (not when done)
+    int listed = 0;
+    if (!done) {
+      for (int base = 0; base <= count; base += kWave) {
+        const int i = base + lane;
+        const bool want = i <= count && st.state[i] == 0 && st.dep[i] < p.depths && st.logS[i] >= logth;
+        const uint64_t m = __ballot(want);
+        const int pos = listed + int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32),
+                                                                __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
+        if (want && pos < kRows) {
+          my_rows[pos] = i;
+          st.state[i] = 1;
+        }
+        listed += __popcll(m);
+      }
+      listed = min(listed, kRows);
+    }
+    if (lane == 0) {
+      s_misc[0] = done;
+      s_misc[1] = count;
+      s_misc[2] = listed;
+    }
+  }
+  __syncthreads();
+  // request state back to the workspace
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(&st);
+    uint4* dst = reinterpret_cast<uint4*>(p.state + r);
+    for (int i = tid; i < kWords; i += kSpThreads) dst[i] = src[i];
+  }
+  if (tid == 0) {
+    hd->done = s_misc[0];
+    hd->count = s_misc[1];
+    p.cnt[size_t(cur) * p.B + r] = s_misc[2];
+    if (s_misc[0]) p.out_count[r] = s_misc[1] + 1;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Phase B: logits of the listed rows.
+
+__device__ void logits_phase(const SparkParams& p, int n_act, const int* s_rx, const long long* s_ru,
+                             uint16_t* s_w1) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), l16 = lane & 15, lg = lane >> 4;
+  const int wave = tid / kWave;
+  const int KK = p.r / 32;
+  const int nt = (p.V + 15) / 16;
+  const int gw = blockIdx.x * kSpWaves + wave;
+  const int nwave = p.nwg * kSpWaves;
+  const bool vec = (p.V & 3) == 0;
+  auto load_a = [&](int tile, bf16x8 (&A)[kMaxRank / 32]) __attribute__((always_inline)) {
+    const int tok = min(tile * 16 + l16, p.V - 1);
+#pragma unroll
+    for (int kk = 0; kk < kMaxRank / 32; ++kk)
+      if (kk < KK) A[kk] = *reinterpret_cast<const bf16x8*>(p.w2 + size_t(tok) * p.r + kk * 32 + 8 * lg);
+  };
+  for (int g0 = 0; g0 < n_act; g0 += kGroupRows) {
+    const int gn = min(kGroupRows, n_act - g0);
+    // stage the group's W1 rows (zero past the group)
+    __syncthreads();
+    const int chunks = p.r / 8;  // 16-byte pieces per row
+    for (int c = tid; c < kGroupRows * chunks; c += kSpThreads) {
+      const int row = c / chunks, piece = c - row * chunks;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (row < gn) v = *reinterpret_cast<const uint4*>(p.w1 + size_t(s_rx[g0 + row]) * p.r + piece * 8);
+      *reinterpret_cast<uint4*>(s_w1 + row * kW1Stride + piece * 8) = v;
+    }
+    __syncthreads();
+    const int nrt = (gn + 15) / 16;
+    bf16x8 A[kMaxRank / 32], An[kMaxRank / 32];
+    if (gw < nt) load_a(gw, A);
+    for (int tile = gw; tile < nt; tile += nwave) {
+      if (tile + nwave < nt) load_a(tile + nwave, An);  // in flight while this tile is used
+      const int y0 = tile * 16 + 4 * lg;
+      // U of the four row tiles, loaded before the products
+      float4 uu[4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const int g = g0 + rt * 16 + l16;
+        uu[rt] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (rt < nrt && g < g0 + gn) {
+          const float* u = p.U + s_ru[g];
+          if (vec && y0 + 3 < p.V) {
+            uu[rt] = *reinterpret_cast<const float4*>(u + y0);
+          } else {
+            uu[rt].x = y0 < p.V ? u[y0] : 0.f;
+            uu[rt].y = y0 + 1 < p.V ? u[y0 + 1] : 0.f;
+            uu[rt].z = y0 + 2 < p.V ? u[y0 + 2] : 0.f;
+            uu[rt].w = y0 + 3 < p.V ? u[y0 + 3] : 0.f;
+          }
+        }
+      }
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        if (rt >= nrt) break;
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        const uint16_t* brow = s_w1 + (rt * 16 + l16) * kW1Stride + 8 * lg;
+#pragma unroll
+        for (int kk = 0; kk < kMaxRank / 32; ++kk)
+          if (kk < KK)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[kk], *reinterpret_cast<const bf16x8*>(brow + kk * 32),
+                                                          acc, 0, 0, 0);
+        // lane holds row g, tokens y0 .. y0 + 3
+        const int g = g0 + rt * 16 + l16;
+        if (g < g0 + gn) {
+          float* out = p.ell + size_t(g) * p.V;
+          const float4 o = make_float4(acc[0] + uu[rt].x, acc[1] + uu[rt].y, acc[2] + uu[rt].z,
+                                       acc[3] + uu[rt].w);
+          if (vec && y0 + 3 < p.V) {
+            *reinterpret_cast<float4*>(out + y0) = o;
+          } else {
+            if (y0 < p.V) out[y0] = o.x;
+            if (y0 + 1 < p.V) out[y0 + 1] = o.y;
+            if (y0 + 2 < p.V) out[y0 + 2] = o.z;
+            if (y0 + 3 < p.V) out[y0 + 3] = o.w;
+          }
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < kMaxRank / 32; ++kk) A[kk] = An[kk];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Phase C: statistics of one (row, segment).
+
+template <int L>
+__device__ void stats_item(const SparkParams& p, int g, int seg, int S, int req, int node, float T,
+                           float* s_v, int* s_i, double* s_d, float* m_v, int* m_i) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int K = p.K, nl = K + 1;
+  const bool noisy = T > 0.f;
+  const float invT = noisy ? 1.f / T : 0.f;
+  const float* row = p.ell + size_t(g) * p.V;
+  const int ng = (p.V + 3) / 4;
+  const int q0 = int(long(ng) * seg / S), q1 = int(long(ng) * (seg + 1) / S);
+  const uint32_t node_row = uint32_t(req) * uint32_t(p.N + 1) + uint32_t(node);
+  const bool vec = (p.V & 3) == 0;
+  constexpr float kLog2e = 1.4426950408889634f;
+
+  TopList<L> A, G;
+  A.init();
+  G.init();
+  float m = -INFINITY, s = 0.f, thA = -INFINITY, thG = -INFINITY;
+  bool bad = false;
+  int step = 0;
+  // Every thread runs the same batches (the thresholds are wave-wide
+  // shuffles); a thread past the segment's end carries -inf values.
+  const int steps = (q1 - q0 + kSpThreads - 1) / kSpThreads;
+  for (int b0 = 0; b0 < steps; b0 += kStatBatch) {
+    float4 buf[kStatBatch];
+#pragma unroll
+    for (int u = 0; u < kStatBatch; ++u) {
+      const int q = q0 + (b0 + u) * kSpThreads + tid;
+      const int y = 4 * q;
+      buf[u] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      if (b0 + u < steps && q < q1) {
+        if (vec) {
+          buf[u] = *reinterpret_cast<const float4*>(row + y);
+        } else {
+          buf[u].x = row[y];
+          buf[u].y = y + 1 < p.V ? row[y + 1] : -INFINITY;
+          buf[u].z = y + 2 < p.V ? row[y + 2] : -INFINITY;
+          buf[u].w = y + 3 < p.V ? row[y + 3] : -INFINITY;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kStatBatch; ++u) {
+      if (b0 + u >= steps) break;
+      const int q = q0 + (b0 + u) * kSpThreads + tid;
+      const bool in = q < q1;
+      const int y = 4 * q;
+      const float v[4] = {buf[u].x, buf[u].y, buf[u].z, buf[u].w};
+      const float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+      if (in) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bad |= y + e < p.V && !(v[e] - v[e] == 0.f);
+        if (mx > m) {
+          s *= __builtin_amdgcn_exp2f((m - mx) * kLog2e);
+          m = mx;
+        }
+        s += __builtin_amdgcn_exp2f((v[0] - m) * kLog2e) + __builtin_amdgcn_exp2f((v[1] - m) * kLog2e) +
+             __builtin_amdgcn_exp2f((v[2] - m) * kLog2e) + __builtin_amdgcn_exp2f((v[3] - m) * kLog2e);
+      }
+      if (__builtin_amdgcn_ballot_w64(in && (mx >= thA) && (mx > A.v[L - 1])) != 0 && in) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (v[e] >= thA) A.insert(v[e], y + e);
+      }
+      if (noisy) {
+        const uint4 w4 = philox4x32_10(make_uint4(uint32_t(q), node_row, p.stream, 0u), p.key0, p.key1);
+        const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
+        float bmax = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = (float(16777216u - (w[e] >> 8)) - 0.5f) * (1.f / 16777216.f);  // 1 - u
+          bmax = fmaxf(bmax, v[e] * invT - __logf(x) + 1e-3f);  // g <= -ln(1 - u)
+        }
+        if (__builtin_amdgcn_ballot_w64(in && (bmax >= thG) && (bmax > G.v[L - 1])) != 0 && in) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (v[e] == -INFINITY) continue;
+            const float x = (float(16777216u - (w[e] >> 8)) - 0.5f) * (1.f / 16777216.f);
+            if (v[e] * invT - __logf(x) + 1e-3f < thG) continue;
+            const float uu = (float(w[e] >> 8) + 0.5f) * (1.f / 16777216.f);
+            const float en = uu > 0.5f ? -log1pf(-x) : -logf(uu);  // -ln u, accurate near u = 1
+            G.insert(v[e] * invT - logf(en), y + e);
+          }
+        }
+      }
+      ++step;
+      if (step == 2 || step == 4 || (step & 7) == 0) {  // early refreshes: the lists fill fast
+        thA = wave_kth_largest(A.v[0], nl);
+        if (noisy) thG = wave_kth_largest(G.v[0], K);
+      }
+    }
+  }
+  if (bad) raise_status(p.status, TV_DEV_LOGITS);
+
+  Part* out = p.part + size_t(g) * kMaxSeg + seg;
+  // log-sum-exp partial: block maximum, then the rescaled sums in fp64
+  float M = m;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
+  if (lane == 0) s_v[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(s_v[0], s_v[1]), fmaxf(s_v[2], s_v[3]));
+  double sd = m == -INFINITY ? 0.0 : double(s) * exp(double(m) - double(M));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) sd += __shfl_xor(sd, o, kWave);
+  if (lane == 0) s_d[wave] = sd;
+  // the lists: each wave's n best by shuffles, then one wave over the waves'
+  auto wave_list = [&](TopList<L>& Lst, int n, float* dv, int* di) __attribute__((always_inline)) {
+    for (int k = 0; k < n; ++k) {
+      float bv = Lst.v[0];
+      int bi = Lst.i[0];
+      wave_best(bv, bi);
+      if (Lst.i[0] == bi && bi != 0x7fffffff) Lst.pop();
+      if (lane == 0) {
+        dv[k] = bv;
+        di[k] = bi;
+      }
+    }
+  };
+  wave_list(A, nl, m_v + wave * kList, m_i + wave * kList);
+  if (noisy) wave_list(G, K, m_v + (kSpWaves + wave) * kList, m_i + (kSpWaves + wave) * kList);
+  __syncthreads();
+  if (tid < kWave) {
+    constexpr int kC = (kSpWaves * kList + kWave - 1) / kWave;
+    float cv[kC];
+    int ci[kC];
+#pragma unroll
+    for (int u = 0; u < kC; ++u) {
+      const int c = lane + u * kWave, w = c / kList, e = c - w * kList;
+      const bool ok = w < kSpWaves && e < nl;
+      cv[u] = ok ? m_v[w * kList + e] : -INFINITY;
+      ci[u] = ok ? m_i[w * kList + e] : 0x7fffffff;
+    }
+    wave_top(cv, ci, nl, out->tv, out->ti);
+    if (noisy) {
+#pragma unroll
+      for (int u = 0; u < kC; ++u) {
+        const int c = lane + u * kWave, w = c / kList, e = c - w * kList;
+        const bool ok = w < kSpWaves && e < K;
+        cv[u] = ok ? m_v[(kSpWaves + w) * kList + e] : -INFINITY;
+        ci[u] = ok ? m_i[(kSpWaves + w) * kList + e] : 0x7fffffff;
+      }
+      wave_top(cv, ci, K, out->gv, out->gi);
+    }
+    if (lane == 0) {
+      out->m = M;
+      out->s = (s_d[0] + s_d[1]) + (s_d[2] + s_d[3]);
+    }
+  }
+  __syncthreads();
+}
+
+template <int L>
+__global__ __launch_bounds__(kSpThreads) void spark_kernel(SparkParams p) {
+  __shared__ __align__(16) unsigned char s_phase[kPhaseBytes];
+  __shared__ int s_rx[kSparkMaxRows];
+  __shared__ long long s_ru[kSparkMaxRows];
+  __shared__ int s_rq[kSparkMaxRows], s_rn[kSparkMaxRows];
+  __shared__ float s_v[kSpWaves];
+  __shared__ int s_i[kSpWaves];
+  __shared__ double s_d[kSpWaves];
+  __shared__ int s_misc[4];
+  __shared__ int s_dead;
+  if (threadIdx.x == 0) s_dead = 0;
+  __syncthreads();
+  ReqState& st = *reinterpret_cast<ReqState*>(s_phase);
+  uint16_t* s_w1 = reinterpret_cast<uint16_t*>(s_phase);
+  float* m_v = reinterpret_cast<float*>(s_phase);
+  int* m_i = reinterpret_cast<int*>(s_phase + size_t(2) * kSpWaves * kList * sizeof(float));
+  uint32_t gen = __hip_atomic_load(p.bar + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint32_t expanded = 0;
+  for (int round = 0; round <= p.N + 2; ++round) {
+    for (int r = blockIdx.x; r < p.B; r += p.nwg) {
+      select_request(p, r, round, st, s_misc);
+      __syncthreads();
+    }
+    if (!grid_sync(p, gen, &s_dead)) return;
+    // the rows listed this round, in request order
+    const int cur = round & 1;
+    if (threadIdx.x < kWave) {
+      int listed = 0;
+      for (int q0 = 0; q0 < p.B; q0 += kWave) {
+        const int q = q0 + int(threadIdx.x);
+        const int c = q < p.B ? p.cnt[size_t(cur) * p.B + q] : 0;
+        int inc = c;  // inclusive prefix over the wave
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          const int t = __shfl_up(inc, o, kWave);
+          if (int(threadIdx.x) >= o) inc += t;
+        }
+        const int start = listed + inc - c;
+        for (int j = 0; j < c; ++j) {
+          const int i = p.rows[(size_t(cur) * p.B + q) * kRows + j];
+          s_rx[start + j] = p.state[q].tok[i];
+          s_ru[start + j] = ((long long)q * p.depths + p.state[q].dep[i]) * p.V;
+          s_rq[start + j] = q;
+          s_rn[start + j] = i;
+        }
+        listed += __shfl(inc, kWave - 1, kWave);
+      }
+      if (threadIdx.x == 0) s_misc[3] = listed;
+    }
+    __syncthreads();
+    const int n_act = s_misc[3];
+    if (n_act == 0) {  // every request is done (the same for every workgroup)
+      if (blockIdx.x == 0 && threadIdx.x == 0) {  // diagnostics: rounds run, rows expanded
+        p.status[2] = uint32_t(round);
+        p.status[3] = expanded;
+      }
+      return;
+    }
+    expanded += uint32_t(n_act);
+    logits_phase(p, n_act, s_rx, s_ru, s_w1);
+    if (!grid_sync(p, gen, &s_dead)) return;
+    const int S = spark_segments(n_act, p.nwg);
+    for (int it = blockIdx.x; it < n_act * S; it += p.nwg) {
+      const int g = it / S, seg = it - g * S;
+      stats_item<L>(p, g, seg, S, s_rq[g], s_rn[g], p.temperature[s_rq[g]], s_v, s_i, s_d, m_v, m_i);
+    }
+    if (!grid_sync(p, gen, &s_dead)) return;
+  }
+}
+
+// Per-device resident workgroups of each kernel instantiation.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_nwg9[kMaxDevices], g_nwg17[kMaxDevices];
+
+template <int L>
+hipError_t resident_workgroups(int* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::atomic<int>* cache = L == 9 ? g_nwg9 : g_nwg17;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int v = cache[dev].load(std::memory_order_acquire);
+    if (v > 0) {
+      *out = v;
+      return hipSuccess;
+    }
+  }
+  int cus = 0, per = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, reinterpret_cast<const void*>(spark_kernel<L>),
+                                                   kSpThreads, 0);
+  if (e != hipSuccess) return e;
+  if (per < 1 || cus < 1) return hipErrorInvalidDevice;
+  const int v = per * cus;
+  if (dev >= 0 && dev < kMaxDevices) cache[dev].store(v, std::memory_order_release);
+  *out = v;
+  return hipSuccess;
+}
+
+template <int L>
+hipError_t launch(SparkParams& p, hipStream_t stream) {
+  int nwg = 0;
+  hipError_t e = resident_workgroups<L>(&nwg);
+  if (e != hipSuccess) return e;
+  p.nwg = nwg;
+  void* args[] = {&p};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(spark_kernel<L>), dim3(unsigned(nwg)),
+                                    dim3(kSpThreads), args, 0, stream);
+}
+
+}  // namespace
+
+size_t spark_workspace_bytes(const tv_spark_desc& d) {
+  size_t off = kHeaderBytes;                      // status word
+  off += 256;                                     // grid barrier words
+  off += align256(size_t(d.batch) * sizeof(ReqHead));
+  off += align256(size_t(d.batch) * sizeof(ReqState));
+  off += align256(size_t(2) * d.batch * kRows * sizeof(int));
+  off += align256(size_t(2) * d.batch * sizeof(int));
+  off += align256(size_t(d.batch) * kRows * kMaxSeg * sizeof(Part));
+  off += align256(size_t(d.batch) * kRows * size_t(d.vocab) * sizeof(float));
+  return off;
+}
+
+hipError_t launch_spark(const tv_spark_desc& d, const SparkArgs& a, hipStream_t stream) {
+  SparkParams p{};
+  char* ws = static_cast<char*>(a.workspace);
+  size_t off = 0;
+  p.status = reinterpret_cast<uint32_t*>(ws);
+  off += kHeaderBytes;
+  p.bar = reinterpret_cast<uint32_t*>(ws + off);
+  off += 256;
+  p.head = reinterpret_cast<ReqHead*>(ws + off);
+  off += align256(size_t(d.batch) * sizeof(ReqHead));
+  p.state = reinterpret_cast<ReqState*>(ws + off);
+  off += align256(size_t(d.batch) * sizeof(ReqState));
+  p.rows = reinterpret_cast<int*>(ws + off);
+  off += align256(size_t(2) * d.batch * kRows * sizeof(int));
+  p.cnt = reinterpret_cast<int*>(ws + off);
+  off += align256(size_t(2) * d.batch * sizeof(int));
+  p.part = reinterpret_cast<Part*>(ws + off);
+  off += align256(size_t(d.batch) * kRows * kMaxSeg * sizeof(Part));
+  p.ell = reinterpret_cast<float*>(ws + off);
+  p.U = a.base_logits;
+  p.w1 = static_cast<const uint16_t*>(a.w1);
+  p.w2 = static_cast<const uint16_t*>(a.w2);
+  p.anchor = a.anchor;
+  p.temperature = a.temperature;
+  p.theta = a.theta;
+  p.out_parent = a.out_parent;
+  p.out_token = a.out_token;
+  p.out_count = a.out_count;
+  p.out_logs = a.out_logsurv;
+  p.B = d.batch;
+  p.V = d.vocab;
+  p.r = d.rank;
+  p.depths = d.depths;
+  p.N = d.max_nodes;
+  p.K = d.max_siblings;
+  p.a = d.calib_a;
+  p.b = d.calib_b;
+  p.stream = a.stream_id;
+  p.key0 = uint32_t(a.seed);
+  p.key1 = uint32_t(a.seed >> 32);
+  if (d.max_siblings + 1 <= 9) return launch<9>(p, stream);
+  return launch<17>(p, stream);
+}
+
+}  // namespace tv

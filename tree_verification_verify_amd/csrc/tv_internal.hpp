@@ -123,4 +123,37 @@ hipError_t launch_rerank(int32_t batch, int32_t num_cand, int32_t cap, int32_t m
 
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream);
 
+// TreeSpark best-first construction.
+constexpr int kSparkMaxNodes = 64;      // drafted nodes per tree
+constexpr int kSparkMaxSiblings = 16;   // children per node
+constexpr int kSparkRowsPerRound = 4;   // expansions per request per round
+constexpr int kSparkMaxBatch = 256;
+constexpr int kSparkMaxRows = kSparkMaxBatch * kSparkRowsPerRound;
+constexpr int kSparkMaxDepths = 16;
+// Segments per expanded row in the statistics phase: at most one item per
+// workgroup, at most kSparkMaxSeg.
+constexpr int kSparkMaxSeg = 32;
+__host__ __device__ inline int spark_segments(int rows, int nwg) {
+  if (rows <= 0) return 1;
+  const int s = nwg / rows;
+  return s < 1 ? 1 : (s > kSparkMaxSeg ? kSparkMaxSeg : s);
+}
+struct SparkArgs {
+  const float* base_logits;
+  const void* w1;
+  const void* w2;
+  const int32_t* anchor;
+  const float* temperature;
+  const float* theta;
+  uint32_t stream_id;
+  uint64_t seed;
+  int32_t* out_parent;
+  int32_t* out_token;
+  int32_t* out_count;
+  float* out_logsurv;
+  void* workspace;
+};
+size_t spark_workspace_bytes(const tv_spark_desc& d);
+hipError_t launch_spark(const tv_spark_desc& d, const SparkArgs& a, hipStream_t stream);
+
 }  // namespace tv
