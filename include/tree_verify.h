@@ -201,8 +201,11 @@ tv_status tree_verify_attn(const tv_attn_desc* desc,
  *   node_indptr [B+1], parent [T] int32; temperature [B] fp32 >= 0;
  *   uniforms [T][2] fp32 in [0,1).
  *   accept_flag [T] int8, next_token [T] int32: outputs.
- * Arithmetic is fp64 (exp, sums, ratios); decisions therefore match an fp64
- * reference except within ~1e-12 of a threshold. */
+ * Every single decision value (p(x), q(x), ratios, normalisers) is formed in
+ * fp64; the vocabulary sums add fp32 exps (each from an fp64 argument, about
+ * 1.5e-7 relative) in fp64. Decisions therefore match an fp64 reference
+ * except within ~1e-6 of a threshold: an acceptance ratio, or a boundary of
+ * the final draw's cumulative sum (in units of u). */
 tv_status tree_spec_sample(const tv_sample_desc* desc,
                            const float* target_logits, const float* draft_logits,
                            const int32_t* tokens, const int32_t* node_indptr,

@@ -13,14 +13,13 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle.sampler import near_threshold
 from workloads import make_config, make_attention_inputs, make_sampler_inputs, random_tree
 from workloads.relabel import relabel_trees, relabel_attention, relabel_sampler, global_perm
 
 pytestmark = pytest.mark.gpu
 
 TOL = {"bf16": 2e-2, "fp32": 1e-5}
-EPS = 1e-9
+EPS = 1e-6   # the near-threshold band of the specification
 
 
 def _attn(inp):
@@ -68,15 +67,12 @@ def _sample(inp, md, prefix_lens):
 
 
 def _check_sampler(inp, got, prefix_lens):
+    from test_gpu_sampler import compare_walk
     flags, nts, logs = oracle.tree_spec_sample(inp)
     pn, ot, ol, kk = oracle.tree_accept_path(inp.node_indptr, inp.parent, inp.tokens, flags,
                                              nts, prefix_lens, got["max_depth"])
-    for r in range(inp.batch):
-        assert not near_threshold(logs[r], EPS), r
-    np.testing.assert_array_equal(got["flag"], flags)
-    np.testing.assert_array_equal(got["next_token"], nts)
-    for key, ref in (("out_len", ol), ("path_nodes", pn), ("out_tokens", ot), ("kv_keep", kk)):
-        np.testing.assert_array_equal(got[key], ref, err_msg=key)
+    skipped, _ = compare_walk(inp, got, flags, nts, logs, pn, ot, ol, kk)
+    assert skipped == 0, skipped
 
 
 @pytest.mark.parametrize("kind", ["dfs", "random"])
@@ -92,6 +88,8 @@ def test_sampler_and_path_relabelled(kind, temp):
     _check_sampler(rel, got, cfg.prefix_lens)
     base = _sample(cfg.sampler, 8, cfg.prefix_lens)
     perm = global_perm(cfg.sampler.node_indptr, maps)
+    # the same decisions at the same nodes: the GPU's arithmetic does not
+    # depend on the numbering
     np.testing.assert_array_equal(got["flag"][perm], base["flag"])
     np.testing.assert_array_equal(got["next_token"][perm], base["next_token"])
     np.testing.assert_array_equal(got["out_len"], base["out_len"])

@@ -1,8 +1,10 @@
 """GPU parity: tree_spec_sample + tree_accept_path (HIP, via the C ABI)
 against the fp64 oracle. Decisions are bit-exact; a request whose oracle log
 holds a decision within EPS of its threshold (or a degenerate residual) is
-excluded from the bit-exact comparison and counted (none is expected at
-EPS = 1e-9: both sides compute in fp64)."""
+excluded from the bit-exact comparison and counted. EPS is the specification's
+band, 1e-6: the GPU sums the vocabulary from fp32 exps (fp64 arguments and
+accumulation, ~1.5e-7 relative per term) and takes every single decision
+value in fp64, so its decision values lie within ~1e-7 of the oracle's."""
 import numpy as np
 import pytest
 
@@ -12,7 +14,7 @@ from workloads import make_config, make_sampler_inputs, random_tree, chain_tree,
 
 pytestmark = pytest.mark.gpu
 
-EPS = 1e-9
+EPS = 1e-6   # the near-threshold band of the specification
 
 
 def _run(inp, **kw):
@@ -20,7 +22,51 @@ def _run(inp, **kw):
     return run_sampler(inp, **kw)
 
 
-def _compare(inp, got, prefix_lens=None, allow_near=0, replacement=False):
+def near_kind(log, eps):
+    """How a request's decisions sit against the band: "accept" when an
+    acceptance test lies within eps of its ratio (or a residual degenerated),
+    "draw" when only the final draw lies within eps of a boundary, None."""
+    if any(k == "degenerate" or (k == "accept" and m < eps) for k, _, m in log):
+        return "accept"
+    if any(k == "draw" and m < eps for k, _, m in log):
+        return "draw"
+    return None
+
+
+def compare_walk(inp, got, flags, nts, logs, pn, ot, ol, kk):
+    """Bit-exact comparison; a request with a near acceptance test is skipped
+    whole, one whose only near decision is the final draw is compared on
+    everything upstream of the draw (flags, path, keep-list, emitted tokens
+    but the last). Returns (skipped, draw_only)."""
+    skipped = draw_only = 0
+    for r in range(inp.batch):
+        a, b = int(inp.node_indptr[r]), int(inp.node_indptr[r + 1])
+        kind = near_kind(logs[r], EPS)
+        if kind == "accept":
+            skipped += 1
+            continue
+        np.testing.assert_array_equal(got["flag"][a:b], flags[a:b], err_msg=f"request {r}")
+        assert got["out_len"][r] == ol[r], r
+        np.testing.assert_array_equal(got["path_nodes"][r], pn[r])
+        np.testing.assert_array_equal(got["kv_keep"][r], kk[r])
+        n = int(ol[r])
+        if kind == "draw":
+            draw_only += 1
+            stop = int(pn[r][n - 1])
+            keep = np.ones(b - a, bool)
+            keep[stop] = False
+            np.testing.assert_array_equal(got["next_token"][a:b][keep], nts[a:b][keep], err_msg=f"request {r}")
+            np.testing.assert_array_equal(got["out_tokens"][r][:n - 1], ot[r][:n - 1])
+            assert 0 <= got["out_tokens"][r][n - 1] < inp.vocab
+        else:
+            np.testing.assert_array_equal(got["next_token"][a:b], nts[a:b], err_msg=f"request {r}")
+            np.testing.assert_array_equal(got["out_tokens"][r], ot[r])
+    return skipped, draw_only
+
+
+def _compare(inp, got, prefix_lens=None, allow_near=0, replacement=False, draw_near=None):
+    """allow_near: requests with a near acceptance test (skipped); draw_near:
+    the expected number whose only near decision is the draw (None: any)."""
     assert got["status"] == 0, (got["status"], got["bits"])
     flags, nts, logs = oracle.tree_spec_sample(inp, replacement=replacement)
     md = got["max_depth"]
@@ -28,20 +74,11 @@ def _compare(inp, got, prefix_lens=None, allow_near=0, replacement=False):
     prefix_lens = prefix_lens if prefix_lens is not None else [0] * B
     pn, ot, ol, kk = oracle.tree_accept_path(inp.node_indptr, inp.parent, inp.tokens, flags,
                                              nts, prefix_lens, md)
-    near = 0
-    for r in range(B):
-        a, b = int(inp.node_indptr[r]), int(inp.node_indptr[r + 1])
-        if near_threshold(logs[r], EPS):
-            near += 1
-            continue
-        np.testing.assert_array_equal(got["flag"][a:b], flags[a:b], err_msg=f"request {r}")
-        np.testing.assert_array_equal(got["next_token"][a:b], nts[a:b], err_msg=f"request {r}")
-        assert got["out_len"][r] == ol[r], r
-        np.testing.assert_array_equal(got["path_nodes"][r], pn[r])
-        np.testing.assert_array_equal(got["out_tokens"][r], ot[r])
-        np.testing.assert_array_equal(got["kv_keep"][r], kk[r])
-    assert near <= allow_near, near
-    return near
+    skipped, draw_only = compare_walk(inp, got, flags, nts, logs, pn, ot, ol, kk)
+    assert skipped <= allow_near, skipped
+    if draw_near is not None:
+        assert draw_only == draw_near, draw_only
+    return skipped
 
 
 def test_tiny():
@@ -50,11 +87,13 @@ def test_tiny():
              cfg.prefix_lens)
 
 
-@pytest.mark.parametrize("temp", ["mixed", 0.0, 0.5, 1.0])
-def test_highload_full_vocab(temp):
+# draw_near: requests whose final draw lands within the band of a boundary
+# (tail tokens of probability below ~2e-6); counted by the oracle alone.
+@pytest.mark.parametrize("temp,draw_near", [("mixed", 2), (0.0, 0), (0.5, 1), (1.0, 9)])
+def test_highload_full_vocab(temp, draw_near):
     cfg = make_config("highload", attention=False, temperature=temp)
     _compare(cfg.sampler, _run(cfg.sampler, max_depth=8, prefix_lens=cfg.prefix_lens),
-             cfg.prefix_lens)
+             cfg.prefix_lens, draw_near=draw_near)
 
 
 def test_highload_independent_logits():
@@ -251,12 +290,12 @@ def test_greedy_split_rows_and_ties(V):
 # ---- the with-replacement rule (survey page, Taxonomy rule (b)) ----------
 
 
-@pytest.mark.parametrize("temp", ["mixed", 1.0])
-def test_highload_with_replacement(temp):
+@pytest.mark.parametrize("temp,draw_near", [("mixed", 0), (1.0, 8)])
+def test_highload_with_replacement(temp, draw_near):
     cfg = make_config("highload", attention=False, temperature=temp, draws="with")
     inp = cfg.sampler
     _compare(inp, _run(inp, max_depth=8, prefix_lens=cfg.prefix_lens, replacement=True),
-             cfg.prefix_lens, replacement=True)
+             cfg.prefix_lens, replacement=True, draw_near=draw_near)
 
 
 @pytest.mark.parametrize("V", [3, 7, 64, 1000])

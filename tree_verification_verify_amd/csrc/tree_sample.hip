@@ -128,6 +128,7 @@ constexpr double kZC3 = kZC1 * kZC1 * kZC1 / 6.0;
 constexpr double kZC4 = kZC1 * kZC1 * kZC1 * kZC1 / 24.0;
 constexpr double kZFloor = -1100.0 * kZTable;
 constexpr double kShift52 = 6755399441055744.0;  // 1.5 * 2^52
+constexpr double kLog2E = 1.4426950408889634074;
 
 __device__ inline double exp_z(double z, const double* tbl) {
   z = fmax(z, kZFloor);
@@ -140,6 +141,20 @@ __device__ inline double exp_z(double z, const double* tbl) {
   q *= f;
   const double tj = tbl[n & (kZTable - 1)];
   return ldexp(fma(tj, q, tj), n >> kZBits);
+}
+
+// 2^z for z <= 0 given in fp64: z = n + f with n an integer and |f| <= 1/2
+// (rounding by the 1.5 * 2^52 shift, whose low word is then n), 2^f by the
+// hardware exp2 in fp32 (f is exact to 2^-25, the result to ~1 ulp),
+// scaled by 2^n. The argument keeps its fp64 absolute precision, so the
+// result's relative error stays ~1.5e-7 however far z is below 0; z below
+// -200 (and -inf) gives 0.
+__device__ inline float exp2_split(double z) {
+  z = fmax(z, -200.0);
+  const double nd = z + kShift52;
+  const int n = __double2loint(nd);
+  const float f = float(z - (nd - kShift52));
+  return ldexpf(__builtin_amdgcn_exp2f(f), n);
 }
 
 // Empty volatile asm on a value: the value is taken to be produced (or
@@ -386,6 +401,26 @@ __device__ inline double block_sum(double v, double* sh) {
   for (int w = 0; w < kWaves; ++w) tot += sh[w];
   __syncthreads();
   return tot;
+}
+
+// Block-wide maxima of two values; every thread returns them.
+__device__ inline void block_max2(float& a, float& b, float* shf) {
+  float A = wave_max(a), Bm = wave_max(b);
+  const int wave = threadIdx.x / kWave;
+  if ((threadIdx.x & 63) == 0) {
+    shf[wave] = A;
+    shf[kWaves + wave] = Bm;
+  }
+  __syncthreads();
+  A = shf[0];
+  Bm = shf[kWaves];
+  for (int w = 1; w < kWaves; ++w) {
+    A = fmaxf(A, shf[w]);
+    Bm = fmaxf(Bm, shf[kWaves + w]);
+  }
+  __syncthreads();
+  a = A;
+  b = Bm;
 }
 
 // Block-wide maxima (fp32 logits) and sums of exp(x/T - max/T) of both rows:
@@ -663,6 +698,7 @@ struct WalkLds {
   int* s_nk;          // children of the visited node (kKids + 1: more follow)
   int* s_int;
   float4* s_res;      // [2 rows][kLdsCh][kThreads] LDS-resident chunks
+  double* s_draw;     // [kResCh * kWaves + kWaves] chunk and wave sums of the draw
 };
 
 // 16-byte load of lane offset voff (bytes) from [base, base + bytes) through
@@ -741,6 +777,127 @@ __device__ __attribute__((always_inline)) inline void walk(
     }
   };
 
+  // Stored exps (after a visit's stats pass): registers or LDS, no mask
+  // (masked elements were stored as 0).
+  auto stored = [&](int u, float4& a, float4& b) __attribute__((always_inline)) {
+    if constexpr (RES) {
+      if (u < kRegCh) {
+        a = S.t[u];
+        b = S.d[u];
+      } else {
+        a = L.s_res[(u - kRegCh) * kThreads + threadIdx.x];
+        b = L.s_res[(kLdsCh + u - kRegCh) * kThreads + threadIdx.x];
+      }
+    }
+  };
+  auto put = [&](int u, float4 a, float4 b) __attribute__((always_inline)) {
+    if constexpr (RES) {
+      if (u < kRegCh) {
+        S.t[u] = a;
+        S.d[u] = b;
+      } else {
+        L.s_res[(u - kRegCh) * kThreads + threadIdx.x] = a;
+        L.s_res[(kLdsCh + u - kRegCh) * kThreads + threadIdx.x] = b;
+      }
+    }
+  };
+  float mm_t = -INFINITY, mm_d = -INFINITY;  // the member's maxima of the visited rows
+
+  // Inverse-CDF draw inside this member's resident slice (stored exps):
+  // the smallest token whose running weight w = max(ct p~ - cb q~, 0) passes
+  // thr, in token order (chunk u, thread t, element e); past the end (only
+  // through rounding) the last token with weight. Result in *L.s_int.
+  auto resident_draw = [&](double thr, double ct, double cb) __attribute__((always_inline)) {
+    const int wave = threadIdx.x / kWave;
+    auto weights = [&](int u, double (&w)[4]) __attribute__((always_inline)) {
+      float4 a, b;
+      stored(u, a, b);
+      const float pa[4] = {a.x, a.y, a.z, a.w}, qb[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const double x = fma(-cb, double(qb[e]), ct * double(pa[e]));
+        w[e] = x > 0.0 ? x : 0.0;
+      }
+    };
+    if (threadIdx.x == 0) *L.s_int = -1;
+#pragma unroll
+    for (int u = 0; u < kResCh; ++u) {
+      if (u < nch) {
+        double w[4];
+        weights(u, w);
+        const double t = wave_sum((w[0] + w[1]) + (w[2] + w[3]));
+        if (lane == 0) L.s_draw[u * kWaves + wave] = t;
+      }
+    }
+    __syncthreads();
+    int uc = -1, ulast = -1;
+    double pre = 0.0, base = 0.0, lastbase = 0.0;
+    for (int u = 0; u < nch; ++u) {
+      double cu = 0.0;
+      for (int w = 0; w < kWaves; ++w) cu += L.s_draw[u * kWaves + w];
+      if (cu > 0.0) {
+        ulast = u;
+        lastbase = pre;
+      }
+      if (uc < 0 && pre <= thr && thr < pre + cu) {
+        uc = u;
+        base = pre;
+      }
+      pre += cu;
+    }
+    const bool past = uc < 0;
+    if (past) {
+      uc = ulast;
+      base = lastbase;
+    }
+    if (uc >= 0) {
+      // chunk uc, chosen by a uniform branch (a run-time index into the
+      // register-resident slice would move the slice to scratch memory)
+      double w[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int u = 0; u < kResCh; ++u)
+        if (u == uc) weights(u, w);
+      const double ts = (w[0] + w[1]) + (w[2] + w[3]);
+      double inc = ts;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const double o = __shfl_up(inc, off, kWave);
+        if (lane >= off) inc += o;
+      }
+      if (lane == kWave - 1) L.s_draw[kResCh * kWaves + wave] = inc;
+      __syncthreads();
+      double woff = 0.0;
+      for (int w2 = 0; w2 < wave; ++w2) woff += L.s_draw[kResCh * kWaves + w2];
+      double c = base + woff + inc - ts;
+      const int y0 = lo + uc * 4 * kThreads + 4 * int(threadIdx.x);
+      if (!past && ts > 0.0 && c <= thr && thr < c + ts) {
+        int y = -1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (y < 0 && w[e] > 0.0 && c <= thr && thr < c + w[e]) y = e;
+          c += w[e];
+        }
+        if (y < 0) {  // rounding between the thread's sum and its parts: its last token with weight
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (w[e] > 0.0) y = e;
+        }
+        *L.s_int = y0 + y;
+      }
+      __syncthreads();
+      if (*L.s_int < 0) {  // past the end, or missed by rounding: the last token with weight
+        int last = -1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (w[e] > 0.0) last = y0 + e;
+        if (last >= 0) atomicMax(L.s_int, last);
+      }
+      __syncthreads();
+    }
+    if (threadIdx.x == 0 && *L.s_int < 0) *L.s_int = lo;  // no mass (not reachable with finite logits)
+    __syncthreads();
+  };
+
   int v = 0;
   for (int depth_guard = 0; depth_guard <= N; ++depth_guard) {
     const float* trow = p.t + size_t(nbeg + v) * V;
@@ -801,38 +958,45 @@ __device__ __attribute__((always_inline)) inline void walk(
         }
       }
       kids();
+      // Pass 1: the member's maxima of both rows (and the non-finite check).
       float chk = 0.f;
-      // Three groups: running maxima raised once per group (one rescale).
-      auto group = [&](int u0, int u1) __attribute__((always_inline)) {
-        float gt = -INFINITY, gd = -INFINITY;
+      float gt = -INFINITY, gd = -INFINITY;
 #pragma unroll
-        for (int u = u0; u < u1; ++u) {
-          if (u < nch) {
-            float4 a, b;
-            chunk(u, a, b, &chk);
-            gt = fmaxf(fmaxf(gt, fmaxf(a.x, a.y)), fmaxf(a.z, a.w));
-            gd = fmaxf(fmaxf(gd, fmaxf(b.x, b.y)), fmaxf(b.z, b.w));
-          }
+      for (int u = 0; u < kResCh; ++u) {
+        if (u < nch) {
+          float4 a, b;
+          chunk(u, a, b, &chk);
+          gt = fmaxf(fmaxf(gt, fmaxf(a.x, a.y)), fmaxf(a.z, a.w));
+          gd = fmaxf(fmaxf(gd, fmaxf(b.x, b.y)), fmaxf(b.z, b.w));
         }
-        const float nt = fmaxf(mt, gt), nd = fmaxf(md, gd);
-        st = mt == -INFINITY ? 0.0 : st * exp_nonpos((double(mt) - double(nt)) * invT, L.tbl);
-        sd = md == -INFINITY ? 0.0 : sd * exp_nonpos((double(md) - double(nd)) * invT, L.tbl);
-        mt = nt;
-        md = nd;
-        const double bt = -double(nt) * A, bd = -double(nd) * A;
+      }
+      block_max2(gt, gd, L.shf);
+      mm_t = gt;
+      mm_d = gd;
+      // Pass 2: every element's exp relative to the member's maxima, kept in
+      // place of its logit (the residual passes of this visit reuse it) and
+      // summed in fp64. z = (x - M) / T in log2 units, formed by one fp64 fma.
+      const double A2 = invT * kLog2E;
+      const double bt2 = mm_t == -INFINITY ? 0.0 : -double(mm_t) * A2;
+      const double bd2 = mm_d == -INFINITY ? 0.0 : -double(mm_d) * A2;
 #pragma unroll
-        for (int u = u0; u < u1; ++u) {
-          if (u < nch) {
-            float4 a, b;
-            chunk(u, a, b, nullptr);
-            st += exp4_sum(a, A, bt, L.tblz);
-            sd += exp4_sum(b, A, bd, L.tblz);
-          }
+      for (int u = 0; u < kResCh; ++u) {
+        if (u < nch) {
+          float4 a, b;
+          chunk(u, a, b, nullptr);
+          a = opaque(a);
+          b = opaque(b);
+          a = make_float4(exp2_split(fma(double(a.x), A2, bt2)), exp2_split(fma(double(a.y), A2, bt2)),
+                          exp2_split(fma(double(a.z), A2, bt2)), exp2_split(fma(double(a.w), A2, bt2)));
+          b = make_float4(exp2_split(fma(double(b.x), A2, bd2)), exp2_split(fma(double(b.y), A2, bd2)),
+                          exp2_split(fma(double(b.z), A2, bd2)), exp2_split(fma(double(b.w), A2, bd2)));
+          st = opaque(st + ((double(a.x) + double(a.y)) + (double(a.z) + double(a.w))));
+          sd = opaque(sd + ((double(b.x) + double(b.y)) + (double(b.z) + double(b.w))));
+          put(u, a, b);
         }
-      };
-      group(0, (kRegCh + 1) / 2);
-      group((kRegCh + 1) / 2, kRegCh);
-      group(kRegCh, kResCh);
+      }
+      mt = mm_t;
+      md = mm_d;
       bad = !(chk == 0.f);
     } else {
       kids();
@@ -859,7 +1023,20 @@ __device__ __attribute__((always_inline)) inline void walk(
       L.s_ku[lane] = ku;
       if (lane == 0) *L.s_nk = nk;
     }
-    block_ms2(mt, st, md, sd, invT, L.sh, L.shf, L.tbl);
+    if constexpr (RES) {
+      // every thread's sums are relative to the member's maxima already
+      double vt = wave_sum(st), vd = wave_sum(sd);
+      const int wave = threadIdx.x / kWave;
+      if (lane == 0) {
+        L.sh[wave] = vt;
+        L.sh[kWaves + wave] = vd;
+      }
+      __syncthreads();
+      st = (L.sh[0] + L.sh[1]) + (L.sh[2] + L.sh[3]);
+      sd = (L.sh[kWaves] + L.sh[kWaves + 1]) + (L.sh[kWaves + 2] + L.sh[kWaves + 3]);
+    } else {
+      block_ms2(mt, st, md, sd, invT, L.sh, L.shf, L.tbl);
+    }
     if (threadIdx.x < 6) {
       const uint32_t k = threadIdx.x;
       const double dv = k < 3 ? st : sd;
@@ -928,17 +1105,21 @@ __device__ __attribute__((always_inline)) inline void walk(
       const double an = R.a + B / Sq;
       double part = 0.0;
       if constexpr (RES) {
-        const double bt = -double(Mt32) * A, bd = -double(Md32) * A;
-        const double ca = R.invZt, cb = -an * R.invZd;
-        auto wsum = [&](float t, float d) __attribute__((always_inline)) {
-          const double w = fma(cb, exp_z(fma(double(d), A, bd), L.tblz), ca * exp_z(fma(double(t), A, bt), L.tblz));
+        // p(y) = stored_t * ct, q(y) = stored_d * cq with the member's scale
+        // factors (its maxima against the team's, over Z).
+        const double ct = mm_t == -INFINITY ? 0.0
+                                            : exp_nonpos((double(mm_t) - double(Mt32)) * invT, L.tbl) * R.invZt;
+        const double cb = mm_d == -INFINITY ? 0.0
+                                            : -an * exp_nonpos((double(mm_d) - double(Md32)) * invT, L.tbl) * R.invZd;
+        auto wsum = [&](float pt, float qd) __attribute__((always_inline)) {
+          const double w = fma(cb, double(qd), ct * double(pt));
           return w > 0.0 ? w : 0.0;
         };
 #pragma unroll
         for (int u = 0; u < kResCh; ++u) {
           if (u < nch) {
             float4 a, b;
-            chunk(u, a, b, nullptr);
+            stored(u, a, b);
             a = opaque(a);
             b = opaque(b);
             part = opaque(part + (wsum(a.x, b.x) + wsum(a.y, b.y)));
@@ -1006,7 +1187,19 @@ __device__ __attribute__((always_inline)) inline void walk(
     }
     finder = __builtin_amdgcn_readfirstlane(finder);
     if (finder == member) {
-      slice_search(trow, drow, lo, hi, R, thr - base_w, L.tbl, L.sh, L.s_int);
+      if constexpr (RES) {
+        // The member's stored exps give the residual weights of its slice:
+        // chunk sums locate the 1024-token chunk, a block-wide prefix over
+        // its threads the thread, the thread's four tokens the token.
+        const double ct = mm_t == -INFINITY ? 0.0
+                                            : exp_nonpos((double(mm_t) - double(Mt32)) * invT, L.tbl) * R.invZt;
+        const double cb = mm_d == -INFINITY || R.a == 0.0
+                              ? 0.0
+                              : R.a * exp_nonpos((double(mm_d) - double(Md32)) * invT, L.tbl) * R.invZd;
+        resident_draw(thr - base_w, ct, cb);
+      } else {
+        slice_search(trow, drow, lo, hi, R, thr - base_w, L.tbl, L.sh, L.s_int);
+      }
       if (threadIdx.x == 0) p.next_token[nbeg + v] = *L.s_int;
     } else if (finder < 0 && member == 0 && threadIdx.x == 0) {
       p.next_token[nbeg + v] = 0;  // no mass in any slice (not reachable with finite logits)
@@ -1168,6 +1361,7 @@ __global__ __launch_bounds__(kThreads, 4) void sample_kernel(SampleParams p) {
   __shared__ float s_kt[kKids], s_kd[kKids], s_ku[kKids];
   __shared__ int s_par[kParLds], s_tok[kParLds];
   __shared__ float4 s_res[2 * kLdsCh * kThreads];
+  __shared__ double s_draw[kResCh * kWaves + kWaves];
   __shared__ float shv[kWaves];
   __shared__ int shi[kWaves];
   __shared__ int s_nk, s_int, s_dead;
@@ -1305,7 +1499,7 @@ __global__ __launch_bounds__(kThreads, 4) void sample_kernel(SampleParams p) {
     lo = min(V, member * slice);
     hi = min(V, lo + slice);
   }
-  WalkLds L{tbl, tblz, sh, shf, s_slice, s_words, s_kid, s_kt, s_kd, s_ku, &s_nk, &s_int, s_res};
+  WalkLds L{tbl, tblz, sh, shf, s_slice, s_words, s_kid, s_kt, s_kd, s_ku, &s_nk, &s_int, s_res, s_draw};
   const bool resident = vec4 && (C + p.W - 1) / p.W <= kResCh;  // the same for every member
   if (resident)
     walk<true>(p, tm, nbeg, N, par, invT, lo, hi, nch, vec4, L);
