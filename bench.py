@@ -84,40 +84,57 @@ def read_traffic():
     return float(m_b.group(1))
 
 
-def cpu_baseline(cfg, budget_s=12.0, replacement=False):
-    """The oracle as it stands on the first requests of the same workload,
-    until ~budget_s of CPU time; returns nodes/s and what was sampled."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, budget_s=12.0, replacement=False, requests=32, repeats=3):
+    """The oracle as it stands (fp64 NumPy attention + sampling walk + path)
+    on a fixed sample of the workload's requests (the first `requests`),
+    timed with perf_counter, median of `repeats` runs, once with the BLAS
+    pools limited to every core in this process's affinity set and once
+    with one thread. Returns nodes/s of the all-core run, with the one-thread
+    figure, the CPU model and every run's time beside it."""
     import oracle
     from workloads.inputs import SamplerInputs
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
+    from threadpoolctl import threadpool_limits
     inp, s = cfg.attn, cfg.sampler
-    t0 = time.perf_counter()
-    nodes = 0
-    done = 0
-    for r in range(inp.batch):
-        n = inp.nodes(r)
-        oracle.tree_attention_rows(inp, [(r, i) for i in range(n)])
-        a, b = int(s.node_indptr[r]), int(s.node_indptr[r + 1])
-        one = SamplerInputs(vocab=s.vocab, target_logits=s.target_logits[a:b],
-                            draft_logits=None if s.draft_logits is None else s.draft_logits[a:b],
-                            tokens=s.tokens[a:b], node_indptr=np.array([0, b - a], np.int32),
-                            parent=s.parent[a:b], temperature=s.temperature[r:r + 1],
-                            uniforms=s.uniforms[a:b])
-        f, nt, _ = oracle.tree_spec_sample(one, replacement=replacement)
-        oracle.tree_accept_path(one.node_indptr, one.parent, one.tokens, f, nt,
-                                [int(inp.prefix_len[r])], 16)
-        nodes += n
-        done += 1
-        if time.perf_counter() - t0 > budget_s and done >= 2:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": nodes / dt, "unit": "nodes/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {done} of {inp.batch} requests ({nodes} tree rows): fp64 NumPy "
-                      f"attention + sampling walk + path, {dt:.1f} s"}
+    sample = list(range(min(requests, inp.batch)))
+    nodes = sum(inp.nodes(r) for r in sample)
+
+    def run():
+        t0 = time.perf_counter()
+        for r in sample:
+            n = inp.nodes(r)
+            oracle.tree_attention_rows(inp, [(r, i) for i in range(n)])
+            a, b = int(s.node_indptr[r]), int(s.node_indptr[r + 1])
+            one = SamplerInputs(vocab=s.vocab, target_logits=s.target_logits[a:b],
+                                draft_logits=None if s.draft_logits is None else s.draft_logits[a:b],
+                                tokens=s.tokens[a:b], node_indptr=np.array([0, b - a], np.int32),
+                                parent=s.parent[a:b], temperature=s.temperature[r:r + 1],
+                                uniforms=s.uniforms[a:b])
+            f, nt, _ = oracle.tree_spec_sample(one, replacement=replacement)
+            oracle.tree_accept_path(one.node_indptr, one.parent, one.tokens, f, nt,
+                                    [int(inp.prefix_len[r])], 16)
+        return time.perf_counter() - t0
+
+    cores = len(os.sched_getaffinity(0))
+    times = {}
+    for label, limit in (("all", cores), ("one", 1)):
+        with threadpool_limits(limits=limit):
+            times[label] = [run() for _ in range(repeats)]
+    med = {k: float(np.median(v)) for k, v in times.items()}
+    return {"value": nodes / med["all"], "unit": "nodes/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {len(sample)} of {inp.batch} requests ({nodes} tree rows): fp64 "
+                      f"NumPy attention + sampling walk + path; median of {repeats} runs",
+            "cpu_model": _cpu_model(), "one_thread_value": nodes / med["one"],
+            "runs_s": {k: [round(x, 3) for x in v] for k, v in times.items()}}
 
 
 def attn_sweep(names, rotate_bytes, reps):
