@@ -205,7 +205,13 @@ tv_status tree_verify_attn(const tv_attn_desc* desc,
  * fp64; the vocabulary sums add fp32 exps (each from an fp64 argument, about
  * 1.5e-7 relative) in fp64. Decisions therefore match an fp64 reference
  * except within ~1e-6 of a threshold: an acceptance ratio, or a boundary of
- * the final draw's cumulative sum (in units of u). */
+ * the final draw's cumulative sum (in units of u).
+ * Each request is walked by a team of workgroups that wait on one another
+ * through the workspace; a launch never holds more workgroups than the
+ * device keeps resident at once, so with no other kernels running alongside
+ * every team is resident together. Members held back longer than the wait
+ * limit (0.2 s) by concurrent work make the call set TV_DEV_TIMEOUT (outputs
+ * then unspecified) instead of hanging. */
 tv_status tree_spec_sample(const tv_sample_desc* desc,
                            const float* target_logits, const float* draft_logits,
                            const int32_t* tokens, const int32_t* node_indptr,

@@ -1584,8 +1584,13 @@ hipError_t launch_sample_core(const tv_sample_desc& d, const SampleArgs& a, uint
   int per = 0, cus = 0;
   hipError_t e = device_facts(&per, &cus);
   if (e != hipSuccess) return e;
-  // Team size: as many workgroups per request as stay resident (the
-  // launch is cooperative), at most kMaxTeam; a team lives on one XCD.
+  // Team size: as many workgroups per request as the device keeps resident
+  // at once, at most kMaxTeam; a team lives on one XCD. The grid never
+  // exceeds that residency, so on a device that runs nothing else every
+  // team is resident together. The launch is a plain one (a cooperative
+  // launch costs about 17 us more here); a team whose members are held back
+  // by other work longer than the wait limit reports TV_DEV_TIMEOUT instead
+  // of waiting on.
   const long resident = long(per) * cus;
   int W = int(resident / ((d.batch + 7) / 8 * 8));
   if (W > kMaxTeam) W = kMaxTeam;
@@ -1611,13 +1616,8 @@ hipError_t launch_sample_core(const tv_sample_desc& d, const SampleArgs& a, uint
   p.with_replacement = d.rule == TV_RULE_WITH_REPLACEMENT;
   p.wait_ticks = wait_ticks();
   const dim3 grid(unsigned(grid_for(W))), block(kThreads);
-  if (W == 1) {
-    hipLaunchKernelGGL(sample_kernel, grid, block, 0, stream, p);
-    return hipGetLastError();
-  }
-  void* args[] = {&p};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(sample_kernel), grid, block,
-                                    args, 0, stream);
+  hipLaunchKernelGGL(sample_kernel, grid, block, 0, stream, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_sample(const tv_sample_desc& d, const SamplePlan& pl, const SampleArgs& a,
