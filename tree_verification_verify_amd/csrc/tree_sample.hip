@@ -32,15 +32,18 @@
 //    residual is max(p - a q, 0) / B with scalars a_{j+1} = a_j + B_j / S_j,
 //    B_{j+1} = sum_y max(p(y) - a_{j+1} q(y), 0), S_j = 1 - sum_{i<j} q(x_i)
 //    (a rejected token's residual is already 0, so removing it from the
-//    proposal is implicit). With replacement the proposal stays q: S_j = 1. The per-slice sums of the last pass (or of p, at
-//    a leaf) locate the slice of the correction/bonus draw, so the draw
-//    rescans one slice only.
-//  * Arithmetic is fp64 (logits widened exactly). Vocabulary sums use a
-//    table exp (2^(j/256) in LDS, quartic polynomial, the power of two set by
-//    ldexp) on an argument formed by one fma from the fp32 logit; single
-//    values that decide (p(x), q(x), rescale factors) use a 64-entry table
-//    with a degree-5 polynomial (~1 ulp). Decisions therefore agree with an
-//    fp64 reference except within ~1e-12 of a threshold.
+//    proposal is implicit). With replacement the proposal stays q: S_j = 1.
+//    The per-slice sums of the last pass (or of p, at a leaf) locate the
+//    slice of the correction/bonus draw, so the draw rescans one slice only.
+//  * Arithmetic: every single value that decides (p(x), q(x), ratios,
+//    rescale factors, a, B, S) is fp64, from a 64-entry table with a
+//    degree-5 polynomial (~1 ulp). Vocabulary sums add fp32 exps in fp64:
+//    each exp takes an fp64 argument formed by one fma from the fp32 logit
+//    (about 1.5e-7 relative), and a resident slice keeps the exps in place
+//    of its logits for the residual passes and the final draw. Decisions
+//    therefore agree with an fp64 reference except within ~1e-6 of a
+//    threshold. Streamed slices use a table exp (2^(j/256), quartic
+//    polynomial) throughout.
 //  * T = 0 requests: the team splits the rows; argmax (lowest index on ties)
 //    of every row, then the exact-match flags; no draft logits are read.
 #include <math.h>
