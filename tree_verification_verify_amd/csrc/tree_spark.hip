@@ -130,28 +130,63 @@ constexpr size_t kPhaseBytes =
                             : (kW1Bytes > kMergeBytes ? kW1Bytes : kMergeBytes);
 
 // ---------------------------------------------------------------------------
-// Grid barrier: arrivals counted at agent scope; the last arrival resets the
-// count and bumps the generation the others wait for (bounded by time; after
-// a timeout the workgroup is dead and every later barrier returns false).
+// Grid barrier, in two levels along the XCDs (block b runs on XCD b % 8,
+// and an XCD's L2 is coherent for its own CUs but not with the other XCDs'):
+// a workgroup arrives on its XCD's counter; the XCD's last arrival writes
+// back that L2 (one release per XCD) and arrives on the grid counter; the
+// grid's last arrival bumps the grid generation, which every XCD's last
+// arrival waits for (polled at system scope, past its own L2), then
+// invalidates that L2 (one acquire) and bumps the XCD generation that the
+// XCD's other workgroups wait for. Waits are bounded by time; after a
+// timeout the workgroup is dead and every later barrier returns false.
+// Words: grid counter 0, grid generation 1; XCD x's counter at 64 + 64x and
+// generation at 96 + 64x (separate 256-byte lines). One arrival costs ~6 us
+// at 512 workgroups against ~17 us for one grid-wide counter with an
+// acquire-release arrival per workgroup.
+constexpr int kBarWords = 64 + 8 * 64;
 
 __device__ bool grid_sync(const SparkParams& p, uint32_t& gen, int* s_dead) {
   __syncthreads();
   if (threadIdx.x == 0 && !*s_dead) {
-    const uint32_t old = __hip_atomic_fetch_add(p.bar, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == uint32_t(p.nwg) - 1u) {
-      __hip_atomic_store(p.bar, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(p.bar + 1, gen + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-      while (__hip_atomic_load(p.bar + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
-        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpWaitTicks) {
-          raise_status(p.status, TV_DEV_TIMEOUT);
-          *s_dead = 1;
-          break;
+    const int x = blockIdx.x & 7;
+    const uint32_t members = uint32_t((p.nwg - x + 7) / 8);  // workgroups on XCD x
+    uint32_t* xc = p.bar + 64 + 64 * x;
+    uint32_t* xg = p.bar + 96 + 64 * x;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    bool dead = false;
+    const uint32_t old = __hip_atomic_fetch_add(xc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == members - 1u) {
+      __hip_atomic_store(xc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      const uint32_t groups = uint32_t(p.nwg < 8 ? p.nwg : 8);
+      const uint32_t o2 = __hip_atomic_fetch_add(p.bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (o2 == groups - 1u) {
+        __hip_atomic_store(p.bar, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p.bar + 1, gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      } else {
+        while (__hip_atomic_load(p.bar + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == gen) {
+          if (__builtin_amdgcn_s_memrealtime() - t0 > kSpWaitTicks) {
+            dead = true;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
         }
-        __builtin_amdgcn_s_sleep(2);
       }
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      __hip_atomic_store(xg, gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      while (__hip_atomic_load(xg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpWaitTicks) {
+          dead = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    if (dead) {
+      raise_status(p.status, TV_DEV_TIMEOUT);
+      *s_dead = 1;
     }
   }
   gen += 1u;
@@ -828,7 +863,7 @@ hipError_t launch(SparkParams& p, hipStream_t stream) {
 
 size_t spark_workspace_bytes(const tv_spark_desc& d) {
   size_t off = kHeaderBytes;                      // status word
-  off += 256;                                     // grid barrier words
+  off += align256(size_t(kBarWords) * sizeof(uint32_t));  // grid barrier words
   off += align256(size_t(d.batch) * sizeof(ReqHead));
   off += align256(size_t(d.batch) * sizeof(ReqState));
   off += align256(size_t(2) * d.batch * kRows * sizeof(int));
@@ -845,7 +880,7 @@ hipError_t launch_spark(const tv_spark_desc& d, const SparkArgs& a, hipStream_t 
   p.status = reinterpret_cast<uint32_t*>(ws);
   off += kHeaderBytes;
   p.bar = reinterpret_cast<uint32_t*>(ws + off);
-  off += 256;
+  off += align256(size_t(kBarWords) * sizeof(uint32_t));
   p.head = reinterpret_cast<ReqHead*>(ws + off);
   off += align256(size_t(d.batch) * sizeof(ReqHead));
   p.state = reinterpret_cast<ReqState*>(ws + off);
