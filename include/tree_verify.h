@@ -413,7 +413,7 @@ tv_status tree_rerank(int32_t batch, int32_t num_cand, int32_t cand_capacity, in
  * anchor outside [0, V) TV_DEV_SHAPE. */
 typedef struct {
   int32_t batch;         /* B, 1..256 */
-  int32_t vocab;         /* V >= max_siblings + 1 */
+  int32_t vocab;         /* V: max_siblings + 1 .. 4194304 */
   int32_t rank;          /* r: a multiple of 32, at most 256 */
   int32_t depths;        /* b: base-logit rows per request, 1..16 */
   int32_t max_nodes;     /* N: drafted nodes per tree, 1..64 */

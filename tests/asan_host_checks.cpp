@@ -100,6 +100,11 @@ int main() {
   tv_spark_desc kbad = kd;
   kbad.rank = 48;
   EXPECT(tv_spark_workspace_size(&kbad) == 0);
+  tv_spark_desc kbig = kd;
+  kbig.vocab = (1 << 22) + 1;  // past the vocabulary limit (w2 under 4 GB)
+  EXPECT(tv_spark_workspace_size(&kbig) == 0);
+  kbig.vocab = 1 << 22;
+  EXPECT(tv_spark_workspace_size(&kbig) > 0);
   EXPECT(tree_spark_build(&kbad, ff, fake, fake, fi, ff, ff, 0, 0, fo, fo, fo, fv, ws, sizeof ws, nullptr) ==
          TV_ERR_SHAPE);
   EXPECT(tree_spark_build(&kd, ff, fake, fake, fi, ff, ff, 0, 0, fo, fo, fo, fv, ws, sizeof ws, nullptr) ==

@@ -247,7 +247,8 @@ tv_status tree_rerank(int32_t batch, int32_t num_cand, int32_t cand_capacity, in
 namespace {
 bool spark_desc_ok(const tv_spark_desc& d) {
   return d.batch >= 1 && d.batch <= tv::kSparkMaxBatch && d.max_siblings >= 1 &&
-         d.max_siblings <= tv::kSparkMaxSiblings && d.vocab >= d.max_siblings + 1 && d.rank >= 32 &&
+         d.max_siblings <= tv::kSparkMaxSiblings && d.vocab >= d.max_siblings + 1 &&
+         d.vocab <= tv::kSparkMaxVocab && d.rank >= 32 &&
          d.rank <= 256 && d.rank % 32 == 0 && d.depths >= 1 && d.depths <= tv::kSparkMaxDepths &&
          d.max_nodes >= 1 && d.max_nodes <= tv::kSparkMaxNodes && d.calib_a == d.calib_a &&
          d.calib_b == d.calib_b;

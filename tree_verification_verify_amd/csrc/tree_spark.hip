@@ -27,16 +27,25 @@
 //  B logits   the listed nodes' W1 rows are staged in LDS 64 at a time (rows
 //             padded so an operand read is conflict-free); every wave takes
 //             16-token tiles of W2 as the A operand of
-//             v_mfma_f32_16x16x32_bf16 (the next tile's loads in flight while
-//             the current one is used), against the four 16-row tiles of the
-//             group, adds U (loaded before the products) and writes
-//             l = U + B for every listed row: W2 is read once per row group.
+//             v_mfma_f32_16x16x32_bf16 against the four 16-row tiles of the
+//             group, adds U and writes l = U + B for every listed row: W2 is
+//             read once per row group. The next tile's W2 rows and U values
+//             are loaded while the current tile is used, unconditionally (a
+//             wave's last prefetch repeats the final tile), so the wait
+//             before each product covers only its own tile's loads.
 //  C stats    (row, segment) items stream l once, eight 16-byte loads per
 //             thread in flight: fp32 online log-sum-exp, the row's K+1 best
 //             logits, and at T > 0 its K best Gumbel scores l/T - ln(-ln u)
 //             (u from Philox4x32-10 at counter (y/4, request * (N+1) + node,
-//             stream, 0)), kept in per-thread lists behind a wave threshold,
-//             merged per wave by shuffles and across waves in LDS.
+//             stream, 0)), kept in per-thread lists behind a wave threshold
+//             (each value's insert runs only where some lane's own value
+//             passes), merged per wave by cross-lane reductions and across
+//             waves in LDS.
+// The select and logits phases are functions of their own (each gets the
+// whole register file; inlined into one kernel they spilled into the logits
+// loop), reading the parameters in place in the kernel-argument segment.
+// Wave reductions and sorts exchange lanes by DPP and the row-swap permutes
+// rather than LDS permutes.
 // Grid barriers poll with relaxed loads and take one acquire fence after: an
 // acquire load invalidates the XCD's L2 on every poll, which would evict the
 // lines the working waves of that XCD are using. Rounds end when no request
@@ -120,6 +129,17 @@ struct SparkParams {
   uint32_t stream, key0, key1;
 };
 
+// The kernel's parameters read in place (kernel-argument segment, constant
+// address space): the phases take a pointer to them, made wave-uniform, so
+// their fields are read with scalar loads rather than from a private copy.
+typedef const __attribute__((address_space(4))) SparkParams KParams;
+
+__device__ inline KParams* uniform_params(KParams* q) {
+  const uint64_t v = reinterpret_cast<uint64_t>(q);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v)), hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+  return reinterpret_cast<KParams*>((uint64_t(hi) << 32) | lo);
+}
+
 // Phase-local LDS: the select phase's request state, or the logits phase's
 // staged W1 rows, or the statistics merge lists.
 constexpr size_t kSelectBytes = sizeof(ReqState);
@@ -145,7 +165,7 @@ constexpr size_t kPhaseBytes =
 // acquire-release arrival per workgroup.
 constexpr int kBarWords = 64 + 8 * 64;
 
-__device__ bool grid_sync(const SparkParams& p, uint32_t& gen, int* s_dead) {
+__device__ bool grid_sync(KParams& p, uint32_t& gen, int* s_dead) {
   __syncthreads();
   if (threadIdx.x == 0 && !*s_dead) {
     const int x = blockIdx.x & 7;
@@ -229,8 +249,8 @@ __device__ inline double max_unused_q0(const ReqState& st, int i, bool sampled) 
 __device__ inline void wave_best(float& v, int& id) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(v, o, kWave);
-    const int oi = __shfl_xor(id, o, kWave);
+    const float ov = lane_xor(v, o);
+    const int oi = lane_xor(id, o);
     if (rank_before(ov, oi, v, id)) {
       v = ov;
       id = oi;
@@ -269,7 +289,9 @@ __device__ inline void wave_top(float (&cv)[kC], int (&ci)[kC], int n, float* dv
 // ---------------------------------------------------------------------------
 // Phase A: one request.
 
-__device__ void select_request(const SparkParams& p, int r, int round, ReqState& st, int* s_misc) {
+__device__ __attribute__((noinline)) void select_request(KParams* pin, int r, int round, ReqState& st,
+                                                        int* s_misc) {
+  KParams& p = *uniform_params(pin);
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int N = p.N, K = p.K;
   const int cur = round & 1, prev = cur ^ 1;
@@ -332,11 +354,8 @@ __device__ void select_request(const SparkParams& p, int r, int round, ReqState&
         nprev += c;
         pre += q < r ? c : 0;
       }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        nprev += __shfl_xor(nprev, o, kWave);
-        pre += __shfl_xor(pre, o, kWave);
-      }
+      nprev = wave_sum(nprev);
+      pre = wave_sum(pre);
       const int S = spark_segments(nprev, p.nwg);
       const int mine = p.cnt[size_t(prev) * p.B + r];
       for (int j = 0; j < mine; ++j) {
@@ -346,10 +365,10 @@ __device__ void select_request(const SparkParams& p, int r, int round, ReqState&
         // log-sum-exp of the segments
         double M = lane < S ? double(pp[lane].m) : -INFINITY;
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) M = fmax(M, __shfl_xor(M, o, kWave));
+        for (int o = 32; o > 0; o >>= 1) M = fmax(M, lane_xor(M, o));
         double t = lane < S && pp[lane].m != -INFINITY ? pp[lane].s * exp(double(pp[lane].m) - M) : 0.0;
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, kWave);
+        for (int o = 32; o > 0; o >>= 1) t += lane_xor(t, o);
         // the K+1 best logits and (T > 0) the K best scores over the
         // segments: candidates c = seg * kList + e, up to nine per lane
         constexpr int kC = (kMaxSeg * kList + kWave - 1) / kWave;
@@ -426,14 +445,14 @@ __device__ void select_request(const SparkParams& p, int r, int round, ReqState&
       }
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) {
-        const double ok = __shfl_xor(bk, o, kWave);
-        const int oi = __shfl_xor(bi, o, kWave);
+        const double ok = lane_xor(bk, o);
+        const int oi = lane_xor(bi, o);
         if (ok > bk || (ok == bk && oi < bi)) {
           bk = ok;
           bi = oi;
         }
-        pb = fmax(pb, __shfl_xor(pb, o, kWave));
-        npend += __shfl_xor(npend, o, kWave);
+        pb = fmax(pb, lane_xor(pb, o));
+        npend += lane_xor(npend, o);
       }
       if (npend > 0 && (bi == 0x7fffffff || pb >= bk)) break;  // expand first
       if (bi == 0x7fffffff || bk < logth) {
@@ -509,85 +528,131 @@ __device__ void select_request(const SparkParams& p, int r, int round, ReqState&
 // ---------------------------------------------------------------------------
 // Phase B: logits of the listed rows.
 
-__device__ void logits_phase(const SparkParams& p, int n_act, const int* s_rx, const long long* s_ru,
+// Global-memory views (loads issued as global, not flat, accesses).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(1))) u32x4 g_u32x4;
+typedef const __attribute__((address_space(1))) f32x4 g_f32x4;
+typedef const __attribute__((address_space(1))) float g_float;
+typedef __attribute__((address_space(1))) f32x4 g_out_f32x4;
+
+// A pointer that is the same in every lane, in scalar registers.
+template <typename T>
+__device__ inline T* uniform_ptr(T* q) {
+  const uint64_t v = reinterpret_cast<uint64_t>(q);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v)), hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+  return reinterpret_cast<T*>((uint64_t(hi) << 32) | lo);
+}
+
+// KKc > 0: the rank is 32 KKc (W2 loads and products unconditional);
+// KKc = 0: any rank that is a multiple of 32 up to kMaxRank. kFull: V is a
+// multiple of 16, so every 16-token tile is whole and 16-byte aligned.
+template <int KKc, bool kFull>
+__device__ __attribute__((noinline)) void logits_phase(KParams* pin, int n_act, const int* s_rx, const long long* s_ru,
                              uint16_t* s_w1) {
+  KParams& p = *uniform_params(pin);
+  // the parameters this phase uses, read once into wave-uniform registers
+  // (reads through p inside the loop would be reloads past every store)
+  const int V = __builtin_amdgcn_readfirstlane(p.V), rank = __builtin_amdgcn_readfirstlane(p.r);
+  const int nwg = __builtin_amdgcn_readfirstlane(p.nwg);
+  const uint16_t* w1 = uniform_ptr(p.w1);
+  const float* U = uniform_ptr(p.U);
+  float* ell = uniform_ptr(p.ell);
+  const char* w2 = reinterpret_cast<const char*>(uniform_ptr(p.w2));
   const int tid = threadIdx.x, lane = tid & (kWave - 1), l16 = lane & 15, lg = lane >> 4;
-  const int wave = tid / kWave;
-  const int KK = p.r / 32;
-  const int nt = (p.V + 15) / 16;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  n_act = __builtin_amdgcn_readfirstlane(n_act);
+  constexpr int kK = KKc ? KKc : kMaxRank / 32;
+  const int KK = KKc ? KKc : rank / 32;
+  const int nt = (V + 15) / 16;
   const int gw = blockIdx.x * kSpWaves + wave;
-  const int nwave = p.nwg * kSpWaves;
-  const bool vec = (p.V & 3) == 0;
-  auto load_a = [&](int tile, bf16x8 (&A)[kMaxRank / 32]) __attribute__((always_inline)) {
-    const int tok = min(tile * 16 + l16, p.V - 1);
-#pragma unroll
-    for (int kk = 0; kk < kMaxRank / 32; ++kk)
-      if (kk < KK) A[kk] = *reinterpret_cast<const bf16x8*>(p.w2 + size_t(tok) * p.r + kk * 32 + 8 * lg);
-  };
+  const int nwave = nwg * kSpWaves;
+  const bool vec = (V & 3) == 0;
+  const uint32_t w2_row = uint32_t(rank) * 2u;  // bytes per W2 row (V r 2 < 4 GB)
   for (int g0 = 0; g0 < n_act; g0 += kGroupRows) {
     const int gn = min(kGroupRows, n_act - g0);
     // stage the group's W1 rows (zero past the group)
     __syncthreads();
-    const int chunks = p.r / 8;  // 16-byte pieces per row
+    const int chunks = rank / 8;  // 16-byte pieces per row
     for (int c = tid; c < kGroupRows * chunks; c += kSpThreads) {
       const int row = c / chunks, piece = c - row * chunks;
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (row < gn) v = *reinterpret_cast<const uint4*>(p.w1 + size_t(s_rx[g0 + row]) * p.r + piece * 8);
+      if (row < gn) v = *reinterpret_cast<const uint4*>(w1 + size_t(s_rx[g0 + row]) * rank + piece * 8);
       *reinterpret_cast<uint4*>(s_w1 + row * kW1Stride + piece * 8) = v;
     }
     __syncthreads();
     const int nrt = (gn + 15) / 16;
-    bf16x8 A[kMaxRank / 32], An[kMaxRank / 32];
-    if (gw < nt) load_a(gw, A);
-    for (int tile = gw; tile < nt; tile += nwave) {
-      if (tile + nwave < nt) load_a(tile + nwave, An);  // in flight while this tile is used
+    // this lane's U row in each row tile (rows past the group repeat the
+    // group's last row; their results are not stored)
+    const float* urow[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) urow[rt] = U + s_ru[g0 + min(rt * 16 + l16, gn - 1)];
+    // one tile's operands: W2 rows (A operand) and U of the row tiles
+    auto load_tile = [&](int tile, bf16x8 (&A)[kK], float4 (&uu)[4]) __attribute__((always_inline)) {
+      const uint32_t tok = uint32_t(min(tile * 16 + l16, V - 1));
+      const char* src = w2 + (tok * w2_row + uint32_t(16 * lg));
+#pragma unroll
+      for (int kk = 0; kk < kK; ++kk)
+        if (KKc || kk < KK) A[kk] = __builtin_bit_cast(bf16x8, *(g_u32x4*)(src + kk * 64));
       const int y0 = tile * 16 + 4 * lg;
-      // U of the four row tiles, loaded before the products
-      float4 uu[4];
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        const int g = g0 + rt * 16 + l16;
-        uu[rt] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (rt < nrt && g < g0 + gn) {
-          const float* u = p.U + s_ru[g];
-          if (vec && y0 + 3 < p.V) {
-            uu[rt] = *reinterpret_cast<const float4*>(u + y0);
-          } else {
-            uu[rt].x = y0 < p.V ? u[y0] : 0.f;
-            uu[rt].y = y0 + 1 < p.V ? u[y0 + 1] : 0.f;
-            uu[rt].z = y0 + 2 < p.V ? u[y0 + 2] : 0.f;
-            uu[rt].w = y0 + 3 < p.V ? u[y0 + 3] : 0.f;
-          }
+        if (kFull) {  // every row tile (absent ones repeat a loaded row: cache hits)
+          const f32x4 v = *(g_f32x4*)(urow[rt] + y0);
+          uu[rt] = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+          if (rt >= nrt) break;
+          const g_float* u = (g_float*)urow[rt];
+          uu[rt].x = y0 < V ? u[y0] : 0.f;
+          uu[rt].y = y0 + 1 < V ? u[y0 + 1] : 0.f;
+          uu[rt].z = y0 + 2 < V ? u[y0 + 2] : 0.f;
+          uu[rt].w = y0 + 3 < V ? u[y0 + 3] : 0.f;
         }
       }
+    };
+    auto use_tile = [&](int tile, const bf16x8 (&A)[kK], const float4 (&uu)[4]) __attribute__((always_inline)) {
+      const int y0 = tile * 16 + 4 * lg;
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         if (rt >= nrt) break;
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
         const uint16_t* brow = s_w1 + (rt * 16 + l16) * kW1Stride + 8 * lg;
 #pragma unroll
-        for (int kk = 0; kk < kMaxRank / 32; ++kk)
-          if (kk < KK)
+        for (int kk = 0; kk < kK; ++kk)
+          if (KKc || kk < KK)
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[kk], *reinterpret_cast<const bf16x8*>(brow + kk * 32),
                                                           acc, 0, 0, 0);
         // lane holds row g, tokens y0 .. y0 + 3
         const int g = g0 + rt * 16 + l16;
         if (g < g0 + gn) {
-          float* out = p.ell + size_t(g) * p.V;
+          float* out = ell + size_t(g) * V;
           const float4 o = make_float4(acc[0] + uu[rt].x, acc[1] + uu[rt].y, acc[2] + uu[rt].z,
                                        acc[3] + uu[rt].w);
-          if (vec && y0 + 3 < p.V) {
+          if (kFull) {
+            *(g_out_f32x4*)(out + y0) = f32x4{o.x, o.y, o.z, o.w};
+          } else if (vec && y0 + 3 < V) {
             *reinterpret_cast<float4*>(out + y0) = o;
           } else {
-            if (y0 < p.V) out[y0] = o.x;
-            if (y0 + 1 < p.V) out[y0 + 1] = o.y;
-            if (y0 + 2 < p.V) out[y0 + 2] = o.z;
-            if (y0 + 3 < p.V) out[y0 + 3] = o.w;
+            if (y0 < V) out[y0] = o.x;
+            if (y0 + 1 < V) out[y0 + 1] = o.y;
+            if (y0 + 2 < V) out[y0 + 2] = o.z;
+            if (y0 + 3 < V) out[y0 + 3] = o.w;
           }
         }
       }
-#pragma unroll
-      for (int kk = 0; kk < kMaxRank / 32; ++kk) A[kk] = An[kk];
+    };
+    // two tiles' operands in registers: the next tile in flight while one
+    // is used. The loads are unconditional (a wave's last prefetch reloads
+    // the final tile, which every wave reads: cache hits) so that the wait
+    // before each product covers only the loads of the tile it uses.
+    bf16x8 A0[kK], A1[kK];
+    float4 U0[4], U1[4];
+    if (gw < nt) load_tile(gw, A0, U0);
+    for (int t = gw; t < nt; t += 2 * nwave) {
+      load_tile(min(t + nwave, nt - 1), A1, U1);
+      use_tile(t, A0, U0);
+      if (t + nwave >= nt) break;
+      load_tile(min(t + 2 * nwave, nt - 1), A0, U0);
+      use_tile(t + nwave, A1, U1);
     }
   }
 }
@@ -596,7 +661,7 @@ __device__ void logits_phase(const SparkParams& p, int n_act, const int* s_rx, c
 // Phase C: statistics of one (row, segment).
 
 template <int L>
-__device__ void stats_item(const SparkParams& p, int g, int seg, int S, int req, int node, float T,
+__device__ void stats_item(KParams& p, int g, int seg, int S, int req, int node, float T,
                            float* s_v, int* s_i, double* s_d, float* m_v, int* m_i) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int K = p.K, nl = K + 1;
@@ -654,26 +719,18 @@ __device__ void stats_item(const SparkParams& p, int g, int seg, int S, int req,
         s += __builtin_amdgcn_exp2f((v[0] - m) * kLog2e) + __builtin_amdgcn_exp2f((v[1] - m) * kLog2e) +
              __builtin_amdgcn_exp2f((v[2] - m) * kLog2e) + __builtin_amdgcn_exp2f((v[3] - m) * kLog2e);
       }
-      if (__builtin_amdgcn_ballot_w64(in && (mx >= thA) && (mx > A.v[L - 1])) != 0 && in) {
+      // each value's insert runs only where some lane's own value qualifies
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (v[e] >= thA) A.insert(v[e], y + e);
-      }
+      for (int e = 0; e < 4; ++e)
+        if (in && v[e] >= thA && v[e] > A.v[L - 1]) A.insert(v[e], y + e);
       if (noisy) {
         const uint4 w4 = philox4x32_10(make_uint4(uint32_t(q), node_row, p.stream, 0u), p.key0, p.key1);
         const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
-        float bmax = -INFINITY;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float x = (float(16777216u - (w[e] >> 8)) - 0.5f) * (1.f / 16777216.f);  // 1 - u
-          bmax = fmaxf(bmax, v[e] * invT - __logf(x) + 1e-3f);  // g <= -ln(1 - u)
-        }
-        if (__builtin_amdgcn_ballot_w64(in && (bmax >= thG) && (bmax > G.v[L - 1])) != 0 && in) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (v[e] == -INFINITY) continue;
-            const float x = (float(16777216u - (w[e] >> 8)) - 0.5f) * (1.f / 16777216.f);
-            if (v[e] * invT - __logf(x) + 1e-3f < thG) continue;
+          const float bound = v[e] * invT - __logf(x) + 1e-3f;                             // g <= -ln(1 - u)
+          if (in && v[e] != -INFINITY && bound >= thG && bound > G.v[L - 1]) {
             const float uu = (float(w[e] >> 8) + 0.5f) * (1.f / 16777216.f);
             const float en = uu > 0.5f ? -log1pf(-x) : -logf(uu);  // -ln u, accurate near u = 1
             G.insert(v[e] * invT - logf(en), y + e);
@@ -693,13 +750,13 @@ __device__ void stats_item(const SparkParams& p, int g, int seg, int S, int req,
   // log-sum-exp partial: block maximum, then the rescaled sums in fp64
   float M = m;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, lane_xor(M, o));
   if (lane == 0) s_v[wave] = M;
   __syncthreads();
   M = fmaxf(fmaxf(s_v[0], s_v[1]), fmaxf(s_v[2], s_v[3]));
   double sd = m == -INFINITY ? 0.0 : double(s) * exp(double(m) - double(M));
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) sd += __shfl_xor(sd, o, kWave);
+  for (int o = 32; o > 0; o >>= 1) sd += lane_xor(sd, o);
   if (lane == 0) s_d[wave] = sd;
   // the lists: each wave's n best by shuffles, then one wave over the waves'
   auto wave_list = [&](TopList<L>& Lst, int n, float* dv, int* di) __attribute__((always_inline)) {
@@ -748,7 +805,9 @@ __device__ void stats_item(const SparkParams& p, int g, int seg, int S, int req,
 }
 
 template <int L>
-__global__ __launch_bounds__(kSpThreads) void spark_kernel(SparkParams p) {
+__global__ __launch_bounds__(kSpThreads, 2) void spark_kernel(SparkParams params) {
+  KParams* pk = (KParams*)__builtin_amdgcn_kernarg_segment_ptr();  // the first argument is at offset 0
+  KParams& p = *pk;
   __shared__ __align__(16) unsigned char s_phase[kPhaseBytes];
   __shared__ int s_rx[kSparkMaxRows];
   __shared__ long long s_ru[kSparkMaxRows];
@@ -768,7 +827,7 @@ __global__ __launch_bounds__(kSpThreads) void spark_kernel(SparkParams p) {
   uint32_t expanded = 0;
   for (int round = 0; round <= p.N + 2; ++round) {
     for (int r = blockIdx.x; r < p.B; r += p.nwg) {
-      select_request(p, r, round, st, s_misc);
+      select_request(pk, r, round, st, s_misc);
       __syncthreads();
     }
     if (!grid_sync(p, gen, &s_dead)) return;
@@ -807,7 +866,10 @@ __global__ __launch_bounds__(kSpThreads) void spark_kernel(SparkParams p) {
       return;
     }
     expanded += uint32_t(n_act);
-    logits_phase(p, n_act, s_rx, s_ru, s_w1);
+    if (p.r == 256 && p.V % 16 == 0)
+      logits_phase<8, true>(pk, n_act, s_rx, s_ru, s_w1);
+    else
+      logits_phase<0, false>(pk, n_act, s_rx, s_ru, s_w1);
     if (!grid_sync(p, gen, &s_dead)) return;
     const int S = spark_segments(n_act, p.nwg);
     for (int it = blockIdx.x; it < n_act * S; it += p.nwg) {

@@ -130,6 +130,7 @@ constexpr int kSparkRowsPerRound = 4;   // expansions per request per round
 constexpr int kSparkMaxBatch = 256;
 constexpr int kSparkMaxRows = kSparkMaxBatch * kSparkRowsPerRound;
 constexpr int kSparkMaxDepths = 16;
+constexpr int kSparkMaxVocab = 1 << 22;  // w2 (V x r bf16) stays under 4 GB: 32-bit load offsets
 // Segments per expanded row in the statistics phase: at most one item per
 // workgroup, at most kSparkMaxSeg.
 constexpr int kSparkMaxSeg = 32;

@@ -10,14 +10,15 @@
 namespace tv {
 
 // The K-th largest (K <= 64) of one value per lane, by a bitonic sort across
-// the wave (descending), read from lane K-1.
+// the wave (descending, partners exchanged by VALU cross-lane moves; every
+// lane must be active), read from lane K-1.
 __device__ inline float wave_kth_largest(float v, int K) {
   const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
   for (int size = 2; size <= kWave; size <<= 1) {
 #pragma unroll
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const float o = shfl_xor(v, stride);
+      const float o = lane_xor(v, stride);
       const bool desc = (lane & size) == 0;  // this block of `size` lanes sorts descending
       const bool low = (lane & stride) == 0;
       v = (low == desc) ? fmaxf(v, o) : fminf(v, o);
