@@ -86,7 +86,9 @@ struct ReqState {
   float top_l[kNodes][kList];
   int drw_id[kNodes][kList]; // T > 0: the K first without-replacement draws
   float drw_l[kNodes][kList];
-  int pad[3];
+  double lph_top[kNodes][kList];      // log p_hat of each top logit's q0
+  double lph_drw[kNodes][kList];      // T > 0: log p_hat of each draw's q0
+  uint8_t unused_e[kNodes][kList];    // T > 0: first top entry not among the first j draws
 };
 static_assert(sizeof(ReqState) % 16 == 0, "state is copied in 16-byte units");
 
@@ -229,21 +231,6 @@ __device__ inline bool rank_before(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
-// Largest q0 among node i's tokens not yet used as its children.
-__device__ inline double max_unused_q0(const ReqState& st, int i, bool sampled) {
-  const int nch = st.nch[i];
-  int e = nch;  // greedy: the children are the first nch of the logit order
-  if (sampled) {
-    e = 0;
-    for (; e < kList; ++e) {
-      bool used = false;
-      for (int j = 0; j < nch; ++j) used |= st.drw_id[i][j] == st.top_id[i][e];
-      if (!used) break;
-    }
-  }
-  return exp(double(st.top_l[i][e]) - st.lse[i]);
-}
-
 // Wave argmax over (value, id) candidates, larger value then lower id; every
 // lane returns the winner.
 __device__ inline void wave_best(float& v, int& id) {
@@ -258,24 +245,25 @@ __device__ inline void wave_best(float& v, int& id) {
   }
 }
 
-// n rounds of a wave argmax over kC candidates per lane; the k-th winner goes
-// to (dv[k], di[k]) through lane 0.
+// n rounds of a wave argmax over the first nc of kC candidates per lane
+// (nc the same in every lane); the k-th winner goes to (dv[k], di[k])
+// through lane 0.
 template <int kC>
-__device__ inline void wave_top(float (&cv)[kC], int (&ci)[kC], int n, float* dv, int* di) {
+__device__ inline void wave_top(float (&cv)[kC], int (&ci)[kC], int nc, int n, float* dv, int* di) {
   const int lane = threadIdx.x & (kWave - 1);
   for (int k = 0; k < n; ++k) {
     float bv = cv[0];
     int bi = ci[0];
 #pragma unroll
     for (int u = 1; u < kC; ++u)
-      if (rank_before(cv[u], ci[u], bv, bi)) {
+      if (u < nc && rank_before(cv[u], ci[u], bv, bi)) {
         bv = cv[u];
         bi = ci[u];
       }
     wave_best(bv, bi);
 #pragma unroll
     for (int u = 0; u < kC; ++u)
-      if (ci[u] == bi) {
+      if (u < nc && ci[u] == bi) {
         cv[u] = -INFINITY;
         ci[u] = 0x7fffffff;
       }
@@ -286,11 +274,29 @@ __device__ inline void wave_top(float (&cv)[kC], int (&ci)[kC], int n, float* dv
   }
 }
 
+// A request's head (done, drafted nodes) into s_pf[0..1] and, unless done,
+// its state into LDS; s_pf[2] = 1 marks them loaded.
+__device__ inline void load_request(KParams& p, int r, ReqState& st, int* s_pf) {
+  constexpr int kWords = int(sizeof(ReqState) / 16);
+  if (threadIdx.x == 0) {
+    s_pf[0] = p.head[r].done;
+    s_pf[1] = p.head[r].count;
+  }
+  __syncthreads();
+  if (!s_pf[0]) {
+    const uint4* src = reinterpret_cast<const uint4*>(p.state + r);
+    uint4* dst = reinterpret_cast<uint4*>(&st);
+    for (int i = threadIdx.x; i < kWords; i += kSpThreads) dst[i] = src[i];
+  }
+  if (threadIdx.x == 0) s_pf[2] = 1;
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
 // Phase A: one request.
 
 __device__ __attribute__((noinline)) void select_request(KParams* pin, int r, int round, ReqState& st,
-                                                        int* s_misc) {
+                                                        int* s_misc, int* s_pf) {
   KParams& p = *uniform_params(pin);
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int N = p.N, K = p.K;
@@ -327,27 +333,28 @@ __device__ __attribute__((noinline)) void select_request(KParams* pin, int r, in
       s_misc[1] = 0;  // drafted nodes
     }
   } else {
+    // the request's state, unless the workgroup loaded it at the end of the
+    // last round (its only request)
+    if (!s_pf[2]) load_request(p, r, st, s_pf);
     if (tid == 0) {
-      s_misc[0] = hd->done;
-      s_misc[1] = hd->count;
-    }
-    __syncthreads();
-    if (!s_misc[0]) {  // request state into LDS
-      const uint4* src = reinterpret_cast<const uint4*>(p.state + r);
-      uint4* dst = reinterpret_cast<uint4*>(&st);
-      for (int i = tid; i < kWords; i += kSpThreads) dst[i] = src[i];
+      s_misc[0] = s_pf[0];
+      s_misc[1] = s_pf[1];
     }
   }
   __syncthreads();
+  if (tid == 0) s_pf[2] = 0;
   if (s_misc[0]) {
     if (tid == 0) p.cnt[size_t(cur) * p.B + r] = 0;
     return;
   }
   const int count0 = s_misc[1];
 
-  if (tid < kWave) {
-    // --- merge last round's statistics of this request's listed nodes
-    if (round > 0) {
+  const double ca = p.a, cb = p.b;
+  // --- merge last round's statistics of this request's listed nodes, one
+  // node per wave (each touches only its own node's entries)
+  if (round > 0) {
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    {
       int nprev = 0, pre = 0;
       for (int q = lane; q < p.B; q += kWave) {
         const int c = p.cnt[size_t(prev) * p.B + q];
@@ -358,7 +365,7 @@ __device__ __attribute__((noinline)) void select_request(KParams* pin, int r, in
       pre = wave_sum(pre);
       const int S = spark_segments(nprev, p.nwg);
       const int mine = p.cnt[size_t(prev) * p.B + r];
-      for (int j = 0; j < mine; ++j) {
+      for (int j = wave; j < mine; j += kSpWaves) {
         const int i = p.rows[(size_t(prev) * p.B + r) * kRows + j];
         const size_t g = size_t(pre + j);
         const Part* pp = p.part + g * kMaxSeg;
@@ -370,24 +377,28 @@ __device__ __attribute__((noinline)) void select_request(KParams* pin, int r, in
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) t += lane_xor(t, o);
         // the K+1 best logits and (T > 0) the K best scores over the
-        // segments: candidates c = seg * kList + e, up to nine per lane
+        // segments: candidates c = seg * n + e (n = K+1, resp. K), packed so
+        // only the first ceil(S n / 64) slots of a lane are used
         constexpr int kC = (kMaxSeg * kList + kWave - 1) / kWave;
         const int nl = K + 1;
+        const int ncl = (S * nl + kWave - 1) / kWave, ncg = (S * K + kWave - 1) / kWave;
         float cv[kC], gv[kC];
         int ci[kC], gi[kC];
 #pragma unroll
         for (int u = 0; u < kC; ++u) {
-          const int c = lane + u * kWave, sg = c / kList, e = c - sg * kList;
-          const bool ok = sg < S && e < nl;
+          const int c = lane + u * kWave;
+          const int sg = c / nl, e = c - sg * nl;
+          const bool ok = u < ncl && sg < S;
           cv[u] = ok ? pp[sg].tv[e] : -INFINITY;
           ci[u] = ok ? pp[sg].ti[e] : 0x7fffffff;
-          const bool okg = sampled && sg < S && e < K;
-          gv[u] = okg ? pp[sg].gv[e] : -INFINITY;
-          gi[u] = okg ? pp[sg].gi[e] : 0x7fffffff;
+          const int sgg = c / K, eg = c - sgg * K;
+          const bool okg = sampled && u < ncg && sgg < S;
+          gv[u] = okg ? pp[sgg].gv[eg] : -INFINITY;
+          gi[u] = okg ? pp[sgg].gi[eg] : 0x7fffffff;
         }
-        wave_top(cv, ci, nl, st.top_l[i], st.top_id[i]);
-        if (sampled) wave_top(gv, gi, K, st.drw_l[i], st.drw_id[i]);
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        wave_top(cv, ci, ncl, nl, st.top_l[i], st.top_id[i]);
+        if (sampled) wave_top(gv, gi, ncg, K, st.drw_l[i], st.drw_id[i]);
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
         // fewer than K+1 candidates only with non-finite logits (already
         // reported): keep every id a valid row of W1; the drawn tokens'
@@ -406,43 +417,83 @@ __device__ __attribute__((noinline)) void select_request(KParams* pin, int r, in
           st.drw_id[i][lane] = y;
           st.drw_l[i][lane] = row[y];
         }
+        const double lse_i = M + log(t);
         if (lane == 0) {
-          st.lse[i] = M + log(t);
+          st.lse[i] = lse_i;
           st.state[i] = 2;
-          if (!(t > 0.0) || !isfinite(st.lse[i])) raise_status(p.status, TV_DEV_LOGITS);
+          if (!(t > 0.0) || !isfinite(lse_i)) raise_status(p.status, TV_DEV_LOGITS);
         }
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        // tables for the pops: log p_hat of each top logit's and each
+        // draw's q0 (the child's factor of its path survival), and at T > 0
+        // the first top entry whose token is not among the first j draws
+        // (the node's largest unused q0 after j children), j = 0..K
+        if (lane < nl) st.lph_top[i][lane] = log_p_hat(exp(double(st.top_l[i][lane]) - lse_i), ca, cb);
+        if (sampled) {
+          if (lane < K) st.lph_drw[i][lane] = log_p_hat(exp(double(st.drw_l[i][lane]) - lse_i), ca, cb);
+          int fd = K;  // the first draw of top entry `lane`'s token, K if none
+          if (lane < nl) {
+            const int y = st.top_id[i][lane];
+            for (int j = 0; j < K; ++j)
+              if (fd == K && st.drw_id[i][j] == y) fd = j;
+          }
+          for (int j = 0; j <= K; ++j) {
+            const uint64_t m = __builtin_amdgcn_ballot_w64(lane < nl && fd >= j);
+            if (lane == j) st.unused_e[i][j] = uint8_t(m ? min(__builtin_ctzll(m), kList - 1) : kList - 1);
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
       }
     }
+  }
+  __syncthreads();
 
-    // --- pops
+  if (tid < kWave) {
+    // --- pops. Each lane caches the slot key and the pending bound of its
+    // nodes (lane and lane + 64); a pop changes only the popped node's key
+    // (one more child) and adds one pending node, so only those two are
+    // recomputed.
     int count = count0;
     int done = 0;
-    const double ca = p.a, cb = p.b;
+    static_assert(kNodes <= 2 * kWave, "two nodes per lane");
+    double key[2], pend[2];
+    bool keyed[2], pending[2];
+    auto refresh = [&](int k) __attribute__((always_inline)) {
+      const int i = lane + k * kWave;
+      keyed[k] = pending[k] = false;
+      key[k] = pend[k] = -INFINITY;
+      if (i > count || st.dep[i] >= p.depths) return;
+      if (st.state[i] == 2) {
+        const int nch = st.nch[i];
+        if (nch < K) {
+          keyed[k] = true;
+          key[k] = st.logS[i] + st.lph_top[i][sampled ? int(st.unused_e[i][nch]) : nch];
+        }
+      } else if (st.logS[i] >= logth) {
+        pending[k] = true;
+        pend[k] = st.logS[i];
+      }
+    };
+    refresh(0);
+    refresh(1);
     while (true) {
       if (count >= N) {
         done = 1;
         break;
       }
+      // best slot (larger key, then lower node index), pending bound and count
       double bk = -INFINITY;
-      int bi = 0x7fffffff, npend = 0;
-      double pb = -INFINITY;
-      for (int i = lane; i <= count; i += kWave) {
-        if (st.dep[i] >= p.depths) continue;
-        if (st.state[i] == 2) {
-          if (st.nch[i] < K) {
-            const double key = st.logS[i] + log_p_hat(max_unused_q0(st, i, sampled), ca, cb);
-            if (key > bk || (key == bk && i < bi)) {
-              bk = key;
-              bi = i;
-            }
-          }
-        } else if (st.logS[i] >= logth) {
-          pb = fmax(pb, st.logS[i]);
-          ++npend;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        if (keyed[k] && (key[k] > bk || (key[k] == bk && lane + k * kWave < bi))) {
+          bk = key[k];
+          bi = lane + k * kWave;
         }
-      }
+      double pb = fmax(pend[0], pend[1]);
+      int npend = (pending[0] ? 1 : 0) + (pending[1] ? 1 : 0);
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) {
         const double ok = lane_xor(bk, o);
@@ -460,12 +511,11 @@ __device__ __attribute__((noinline)) void select_request(KParams* pin, int r, in
         break;
       }
       if (npend >= kRows) break;
-      // pop the slot of node v
+      // pop the slot of node v (the node outputs are written after the loop)
       const int v = __builtin_amdgcn_readfirstlane(bi);
       const int j = st.nch[v];
       const int x = sampled ? st.drw_id[v][j] : st.top_id[v][j];
-      const float lx = sampled ? st.drw_l[v][j] : st.top_l[v][j];
-      const double lS = st.logS[v] + log_p_hat(exp(double(lx) - st.lse[v]), ca, cb);
+      const double lS = st.logS[v] + (sampled ? st.lph_drw[v][j] : st.lph_top[v][j]);
       const int c = count + 1;
       const int dv = st.dep[v];
       __builtin_amdgcn_wave_barrier();
@@ -478,14 +528,19 @@ __device__ __attribute__((noinline)) void select_request(KParams* pin, int r, in
         st.logS[c] = lS;
         st.lse[c] = 0.0;
         st.nch[v] = j + 1;
-        const size_t o = size_t(r) * (N + 1) + c;
-        p.out_parent[o] = v;
-        p.out_token[o] = x;
-        if (p.out_logs) p.out_logs[o] = float(lS);
       }
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // LDS, within this wave
       __builtin_amdgcn_wave_barrier();
       count = c;
+      if (lane == (v & (kWave - 1))) refresh(v / kWave);
+      if (lane == (c & (kWave - 1))) refresh(c / kWave);
+    }
+    // the nodes materialised this round
+    for (int c = count0 + 1 + lane; c <= count; c += kWave) {
+      const size_t o = size_t(r) * (N + 1) + c;
+      p.out_parent[o] = st.par[c];
+      p.out_token[o] = st.tok[c];
+      if (p.out_logs) p.out_logs[o] = float(st.logS[c]);
     }
     // --- list the nodes to expand (not when done)
     int listed = 0;
@@ -785,7 +840,7 @@ __device__ void stats_item(KParams& p, int g, int seg, int S, int req, int node,
       cv[u] = ok ? m_v[w * kList + e] : -INFINITY;
       ci[u] = ok ? m_i[w * kList + e] : 0x7fffffff;
     }
-    wave_top(cv, ci, nl, out->tv, out->ti);
+    wave_top(cv, ci, kC, nl, out->tv, out->ti);
     if (noisy) {
 #pragma unroll
       for (int u = 0; u < kC; ++u) {
@@ -794,7 +849,7 @@ __device__ void stats_item(KParams& p, int g, int seg, int S, int req, int node,
         cv[u] = ok ? m_v[(kSpWaves + w) * kList + e] : -INFINITY;
         ci[u] = ok ? m_i[(kSpWaves + w) * kList + e] : 0x7fffffff;
       }
-      wave_top(cv, ci, K, out->gv, out->gi);
+      wave_top(cv, ci, kC, K, out->gv, out->gi);
     }
     if (lane == 0) {
       out->m = M;
@@ -816,8 +871,12 @@ __global__ __launch_bounds__(kSpThreads, 2) void spark_kernel(SparkParams params
   __shared__ int s_i[kSpWaves];
   __shared__ double s_d[kSpWaves];
   __shared__ int s_misc[4];
+  __shared__ int s_pf[3];  // prefetched request head (done, count), loaded flag
   __shared__ int s_dead;
-  if (threadIdx.x == 0) s_dead = 0;
+  if (threadIdx.x == 0) {
+    s_dead = 0;
+    s_pf[2] = 0;
+  }
   __syncthreads();
   ReqState& st = *reinterpret_cast<ReqState*>(s_phase);
   uint16_t* s_w1 = reinterpret_cast<uint16_t*>(s_phase);
@@ -827,7 +886,7 @@ __global__ __launch_bounds__(kSpThreads, 2) void spark_kernel(SparkParams params
   uint32_t expanded = 0;
   for (int round = 0; round <= p.N + 2; ++round) {
     for (int r = blockIdx.x; r < p.B; r += p.nwg) {
-      select_request(pk, r, round, st, s_misc);
+      select_request(pk, r, round, st, s_misc, s_pf);
       __syncthreads();
     }
     if (!grid_sync(p, gen, &s_dead)) return;
@@ -876,6 +935,9 @@ __global__ __launch_bounds__(kSpThreads, 2) void spark_kernel(SparkParams params
       const int g = it / S, seg = it - g * S;
       stats_item<L>(p, g, seg, S, s_rq[g], s_rn[g], p.temperature[s_rq[g]], s_v, s_i, s_d, m_v, m_i);
     }
+    // a workgroup with one request loads its state for the next round now,
+    // while the grid gathers at the barrier
+    if (p.B <= p.nwg && int(blockIdx.x) < p.B) load_request(p, blockIdx.x, st, s_pf);
     if (!grid_sync(p, gen, &s_dead)) return;
   }
 }
