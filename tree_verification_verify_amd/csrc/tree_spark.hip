@@ -147,9 +147,11 @@ __device__ inline KParams* uniform_params(KParams* q) {
 constexpr size_t kSelectBytes = sizeof(ReqState);
 constexpr size_t kW1Bytes = size_t(kGroupRows) * kW1Stride * 2;
 constexpr size_t kMergeBytes = size_t(kSpWaves) * kList * 8 * 2;
-constexpr size_t kPhaseBytes =
+constexpr size_t kPhaseMax =
     kSelectBytes > kW1Bytes ? (kSelectBytes > kMergeBytes ? kSelectBytes : kMergeBytes)
                             : (kW1Bytes > kMergeBytes ? kW1Bytes : kMergeBytes);
+// whole 1 KB blocks: the state is loaded a wave-wide 1 KB block at a time
+constexpr size_t kPhaseBytes = (kPhaseMax + 1023) / 1024 * 1024;
 
 // ---------------------------------------------------------------------------
 // Grid barrier, in two levels along the XCDs (block b runs on XCD b % 8,
@@ -167,8 +169,10 @@ constexpr size_t kPhaseBytes =
 // acquire-release arrival per workgroup.
 constexpr int kBarWords = 64 + 8 * 64;
 
-__device__ bool grid_sync(KParams& p, uint32_t& gen, int* s_dead) {
+template <typename During>
+__device__ bool grid_sync(KParams& p, uint32_t& gen, int* s_dead, During&& during) {
   __syncthreads();
+  during();  // work whose memory latency may overlap the wait (no LDS, no barrier)
   if (threadIdx.x == 0 && !*s_dead) {
     const int x = blockIdx.x & 7;
     const uint32_t members = uint32_t((p.nwg - x + 7) / 8);  // workgroups on XCD x
@@ -214,6 +218,10 @@ __device__ bool grid_sync(KParams& p, uint32_t& gen, int* s_dead) {
   gen += 1u;
   __syncthreads();
   return !*reinterpret_cast<volatile int*>(s_dead);
+}
+
+__device__ bool grid_sync(KParams& p, uint32_t& gen, int* s_dead) {
+  return grid_sync(p, gen, s_dead, [] {});
 }
 
 // ---------------------------------------------------------------------------
@@ -274,13 +282,16 @@ __device__ inline void wave_top(float (&cv)[kC], int (&ci)[kC], int nc, int n, f
   }
 }
 
-// A request's head (done, drafted nodes) into s_pf[0..1] and, unless done,
-// its state into LDS; s_pf[2] = 1 marks them loaded.
+// A request's head (done, drafted nodes) into s_pf[0..1], its temperature
+// and theta (bits) into s_pf[3..4] and, unless done, its state into LDS;
+// s_pf[2] = 1 marks them loaded.
 __device__ inline void load_request(KParams& p, int r, ReqState& st, int* s_pf) {
   constexpr int kWords = int(sizeof(ReqState) / 16);
   if (threadIdx.x == 0) {
     s_pf[0] = p.head[r].done;
     s_pf[1] = p.head[r].count;
+    s_pf[3] = __float_as_int(p.temperature[r]);
+    s_pf[4] = __float_as_int(p.theta[r]);
   }
   __syncthreads();
   if (!s_pf[0]) {
@@ -301,9 +312,10 @@ __device__ __attribute__((noinline)) void select_request(KParams* pin, int r, in
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int N = p.N, K = p.K;
   const int cur = round & 1, prev = cur ^ 1;
-  const float T = p.temperature[r];
+  const bool pre = round > 0 && s_pf[2];  // loaded at the end of the last round
+  const float T = pre ? __int_as_float(s_pf[3]) : p.temperature[r];
   const bool sampled = T > 0.f;
-  const float th = p.theta[r];
+  const float th = pre ? __int_as_float(s_pf[4]) : p.theta[r];
   const double logth = th > 0.f ? log(double(th)) : -INFINITY;
   ReqHead* hd = p.head + r;
   int* my_rows = p.rows + (size_t(cur) * p.B + r) * kRows;
@@ -403,7 +415,6 @@ __device__ __attribute__((noinline)) void select_request(KParams* pin, int r, in
         // fewer than K+1 candidates only with non-finite logits (already
         // reported): keep every id a valid row of W1; the drawn tokens'
         // logits are read back from the row, all at once
-        const float* row = p.ell + g * size_t(p.V);
         if (lane < nl) {
           const int y = st.top_id[i][lane];
           if (y < 0 || y >= p.V) {
@@ -415,7 +426,7 @@ __device__ __attribute__((noinline)) void select_request(KParams* pin, int r, in
           int y = st.drw_id[i][lane];
           if (y < 0 || y >= p.V) y = 0;
           st.drw_id[i][lane] = y;
-          st.drw_l[i][lane] = row[y];
+          st.drw_l[i][lane] = p.ell[g * size_t(p.V) + y];
         }
         const double lse_i = M + log(t);
         if (lane == 0) {
@@ -813,44 +824,46 @@ __device__ void stats_item(KParams& p, int g, int seg, int S, int req, int node,
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) sd += lane_xor(sd, o);
   if (lane == 0) s_d[wave] = sd;
-  // the lists: each wave's n best by shuffles, then one wave over the waves'
-  auto wave_list = [&](TopList<L>& Lst, int n, float* dv, int* di) __attribute__((always_inline)) {
-    for (int k = 0; k < n; ++k) {
-      float bv = Lst.v[0];
-      int bi = Lst.i[0];
-      wave_best(bv, bi);
-      if (Lst.i[0] == bi && bi != 0x7fffffff) Lst.pop();
+  // the lists: each wave's n best by cross-lane reductions, then one wave
+  // over the waves'
+  for (int k = 0; k < nl; ++k) {
+    float bv = A.v[0];
+    int bi = A.i[0];
+    wave_best(bv, bi);
+    if (A.i[0] == bi && bi != 0x7fffffff) A.pop();
+    if (lane == 0) {
+      m_v[wave * kList + k] = bv;
+      m_i[wave * kList + k] = bi;
+    }
+  }
+  if (noisy)
+    for (int k = 0; k < K; ++k) {
+      float hv = G.v[0];
+      int hi = G.i[0];
+      wave_best(hv, hi);
+      if (G.i[0] == hi && hi != 0x7fffffff) G.pop();
       if (lane == 0) {
-        dv[k] = bv;
-        di[k] = bi;
+        m_v[(kSpWaves + wave) * kList + k] = hv;
+        m_i[(kSpWaves + wave) * kList + k] = hi;
       }
     }
-  };
-  wave_list(A, nl, m_v + wave * kList, m_i + wave * kList);
-  if (noisy) wave_list(G, K, m_v + (kSpWaves + wave) * kList, m_i + (kSpWaves + wave) * kList);
   __syncthreads();
   if (tid < kWave) {
     constexpr int kC = (kSpWaves * kList + kWave - 1) / kWave;
-    float cv[kC];
-    int ci[kC];
+    float cv[kC], gv[kC];
+    int ci[kC], gi[kC];
 #pragma unroll
     for (int u = 0; u < kC; ++u) {
       const int c = lane + u * kWave, w = c / kList, e = c - w * kList;
       const bool ok = w < kSpWaves && e < nl;
       cv[u] = ok ? m_v[w * kList + e] : -INFINITY;
       ci[u] = ok ? m_i[w * kList + e] : 0x7fffffff;
+      const bool okg = noisy && w < kSpWaves && e < K;
+      gv[u] = okg ? m_v[(kSpWaves + w) * kList + e] : -INFINITY;
+      gi[u] = okg ? m_i[(kSpWaves + w) * kList + e] : 0x7fffffff;
     }
     wave_top(cv, ci, kC, nl, out->tv, out->ti);
-    if (noisy) {
-#pragma unroll
-      for (int u = 0; u < kC; ++u) {
-        const int c = lane + u * kWave, w = c / kList, e = c - w * kList;
-        const bool ok = w < kSpWaves && e < K;
-        cv[u] = ok ? m_v[(kSpWaves + w) * kList + e] : -INFINITY;
-        ci[u] = ok ? m_i[(kSpWaves + w) * kList + e] : 0x7fffffff;
-      }
-      wave_top(cv, ci, kC, K, out->gv, out->gi);
-    }
+    if (noisy) wave_top(gv, gi, kC, K, out->gv, out->gi);
     if (lane == 0) {
       out->m = M;
       out->s = (s_d[0] + s_d[1]) + (s_d[2] + s_d[3]);
@@ -871,7 +884,7 @@ __global__ __launch_bounds__(kSpThreads, 2) void spark_kernel(SparkParams params
   __shared__ int s_i[kSpWaves];
   __shared__ double s_d[kSpWaves];
   __shared__ int s_misc[4];
-  __shared__ int s_pf[3];  // prefetched request head (done, count), loaded flag
+  __shared__ int s_pf[5];  // prefetched request: done, count, loaded flag, temperature, theta
   __shared__ int s_dead;
   if (threadIdx.x == 0) {
     s_dead = 0;
@@ -884,6 +897,11 @@ __global__ __launch_bounds__(kSpThreads, 2) void spark_kernel(SparkParams params
   int* m_i = reinterpret_cast<int*>(s_phase + size_t(2) * kSpWaves * kList * sizeof(float));
   uint32_t gen = __hip_atomic_load(p.bar + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   uint32_t expanded = 0;
+  // state prefetch (a workgroup whose only request is blockIdx.x)
+  constexpr int kStateBlocks = int((sizeof(ReqState) + 1023) / 1024);
+  static_assert(size_t(kStateBlocks) * 1024 <= kPhaseBytes, "the state's blocks fit the phase area");
+  const bool pf_on = p.B <= p.nwg && int(blockIdx.x) < p.B;
+  int4 pf_head = make_int4(0, 0, 0, 0);
   for (int round = 0; round <= p.N + 2; ++round) {
     for (int r = blockIdx.x; r < p.B; r += p.nwg) {
       select_request(pk, r, round, st, s_misc, s_pf);
@@ -935,10 +953,37 @@ __global__ __launch_bounds__(kSpThreads, 2) void spark_kernel(SparkParams params
       const int g = it / S, seg = it - g * S;
       stats_item<L>(p, g, seg, S, s_rq[g], s_rn[g], p.temperature[s_rq[g]], s_v, s_i, s_d, m_v, m_i);
     }
-    // a workgroup with one request loads its state for the next round now,
-    // while the grid gathers at the barrier
-    if (p.B <= p.nwg && int(blockIdx.x) < p.B) load_request(p, blockIdx.x, st, s_pf);
-    if (!grid_sync(p, gen, &s_dead)) return;
+    // a workgroup with one request loads its state for the next round
+    // during the barrier, straight into LDS (16-byte buffer-to-LDS loads,
+    // 1 KB per wave instruction; the phase area is free by then) from waves
+    // 1-3: wave 0 arrives on the barrier, and its release fence would wait
+    // for its own loads
+    const bool live = grid_sync(p, gen, &s_dead, [&] {
+      if (pf_on && threadIdx.x >= kWave) {
+        const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave) - 1;
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(p.state + blockIdx.x, 0, int(sizeof(ReqState)), 0x00020000);
+        const int lane = threadIdx.x & (kWave - 1);
+        for (int c = w; c < kStateBlocks; c += kSpWaves - 1)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(s_phase + c * 1024),
+                                                   16, c * 1024 + lane * 16, 0, 0, 0);
+        if (threadIdx.x == kWave)
+          pf_head = make_int4(p.head[blockIdx.x].done, p.head[blockIdx.x].count,
+                              __float_as_int(p.temperature[blockIdx.x]), __float_as_int(p.theta[blockIdx.x]));
+      }
+    });
+    if (!live) return;
+    if (pf_on) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // LDS reads are not ordered after these loads
+      if (threadIdx.x == kWave) {
+        s_pf[0] = pf_head.x;
+        s_pf[1] = pf_head.y;
+        s_pf[2] = 1;
+        s_pf[3] = pf_head.z;
+        s_pf[4] = pf_head.w;
+      }
+      __syncthreads();
+    }
   }
 }
 
