@@ -13,7 +13,7 @@
 // Weyl key increments), counter (y/4, row, stream, 0), key (seed lo, seed hi),
 // output word y%4: u = ((word >> 8) + 1/2) / 2^24, strictly inside (0, 1).
 //
-// One workgroup of 256 threads per row streams the row once (float4 loads,
+// One workgroup of 512 threads per row streams the row once (float4 loads,
 // two ahead of the one being scored; one Philox call per float4). Each thread
 // keeps its K best (score, id) in registers, sorted (K = the next power of
 // two >= k). Per float4 the four score bounds (-ln u >= 1 - u gives
@@ -31,7 +31,7 @@ namespace tv {
 
 namespace {
 
-constexpr int kSibThreads = 256;
+constexpr int kSibThreads = 512;  // 8 waves: about five waves per SIMD over the rows
 constexpr int kMaxChildren = 16;
 
 struct SibParams {
