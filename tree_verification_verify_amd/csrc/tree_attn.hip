@@ -77,13 +77,10 @@ __device__ inline size_t qo_offset(const AttnParams& p, int nbeg, int g, int row
 }
 
 // Ancestor-or-self bitsets of nodes first_node .. first_node+nn-1 in LDS
-// (nn rows of `words`), walking parent links staged in LDS (`par`, the
-// request's N parents). Caller synchronises before and after.
-__device__ inline void build_anc(const AttnParams& p, int nbeg, int N, int first_node, int nn,
-                                 int words, uint32_t* anc, int* par) {
-  for (int i = threadIdx.x; i < nn * words; i += blockDim.x) anc[i] = 0u;
-  for (int i = threadIdx.x; i < N; i += blockDim.x) par[i] = p.parent[nbeg + i];
-  __syncthreads();
+// (nn rows of `words`, zero-filled), walking the request's parent links
+// already staged in LDS (`par`). Caller synchronises before and after.
+__device__ inline void link_anc(const AttnParams& p, int first_node, int nn, int words,
+                                uint32_t* anc, const int* par) {
   for (int t = threadIdx.x; t < nn; t += blockDim.x) {
     uint32_t* row = anc + t * words;
     int j = first_node + t;
@@ -101,6 +98,16 @@ __device__ inline void build_anc(const AttnParams& p, int nbeg, int N, int first
       j = pj;
     }
   }
+}
+
+// As link_anc, staging the request's N parents and clearing the bitsets
+// first. Caller synchronises before and after.
+__device__ inline void build_anc(const AttnParams& p, int nbeg, int N, int first_node, int nn,
+                                 int words, uint32_t* anc, int* par) {
+  for (int i = threadIdx.x; i < nn * words; i += blockDim.x) anc[i] = 0u;
+  for (int i = threadIdx.x; i < N; i += blockDim.x) par[i] = p.parent[nbeg + i];
+  __syncthreads();
+  link_anc(p, first_node, nn, words, anc, par);
 }
 
 // Keep bf16 elements [0, n) of an 8-element chunk, zero the rest (no branches).
@@ -434,6 +441,11 @@ __device__ inline void load_lds16(const void* src, void* lds_base) {
   const uint32_t base = uint32_t(reinterpret_cast<uintptr_t>(lds_base));
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(base) : "memory");
 }
+// As load_lds16 with 4 bytes per lane (lane i writes lds_base + 4*i).
+__device__ inline void load_lds4(const void* src, void* lds_base) {
+  const uint32_t base = uint32_t(reinterpret_cast<uintptr_t>(lds_base));
+  asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(base) : "memory");
+}
 
 // Workgroup barrier without a memory fence (no wait for pending global
 // loads or stores); this wave's LDS operations complete first. The empty
@@ -481,8 +493,8 @@ __global__ __launch_bounds__(kThreadsS, 1) void attn_stream_kernel(AttnParams p,
   __shared__ int s_scan[kWavesS];
   extern __shared__ int dyn_lds[];
   int* off = dyn_lds;                                                 // [B + 1]
-  int* par = dyn_lds + p.B + 1;                                       // [max_nodes]
-  uint32_t* anc = reinterpret_cast<uint32_t*>(par + p.max_nodes);     // [nn][words]
+  int* par = dyn_lds + p.B + 1;                                       // [max_nodes, to 64]
+  uint32_t* anc = reinterpret_cast<uint32_t*>(par + ((p.max_nodes + 63) & ~63));  // [nn][words]
 
   auto slot = [&](auto j_c) __attribute__((always_inline)) -> uint16_t* {
     constexpr int J = decltype(j_c)::value % NS;
@@ -583,14 +595,28 @@ __global__ __launch_bounds__(kThreadsS, 1) void attn_stream_kernel(AttnParams p,
     bool active = rt >= 0;
     const int row = rt * 16 + l16;  // block-local row of this lane
 
-    bf16x8 qf[KK];
-    if (active && row < rows_here) {
-      const uint16_t* src = qb + qo_offset(p, nbeg, g, row0 + row, D) + lg * 8;
+    // Q and the parent links come through LDS by the same direct loads as
+    // the stages, issued ahead of them: the wait for them then leaves the
+    // prologue stages in flight (a load into registers would make the
+    // compiler wait for every earlier load, the stages included). A wave's
+    // Q rows (lane (l16, lg), load kk: 16 bytes at column 8lg + 32kk) go to
+    // its own 1 KB pieces of the last ring slot, which the first step
+    // refills only after its barrier; rows past the block read the block's
+    // last row and are zeroed in registers.
+    bf16x8 qf[KK];  // read from LDS once the loads have landed
+    uint16_t* qlds = slot(std::integral_constant<int, NS - 1>{}) + wave * (KK * 512);
+    if (active) {
+      const uint16_t* src = qb + qo_offset(p, nbeg, g, row0 + min(row, rows_here - 1), D) + lg * 8;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(src + kk * 32);
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) qf[kk] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      for (int kk = 0; kk < KK; ++kk) load_lds16(src + kk * 32, qlds + kk * 512);
+    }
+    const bool tree_keys = thi * kStage > P;  // the segment reaches tree keys: masks needed
+    if (tree_keys) {
+      // 64 parents per load (the region is rounded up to 64 entries; lanes
+      // past N repeat the last parent)
+      for (int c0 = wave * 64; c0 < N; c0 += kThreadsS)
+        load_lds4(p.parent + nbeg + min(c0 + lane, N - 1), par + c0);
+      for (int i = tid; i < nn_blk * words; i += kThreadsS) anc[i] = 0u;
     }
 
     // Every load of a wave lies in page wave/2 of its stage (K rows 8*wave..
@@ -803,14 +829,19 @@ __global__ __launch_bounds__(kThreadsS, 1) void attn_stream_kernel(AttnParams p,
     });
     int idn = load_id(tlo + NS - 1);  // page id of the next stage to issue
 
+    // This wave's Q and parent loads have landed (the stages stay pending).
+    wait_vm<(NS - 1) * NI>();
     // The ancestor bitsets are built while the first stages load.
-    if (thi * kStage > P) {
-      build_anc(p, nbeg, N, first_node, nn_blk, words, anc, par);
-      __syncthreads();
+    if (tree_keys) {
+      stage_barrier();  // every wave's parent loads landed, the bitsets cleared
+      link_anc(p, first_node, nn_blk, words, anc, par);
+      stage_barrier();
     }
-    // Q and the first stages have landed (the first step would wait for the
-    // first stage anyway; Q is then settled for the whole segment).
-    wait_vm<0>();
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qlds + kk * 512 + lane * 8);
+      qf[kk] = active && row < rows_here ? v : bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
 
     // Step i (stage i in slot J = (i - tlo) % NS): wait for this wave's
     // loads of stage i (NS-2 later stages stay pending), barrier (every
@@ -1175,7 +1206,7 @@ bool plan_attn(const tv_attn_desc& d, AttnPlan* out) {
     pl.grid = size_t(nwg);
     pl.slots = 2 * size_t(nwg);
     const int nn_max = kRowsPB / pl.group + 2;
-    pl.dyn_lds = size_t(d.batch + 1 + d.max_nodes) * sizeof(int) +
+    pl.dyn_lds = size_t(d.batch + 1 + ((d.max_nodes + 63) & ~63)) * sizeof(int) +  // parents by 64
                  size_t(nn_max) * pl.words * sizeof(uint32_t);
     // Stage ring depth: four 64-key slots when they fit next to the
     // dynamic arrays in the 160 KB of LDS, else two.
