@@ -254,8 +254,9 @@ tv_status tree_spec_sample_noalloc(const tv_sample_desc* desc,
  *   out_tokens: tokens of the path's non-root nodes, then next_token[stop]
  *   kv_keep:    logical KV positions prefix_len[r] + node of the path rows
  * and out_len [B] = path length (accepted drafts + 1). A node with two
- * flagged children sets out_len[r] = -1 and, if status_workspace is not
- * NULL, TV_DEV_PATH in its status word. */
+ * flagged children, or a path longer than max_depth + 1, sets
+ * out_len[r] = -1 (that request's three rows are then unspecified) and, if
+ * status_workspace is not NULL, TV_DEV_PATH in its status word. */
 tv_status tree_accept_path(int32_t batch, int32_t max_depth,
                            const int32_t* node_indptr, const int32_t* parent,
                            const int32_t* tokens, const int8_t* accept_flag,

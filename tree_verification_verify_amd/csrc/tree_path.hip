@@ -14,13 +14,23 @@ namespace tv {
 
 namespace {
 
+// Rows of a request staged in LDS for the walk (larger requests read them
+// from memory at every level).
+constexpr int kPathStage = 1024;
+
 // One wave per request: from the root, find the unique flagged child with a
-// ballot over the request's rows, descend, repeat.
+// ballot over the request's rows, descend, repeat. A request of at most
+// kPathStage rows has its parents and flags staged in LDS first (one load
+// per row instead of one per row and level) and its path kept there, so
+// the outputs are written by all lanes after the walk.
 __global__ __launch_bounds__(64) void accept_path_kernel(
     int32_t batch, int32_t width, const int32_t* node_indptr, const int32_t* parent,
     const int32_t* tokens, const int8_t* flag, const int32_t* next_token,
     const int32_t* prefix_len, int32_t* path_nodes, int32_t* out_tokens, int32_t* out_len,
     int32_t* kv_keep, uint32_t* status) {
+  __shared__ int s_par[kPathStage];
+  __shared__ int8_t s_flag[kPathStage];
+  __shared__ int s_path[kPathStage];
   const int r = blockIdx.x;
   const int lane = threadIdx.x;
   const int nbeg = node_indptr[r];
@@ -29,6 +39,13 @@ __global__ __launch_bounds__(64) void accept_path_kernel(
   int32_t* pn = path_nodes + size_t(r) * width;
   int32_t* ot = out_tokens + size_t(r) * width;
   int32_t* kk = kv_keep + size_t(r) * width;
+  const bool staged = N <= kPathStage;
+  if (staged) {
+    for (int i = lane; i < N; i += 64) {
+      s_par[i] = parent[nbeg + i];
+      s_flag[i] = flag[nbeg + i];
+    }
+  }
   for (int i = lane; i < width; i += 64) {
     pn[i] = -1;
     ot[i] = -1;
@@ -38,19 +55,25 @@ __global__ __launch_bounds__(64) void accept_path_kernel(
     if (lane == 0) out_len[r] = 0;
     return;
   }
+  __syncthreads();  // the staged rows are visible to every lane
   int v = 0;
   int len = 1;
   bool error = false;
   if (lane == 0) {
-    pn[0] = 0;
-    kk[0] = P;
+    if (staged) {
+      s_path[0] = 0;
+    } else {
+      pn[0] = 0;
+      kk[0] = P;
+    }
   }
   while (true) {
     int found = -1;
     int nfound = 0;
     for (int base = v + 1; base < N; base += 64) {
       const int i = base + lane;
-      const bool hit = i < N && parent[nbeg + i] == v && flag[nbeg + i] == 1;
+      bool hit = false;
+      if (i < N) hit = staged ? (s_par[i] == v && s_flag[i] == 1) : (parent[nbeg + i] == v && flag[nbeg + i] == 1);
       const unsigned long long m = __ballot(hit);
       if (m) {
         if (found < 0) found = base + __ffsll(static_cast<long long>(m)) - 1;
@@ -67,19 +90,32 @@ __global__ __launch_bounds__(64) void accept_path_kernel(
       break;
     }
     if (lane == 0) {
-      pn[len] = found;
-      ot[len - 1] = tokens[nbeg + found];
-      kk[len] = P + found;
+      if (staged) {
+        s_path[len] = found;
+      } else {
+        pn[len] = found;
+        ot[len - 1] = tokens[nbeg + found];
+        kk[len] = P + found;
+      }
     }
     v = found;
     ++len;
+  }
+  if (staged && !error) {
+    __syncthreads();  // lane 0's path entries are visible
+    for (int i = lane; i < len; i += 64) {
+      const int node = s_path[i];
+      pn[i] = node;
+      kk[i] = P + node;
+      ot[i] = i + 1 < len ? tokens[nbeg + s_path[i + 1]] : next_token[nbeg + v];
+    }
   }
   if (lane == 0) {
     if (error) {
       out_len[r] = -1;
       raise_status(status, TV_DEV_PATH);
     } else {
-      ot[len - 1] = next_token[nbeg + v];
+      if (!staged) ot[len - 1] = next_token[nbeg + v];
       out_len[r] = len;
     }
   }
