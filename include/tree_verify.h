@@ -59,7 +59,7 @@ typedef enum {
   TV_ERR_PAGES = 6,      /* page table does not cover a request or id out of range */
   TV_ERR_HIP = 7,        /* a HIP runtime call failed (tv_last_hip_error) */
   TV_ERR_LOGITS = 8,     /* NaN or Inf logits, or draft logits missing at T > 0 */
-  TV_ERR_PATH = 9,       /* two accepted siblings */
+  TV_ERR_PATH = 9,       /* invalid accepted path (two accepted siblings, too deep) or keep-list */
   TV_ERR_TIMEOUT = 10    /* a team barrier exceeded its spin limit */
 } tv_status;
 

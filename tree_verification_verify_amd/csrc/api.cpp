@@ -39,7 +39,7 @@ const char* tv_status_string(tv_status s) {
     case TV_ERR_PAGES: return "page table does not cover the request or page id out of range";
     case TV_ERR_HIP: return "HIP runtime error";
     case TV_ERR_LOGITS: return "non-finite logits, bad temperature or missing draft logits";
-    case TV_ERR_PATH: return "two accepted siblings";
+    case TV_ERR_PATH: return "invalid accepted path (two accepted siblings, deeper than max_depth) or keep-list";
     case TV_ERR_TIMEOUT: return "team barrier exceeded its spin limit";
   }
   return "unknown status";
