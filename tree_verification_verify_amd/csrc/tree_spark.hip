@@ -122,7 +122,7 @@ struct SparkParams {
   uint32_t* bar;           // [0] arrivals, [1] generation
   ReqHead* head;           // [B]
   ReqState* state;         // [B]
-  int* rows;               // [2][B][kRows]
+  int4* rows;              // [2][B][kRows]: listed node, its token, its depth
   int* cnt;                // [2][B]
   float* ell;              // [B * kRows][V]
   Part* part;              // [B * kRows][kMaxSeg]
@@ -318,7 +318,7 @@ __device__ __attribute__((noinline)) void select_request(KParams* pin, int r, in
   const float th = pre ? __int_as_float(s_pf[4]) : p.theta[r];
   const double logth = th > 0.f ? log(double(th)) : -INFINITY;
   ReqHead* hd = p.head + r;
-  int* my_rows = p.rows + (size_t(cur) * p.B + r) * kRows;
+  int4* my_rows = p.rows + (size_t(cur) * p.B + r) * kRows;
   constexpr int kWords = int(sizeof(ReqState) / 16);
 
   if (round == 0) {
@@ -378,7 +378,7 @@ __device__ __attribute__((noinline)) void select_request(KParams* pin, int r, in
       const int S = spark_segments(nprev, p.nwg);
       const int mine = p.cnt[size_t(prev) * p.B + r];
       for (int j = wave; j < mine; j += kSpWaves) {
-        const int i = p.rows[(size_t(prev) * p.B + r) * kRows + j];
+        const int i = p.rows[(size_t(prev) * p.B + r) * kRows + j].x;
         const size_t g = size_t(pre + j);
         const Part* pp = p.part + g * kMaxSeg;
         // log-sum-exp of the segments
@@ -563,7 +563,7 @@ __device__ __attribute__((noinline)) void select_request(KParams* pin, int r, in
         const int pos = listed + int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32),
                                                                 __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
         if (want && pos < kRows) {
-          my_rows[pos] = i;
+          my_rows[pos] = make_int4(i, st.tok[i], st.dep[i], 0);  // what the logits phase needs
           st.state[i] = 1;
         }
         listed += __popcll(m);
@@ -915,6 +915,12 @@ __global__ __launch_bounds__(kSpThreads, 2) void spark_kernel(SparkParams params
       for (int q0 = 0; q0 < p.B; q0 += kWave) {
         const int q = q0 + int(threadIdx.x);
         const int c = q < p.B ? p.cnt[size_t(cur) * p.B + q] : 0;
+        // the request's row descriptors, loaded together with its count
+        // (every slot is in the workspace; slots past the count unused)
+        int4 dsc[kRows];
+        const int4* qd = p.rows + (size_t(cur) * p.B + (q < p.B ? q : 0)) * kRows;
+#pragma unroll
+        for (int j = 0; j < kRows; ++j) dsc[j] = qd[j];
         int inc = c;  // inclusive prefix over the wave
 #pragma unroll
         for (int o = 1; o < kWave; o <<= 1) {
@@ -922,12 +928,14 @@ __global__ __launch_bounds__(kSpThreads, 2) void spark_kernel(SparkParams params
           if (int(threadIdx.x) >= o) inc += t;
         }
         const int start = listed + inc - c;
-        for (int j = 0; j < c; ++j) {
-          const int i = p.rows[(size_t(cur) * p.B + q) * kRows + j];
-          s_rx[start + j] = p.state[q].tok[i];
-          s_ru[start + j] = ((long long)q * p.depths + p.state[q].dep[i]) * p.V;
-          s_rq[start + j] = q;
-          s_rn[start + j] = i;
+#pragma unroll
+        for (int j = 0; j < kRows; ++j) {
+          if (j < c) {
+            s_rx[start + j] = dsc[j].y;
+            s_ru[start + j] = ((long long)q * p.depths + dsc[j].z) * p.V;
+            s_rq[start + j] = q;
+            s_rn[start + j] = dsc[j].x;
+          }
         }
         listed += __shfl(inc, kWave - 1, kWave);
       }
@@ -1035,7 +1043,7 @@ size_t spark_workspace_bytes(const tv_spark_desc& d) {
   off += align256(size_t(kBarWords) * sizeof(uint32_t));  // grid barrier words
   off += align256(size_t(d.batch) * sizeof(ReqHead));
   off += align256(size_t(d.batch) * sizeof(ReqState));
-  off += align256(size_t(2) * d.batch * kRows * sizeof(int));
+  off += align256(size_t(2) * d.batch * kRows * sizeof(int4));
   off += align256(size_t(2) * d.batch * sizeof(int));
   off += align256(size_t(d.batch) * kRows * kMaxSeg * sizeof(Part));
   off += align256(size_t(d.batch) * kRows * size_t(d.vocab) * sizeof(float));
@@ -1054,8 +1062,8 @@ hipError_t launch_spark(const tv_spark_desc& d, const SparkArgs& a, hipStream_t 
   off += align256(size_t(d.batch) * sizeof(ReqHead));
   p.state = reinterpret_cast<ReqState*>(ws + off);
   off += align256(size_t(d.batch) * sizeof(ReqState));
-  p.rows = reinterpret_cast<int*>(ws + off);
-  off += align256(size_t(2) * d.batch * kRows * sizeof(int));
+  p.rows = reinterpret_cast<int4*>(ws + off);
+  off += align256(size_t(2) * d.batch * kRows * sizeof(int4));
   p.cnt = reinterpret_cast<int*>(ws + off);
   off += align256(size_t(2) * d.batch * sizeof(int));
   p.part = reinterpret_cast<Part*>(ws + off);
