@@ -23,7 +23,7 @@ from .tree import (check_tree, depths, ancestors_or_self, children,
 from .attention import tree_attention, tree_attention_rows, decode_values
 from .sampler import (softmax_T, proposal_without, proposal_with, residual_update,
                       acceptance_ratio, inverse_cdf, greedy_request,
-                      walk_request, tree_spec_sample)
+                      greedy_walk_request, walk_request, tree_spec_sample)
 from .path import accept_path_request, tree_accept_path
 from .commit import BadKeepList, check_keep, kv_commit_layer, kv_commit
 from .siblings import philox4x32_10, draw_children, tree_draw_siblings
@@ -35,7 +35,7 @@ __all__ = [
     "check_tree", "depths", "ancestors_or_self", "children", "ancestor_bitsets",
     "first_child_next_sibling", "tree_attention", "tree_attention_rows",
     "decode_values", "softmax_T", "proposal_without", "proposal_with", "residual_update",
-    "acceptance_ratio", "inverse_cdf", "greedy_request", "walk_request",
+    "acceptance_ratio", "inverse_cdf", "greedy_request", "greedy_walk_request", "walk_request",
     "tree_spec_sample", "accept_path_request", "tree_accept_path",
     "BadKeepList", "check_keep", "kv_commit_layer", "kv_commit",
     "philox4x32_10", "draw_children", "tree_draw_siblings",

@@ -115,6 +115,34 @@ def greedy_request(t_rows, tokens, parent):
     return flag, nt, []
 
 
+def greedy_walk_request(t_rows, tokens, parent):
+    """T == 0 along the walk only ([survey, Taxonomy] rule (a); [TreeSpark
+    §3.2 step 3]: greedy decoding matches target tokens exactly; the rows the
+    walk never reaches are not needed for the accepted path). From the root:
+    next_token[v] = argmax t_v (lowest index on ties) at every visited node;
+    every child c of v is tested, flag[c] = (token[c] == next_token[v]); the
+    walk moves to the first flagged child in draw order and stops at a node
+    with none. flag[root] = 1; untested nodes keep flag 0 and next_token -1.
+    The accepted path (and the error of two flagged siblings) is the one the
+    every-node form gives."""
+    check_tree(parent)
+    n = len(parent)
+    ch = children(parent)
+    flag = np.zeros(n, dtype=np.int8)
+    flag[0] = 1
+    nt = np.full(n, -1, dtype=np.int32)
+    v = 0
+    while True:
+        y = int(np.argmax(t_rows[v]))
+        nt[v] = y
+        hits = [c for c in ch[v] if int(tokens[c]) == y]
+        for c in ch[v]:
+            flag[c] = 1 if c in hits else 0
+        if not hits:
+            return flag, nt, []
+        v = hits[0]
+
+
 def walk_request(t_rows, d_rows, tokens, parent, T, uniforms, replacement=False):
     """T > 0: the recursive rejection walk, without replacement (rule (c)) or,
     with replacement=True, with replacement (rule (b)).
@@ -161,10 +189,12 @@ def walk_request(t_rows, d_rows, tokens, parent, T, uniforms, replacement=False)
         return flag, nt, log
 
 
-def tree_spec_sample(inp, replacement=False):
+def tree_spec_sample(inp, replacement=False, greedy_path=False):
     """Whole batch. Returns accept_flag [T] int8, next_token [T] int32 and a
     per-request list of decision logs. replacement selects rule (b) for the
-    T > 0 requests (rule (c) otherwise)."""
+    T > 0 requests (rule (c) otherwise); greedy_path selects the T == 0 form
+    that visits only the walk's nodes (greedy_walk_request) instead of every
+    node (greedy_request)."""
     T_total = int(inp.node_indptr[-1])
     flags = np.zeros(T_total, dtype=np.int8)
     nts = np.full(T_total, -1, dtype=np.int32)
@@ -173,7 +203,9 @@ def tree_spec_sample(inp, replacement=False):
         a, b = int(inp.node_indptr[r]), int(inp.node_indptr[r + 1])
         par = inp.parent[a:b]
         temp = float(inp.temperature[r])
-        if temp == 0.0:
+        if temp == 0.0 and greedy_path:
+            f, nt, log = greedy_walk_request(inp.target_logits[a:b], inp.tokens[a:b], par)
+        elif temp == 0.0:
             f, nt, log = greedy_request(inp.target_logits[a:b], inp.tokens[a:b], par)
         else:
             f, nt, log = walk_request(inp.target_logits[a:b], inp.draft_logits[a:b],

@@ -6,6 +6,7 @@ import pytest
 import scipy.special
 
 import oracle
+from oracle.path import TwoAcceptedSiblings
 from oracle.sampler import near_threshold
 from workloads import random_tree, chain_tree, star_tree, gumbel_topk_tokens
 
@@ -282,6 +283,89 @@ def test_greedy_closed_form_path():
     # root argmax 9 -> node 2; node 2's argmax 1 -> node 5; node 5's argmax 7 -> none
     path, out, keep = oracle.accept_path_request(parent, tokens, flag, nt, 100)
     assert path == [0, 2, 5] and out == [9, 1, 7] and keep == [100, 102, 105]
+
+
+def test_greedy_walk_hand_case():
+    """The T = 0 form that visits only the walk's nodes, on the tree of the
+    case above: nodes 0, 2 and 5 are visited, so only their children (1, 2;
+    5; none) are tested and only the visited rows carry a next token. The
+    every-node form also flags 4 and 6, whose parents the walk never
+    reaches; the accepted path is the same."""
+    parent = np.array([-1, 0, 0, 1, 1, 2, 3, 3])
+    tokens = np.array([0, 4, 9, 2, 6, 1, 3, 8], dtype=np.int32)
+    t = np.zeros((8, 10), dtype=np.float32)
+    for i, a in {0: 9, 2: 1, 5: 7, 1: 6, 3: 3, 4: 0, 6: 5, 7: 2}.items():
+        t[i, a] = 5.0
+    flag, nt, _ = oracle.greedy_walk_request(t, tokens, parent)
+    np.testing.assert_array_equal(flag, [1, 0, 1, 0, 0, 1, 0, 0])
+    np.testing.assert_array_equal(nt, [9, -1, 1, -1, -1, 7, -1, -1])
+    ef, ent, _ = oracle.greedy_request(t, tokens, parent)
+    np.testing.assert_array_equal(ef, [1, 0, 1, 0, 1, 1, 1, 0])
+    assert oracle.accept_path_request(parent, tokens, flag, nt, 0) == \
+        oracle.accept_path_request(parent, tokens, ef, ent, 0)
+
+
+@pytest.mark.parametrize("planted", ["last_child_skipped", "rows_shifted"])
+def test_greedy_walk_hand_case_catches_planted_mistakes(monkeypatch, planted):
+    """A child scan that stops one short, or the rows read one node off (the
+    child's row instead of the visited node's), fails the hand case."""
+    import oracle.sampler as smp
+    if planted == "last_child_skipped":
+        real = smp.children
+        monkeypatch.setattr(smp, "children", lambda par: [c[:-1] for c in real(par)])
+    else:
+        real = smp.greedy_walk_request
+        monkeypatch.setattr(oracle, "greedy_walk_request",
+                            lambda t, tok, par: real(np.roll(t, -1, axis=0), tok, par))
+    with pytest.raises(AssertionError):
+        test_greedy_walk_hand_case()
+
+
+def _random_greedy_case(rng, n, V):
+    parent = np.array([-1] + [int(rng.integers(0, i)) for i in range(1, n)])
+    t = rng.integers(-3, 4, size=(n, V)).astype(np.float32)  # integer logits: ties
+    tokens = rng.integers(0, V, size=n).astype(np.int32)
+    # plant matches so that walks go deep: a child often carries its parent's argmax
+    for i in range(1, n):
+        if rng.random() < 0.6:
+            tokens[i] = int(np.argmax(t[parent[i]]))
+    return parent, tokens, t
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_greedy_walk_agrees_with_every_node_form(seed):
+    """Over random trees (integer logits with ties, planted matches, repeated
+    sibling tokens allowed): the walk-only form gives the every-node form's
+    accepted path, or the same two-flagged-siblings error; it flags exactly
+    the children of the visited nodes, each as the every-node form does, and
+    gives the every-node next token at the visited nodes only."""
+    rng = np.random.default_rng(100 + seed)
+    deep = 0
+    for _ in range(60):
+        n, V = int(rng.integers(1, 40)), int(rng.integers(2, 9))
+        parent, tokens, t = _random_greedy_case(rng, n, V)
+        wf, wnt, _ = oracle.greedy_walk_request(t, tokens, parent)
+        ef, ent, _ = oracle.greedy_request(t, tokens, parent)
+        try:
+            want = oracle.accept_path_request(parent, tokens, ef, ent, 0)
+        except TwoAcceptedSiblings:
+            with pytest.raises(TwoAcceptedSiblings):
+                oracle.accept_path_request(parent, tokens, wf, wnt, 0)
+            continue
+        got = oracle.accept_path_request(parent, tokens, wf, wnt, 0)
+        assert got == want
+        path = got[0]
+        deep = max(deep, len(path))
+        visited = set(path)
+        for i in range(n):
+            if i == 0:
+                assert wf[i] == 1
+            elif parent[i] in visited:
+                assert wf[i] == ef[i]
+            else:
+                assert wf[i] == 0
+            assert wnt[i] == (ent[i] if i in visited else -1)
+    assert deep >= 4  # the planted matches made some walks deep
 
 
 def test_alignment_probe():
