@@ -73,6 +73,13 @@ typedef enum { TV_FP32 = 0, TV_BF16 = 1 } tv_dtype;
  * only for siblings drawn its own way. */
 typedef enum { TV_RULE_WITHOUT_REPLACEMENT = 0, TV_RULE_WITH_REPLACEMENT = 1 } tv_rule;
 
+/* What tree_spec_sample computes for greedy (T == 0) requests ([survey]
+ * Taxonomy rule (a); [TreeSpark] §3.2 step 3: exact target-token matching).
+ * Every node: the argmax of every target row and the match flag of every
+ * node. Path: only the rows the walk visits are read; the accepted path,
+ * emitted tokens and keep-list that tree_accept_path derives are the same. */
+typedef enum { TV_GREEDY_EVERY_NODE = 0, TV_GREEDY_PATH = 1 } tv_greedy;
+
 /* Bits of the device status word (first 4 bytes of a workspace). */
 enum {
   TV_DEV_TREE = 1u << 0,
@@ -107,6 +114,7 @@ typedef struct {
   int32_t max_nodes;     /* >= max_r N_r, <= 65536 */
   int32_t max_depth;     /* >= deepest node */
   int32_t rule;          /* tv_rule; 0 (a zero-filled desc) is without replacement */
+  int32_t greedy;        /* tv_greedy; 0 (a zero-filled desc) is every node */
 } tv_sample_desc;
 
 /* ---- workspace -------------------------------------------------------- */
@@ -170,12 +178,20 @@ tv_status tree_verify_attn(const tv_attn_desc* desc,
 /* Multi-step speculative sampling over the tree ([survey] Timeline and
  * Taxonomy rules (a), (c) and (b); [TreeSpark] §1 and §3.3, Proposition 1).
  *
- * Returns TV_ERR_SHAPE when desc->rule is not a tv_rule value.
+ * Returns TV_ERR_SHAPE when desc->rule is not a tv_rule value or
+ * desc->greedy not a tv_greedy value.
  * Row i of the logits is the distribution of the token AFTER node i
  * ([TreeSpark] §3.1, LM-shifted alignment). Per request r with T = temperature[r]:
- *   T == 0 (greedy exact match): next_token[i] = argmax target row i (lowest
- *     index on ties) for EVERY node; accept_flag[i] = (tokens[i] ==
- *     next_token[parent[i]]); accept_flag[root] = 1.
+ *   T == 0 (greedy exact match), desc->greedy == TV_GREEDY_EVERY_NODE:
+ *     next_token[i] = argmax target row i (lowest index on ties) for EVERY
+ *     node; accept_flag[i] = (tokens[i] == next_token[parent[i]]);
+ *     accept_flag[root] = 1.
+ *   T == 0, desc->greedy == TV_GREEDY_PATH: the same along the walk only.
+ *     From the root v: next_token[v] = argmax target row v; every child c of
+ *     v gets accept_flag[c] = (tokens[c] == next_token[v]); the walk moves
+ *     to the first flagged child (draw order) and stops at a node with
+ *     none. Nodes the walk never tests keep accept_flag 0 and next_token -1
+ *     (non-finite logits are detected in the visited rows only).
  *   T > 0 (rejection walk): starting at the root v, with
  *     p = softmax(target_v / T), q = softmax(draft_v / T), the children
  *     c_1 < c_2 < ... of v (draw order) are tested in turn: c_j is accepted

@@ -42,6 +42,11 @@ int main() {
   sbad.rule = tv_rule(7);
   EXPECT(tv_sample_workspace_size(&sbad) == 0);
   sbad = sd;
+  sbad.greedy = 2;
+  EXPECT(tv_sample_workspace_size(&sbad) == 0);
+  sbad.greedy = TV_GREEDY_PATH;
+  EXPECT(tv_sample_workspace_size(&sbad) == tv_sample_workspace_size(&sd));
+  sbad = sd;
   sbad.vocab = 0;
   EXPECT(tv_sample_workspace_size(&sbad) == 0);
   EXPECT(tv_expand_workspace_size(0, 4, 4) == 0);

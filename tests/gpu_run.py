@@ -23,15 +23,17 @@ def run_attention(inp, repeat=1, sm_scale=0.0):
     return (res if repeat > 1 else res[0]), st, bits
 
 
-def run_sampler(inp, max_depth=None, prefix_lens=None, ws=None, replacement=False):
+def run_sampler(inp, max_depth=None, prefix_lens=None, ws=None, replacement=False, greedy_path=False):
     """ws: a workspace to reuse (sized for at least this batch); a fresh
-    zero-filled one when None. replacement: the with-replacement rule."""
+    zero-filled one when None. replacement: the with-replacement rule;
+    greedy_path: greedy requests read only the rows their walk visits."""
     import torch
     import tree_verification_verify_amd as tv
     from workloads.device import sampler_tensors
     t = sampler_tensors(inp)
     md = max_depth if max_depth is not None else inp.max_nodes
-    desc = tv.sample_desc(inp.batch, inp.vocab, inp.max_nodes, md, replacement=replacement)
+    desc = tv.sample_desc(inp.batch, inp.vocab, inp.max_nodes, md, replacement=replacement,
+                          greedy_path=greedy_path)
     if ws is None:
         ws = tv.alloc_workspace(tv.sample_workspace_size(desc))
     else:

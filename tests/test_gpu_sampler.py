@@ -64,11 +64,12 @@ def compare_walk(inp, got, flags, nts, logs, pn, ot, ol, kk):
     return skipped, draw_only
 
 
-def _compare(inp, got, prefix_lens=None, allow_near=0, replacement=False, draw_near=None):
+def _compare(inp, got, prefix_lens=None, allow_near=0, replacement=False, draw_near=None,
+             greedy_path=False):
     """allow_near: requests with a near acceptance test (skipped); draw_near:
     the expected number whose only near decision is the draw (None: any)."""
     assert got["status"] == 0, (got["status"], got["bits"])
-    flags, nts, logs = oracle.tree_spec_sample(inp, replacement=replacement)
+    flags, nts, logs = oracle.tree_spec_sample(inp, replacement=replacement, greedy_path=greedy_path)
     md = got["max_depth"]
     B = inp.batch
     prefix_lens = prefix_lens if prefix_lens is not None else [0] * B
@@ -94,6 +95,52 @@ def test_highload_full_vocab(temp, draw_near):
     cfg = make_config("highload", attention=False, temperature=temp)
     _compare(cfg.sampler, _run(cfg.sampler, max_depth=8, prefix_lens=cfg.prefix_lens),
              cfg.prefix_lens, draw_near=draw_near)
+
+
+# Greedy requests along the walk only (TV_GREEDY_PATH): every output the
+# walk writes is compared, and the untouched nodes' defaults too.
+@pytest.mark.parametrize("temp", [0.0, "mixed"])
+def test_highload_greedy_path(temp):
+    cfg = make_config("highload", attention=False, temperature=temp)
+    got = _run(cfg.sampler, max_depth=8, prefix_lens=cfg.prefix_lens, greedy_path=True)
+    _compare(cfg.sampler, got, cfg.prefix_lens, draw_near=None, greedy_path=True)
+    if temp == 0.0:
+        # the walk tests only the children of visited nodes: most rows untouched
+        assert (got["next_token"] == -1).sum() > cfg.sampler.node_indptr[-1] // 2
+
+
+@pytest.mark.parametrize("V", [7, 64, 1000, 4099])
+@pytest.mark.parametrize("batch", [1, 5, 40])
+def test_greedy_path_random_small(V, batch):
+    """Random trees, mostly greedy requests, children drawn from correlated
+    draft rows so that walks go deep; V = 7 and 4099 take the unvectorised
+    loads."""
+    rng = np.random.default_rng(1000 + V + batch)
+    trees = [random_tree(rng, int(rng.integers(1, min(25, V + 1) + 1)),
+                         depth_cap=int(rng.integers(1, 6)))
+             for _ in range(batch)]
+    temps = rng.choice([0.0, 0.0, 0.0, 0.5, 1.0], size=batch)
+    inp = make_sampler_inputs(rng, rng, rng, trees, V, temps, mode="correlated")
+    _compare(inp, _run(inp, max_depth=6, greedy_path=True), greedy_path=True)
+
+
+def test_greedy_path_ties_and_a_bad_parent():
+    """Ties take the lowest index along the walk, as in the every-node form;
+    a parent link that breaks the order is reported (status TV_DEV_TREE)."""
+    V = 50
+    trees = [star_tree(6), chain_tree(4)]
+    rng = np.random.default_rng(0)
+    inp = make_sampler_inputs(rng, rng, rng, trees, V, [0.0, 0.0])
+    inp.target_logits[:] = 0.0
+    inp.target_logits[:, 7] = 3.0
+    inp.target_logits[:, 31] = 3.0   # tie with 7: argmax must be 7
+    inp.tokens[:] = [0, 9, 31, 7, 2, 5, 0, 7, 7, 1]
+    got = _run(inp, max_depth=6, greedy_path=True)
+    _compare(inp, got, greedy_path=True)
+    assert list(got["out_len"]) == [2, 3]
+    inp.parent[8] = 2   # node 2 of the chain names itself
+    got = _run(inp, max_depth=6, greedy_path=True)
+    assert got["bits"] & 1, got["bits"]   # TV_DEV_TREE
 
 
 def test_highload_independent_logits():

@@ -105,6 +105,14 @@ def test_sampler_host_errors():
     rep = tv.sample_desc(4, 151936, 32, 8, replacement=True)
     assert rep.rule == tv.TV_RULE_WITH_REPLACEMENT
     assert lib.tv_sample_workspace_size(ctypes.byref(rep)) == need
+    for greedy in (-1, 2):
+        bad = tv.sample_desc(4, 151936, 32, 8)
+        bad.greedy = greedy
+        assert lib.tv_sample_workspace_size(ctypes.byref(bad)) == 0
+        assert call(bad, ok_ptrs) == SHAPE
+    gp = tv.sample_desc(4, 151936, 32, 8, greedy_path=True)
+    assert gp.greedy == tv.TV_GREEDY_PATH
+    assert lib.tv_sample_workspace_size(ctypes.byref(gp)) == need
 
 
 def test_path_and_meta_host_errors():

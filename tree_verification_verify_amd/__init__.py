@@ -18,11 +18,12 @@ import numpy as np
 
 from . import _lib
 from ._lib import (AttnDesc, SampleDesc, TV_BF16, TV_FP32, STATUS_NAMES, DEV_BITS,
-                   TV_RULE_WITHOUT_REPLACEMENT, TV_RULE_WITH_REPLACEMENT)
+                   TV_RULE_WITHOUT_REPLACEMENT, TV_RULE_WITH_REPLACEMENT,
+                   TV_GREEDY_EVERY_NODE, TV_GREEDY_PATH)
 
 __all__ = [
     "TVError", "AttnDesc", "SampleDesc", "TV_BF16", "TV_FP32", "TV_RULE_WITHOUT_REPLACEMENT",
-    "TV_RULE_WITH_REPLACEMENT", "attn_desc",
+    "TV_RULE_WITH_REPLACEMENT", "TV_GREEDY_EVERY_NODE", "TV_GREEDY_PATH", "attn_desc",
     "sample_desc", "attn_workspace_size", "sample_workspace_size", "alloc_workspace",
     "workspace_init", "device_status", "tree_verify_attn", "tree_spec_sample",
     "tree_accept_path", "tree_kv_commit", "tree_draw_siblings", "tree_expand_step", "tree_rerank", "expand_workspace_size", "tv_tree_meta", "validate_tree", "validate_pages",
@@ -81,11 +82,13 @@ def attn_desc(batch, num_q_heads, num_kv_heads, head_dim, max_nodes, max_depth,
                     float(sm_scale))
 
 
-def sample_desc(batch, vocab, max_nodes, max_depth, replacement=False):
+def sample_desc(batch, vocab, max_nodes, max_depth, replacement=False, greedy_path=False):
     """replacement selects the with-replacement walk (independent sibling
-    draws) instead of the without-replacement one."""
+    draws) instead of the without-replacement one; greedy_path makes greedy
+    (T == 0) requests read only the rows their walk visits."""
     return SampleDesc(batch, vocab, max_nodes, max_depth,
-                      TV_RULE_WITH_REPLACEMENT if replacement else TV_RULE_WITHOUT_REPLACEMENT)
+                      TV_RULE_WITH_REPLACEMENT if replacement else TV_RULE_WITHOUT_REPLACEMENT,
+                      TV_GREEDY_PATH if greedy_path else TV_GREEDY_EVERY_NODE)
 
 
 def attn_workspace_size(desc):

@@ -28,7 +28,7 @@ class AttnDesc(ctypes.Structure):
 class SampleDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("vocab", ctypes.c_int32),
                 ("max_nodes", ctypes.c_int32), ("max_depth", ctypes.c_int32),
-                ("rule", ctypes.c_int32)]
+                ("rule", ctypes.c_int32), ("greedy", ctypes.c_int32)]
 
 
 class SparkDesc(ctypes.Structure):
@@ -40,6 +40,8 @@ class SparkDesc(ctypes.Structure):
 
 TV_RULE_WITHOUT_REPLACEMENT = 0
 TV_RULE_WITH_REPLACEMENT = 1
+TV_GREEDY_EVERY_NODE = 0
+TV_GREEDY_PATH = 1
 TV_SAMPLE_STATIC_MAX_BATCH = 1024
 
 

@@ -92,6 +92,7 @@ struct SampleParams {
   char* req;  // per-request blocks of kReqBytes
   int B, V, W, max_nodes;
   int with_replacement;  // rule (b): the stage proposal stays q
+  int greedy_path;       // T = 0: only the rows the walk visits
   uint64_t wait_ticks;   // team wait limit (real-time counter ticks)
 };
 
@@ -1353,6 +1354,110 @@ __device__ __attribute__((always_inline)) inline void greedy_rows(const SamplePa
   }
 }
 
+// ---------------------------------------------------------------------------
+// Greedy exact match along the walk only (T = 0, TV_GREEDY_PATH). From the
+// root, the team takes the argmax of the visited node's target row (each
+// member over its slice [lo, hi), lowest index on ties, then one exchange of
+// (value, index) per member), tests every child against it, moves to the
+// first matching child in draw order and stops at a node with none. Member
+// 0 writes every output: first the request's defaults (root flagged, the
+// rest 0, next tokens -1), then each visit's next token and the flags of the
+// children it tested; its default stores precede its first visit's loads,
+// so they have completed before any of its later stores is issued.
+constexpr int kPathLoads = 12;  // 16-byte loads per thread in flight per step
+
+__device__ __attribute__((always_inline)) inline void greedy_path(const SampleParams& p, Team& tm, int nbeg,
+                                                                  int N, const Parents& par, int lo, int hi,
+                                                                  bool vec4, float* shv, int* shi,
+                                                                  uint32_t* s_words, int* s_c) {
+  const int V = p.V;
+  const bool writer = tm.member == 0;
+  if (writer)
+    for (int i = threadIdx.x; i < N; i += kThreads) {
+      p.flag[nbeg + i] = i == 0 ? 1 : 0;
+      p.next_token[nbeg + i] = -1;
+    }
+  float chk = 0.f;  // t * 0 is 0 for finite t, NaN otherwise
+  int v = 0;
+  while (true) {
+    const float* row = p.t + size_t(nbeg + v) * V;
+    // Four running argmaxes per thread (one per float4 lane), each seeing
+    // ascending offsets, so ties keep the first; bi[e] + e is the token.
+    float bv[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    int bi[4] = {0x7fffffff, 0x7fffffff, 0x7fffffff, 0x7fffffff};
+    if (vec4) {
+      const int n4 = (hi - lo) >> 2;  // float4 of this member's slice (V % 4 == 0)
+      const float* base = row + lo;
+      for (int b0 = 0; b0 < n4; b0 += kPathLoads * kThreads) {
+        float4 buf[kPathLoads];
+#pragma unroll
+        for (int u = 0; u < kPathLoads; ++u)  // past the slice: 0, no memory access
+          buf[u] = load4_bounded(base, 16 * n4, 16 * (b0 + u * kThreads + int(threadIdx.x)));
+#pragma unroll
+        for (int u = 0; u < kPathLoads; ++u) {
+          const int i4 = b0 + u * kThreads + int(threadIdx.x);
+          const bool ok = i4 < n4;
+          const int y0 = lo + 4 * i4;
+          const float a[4] = {buf[u].x, buf[u].y, buf[u].z, buf[u].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            chk = fmaf(a[e], 0.f, chk);
+            const bool take = ok && a[e] > bv[e];
+            bv[e] = take ? a[e] : bv[e];
+            bi[e] = take ? y0 : bi[e];
+          }
+        }
+      }
+    } else {
+      sweep<false>(row, row, lo, hi, false, [&](float t, float, int y, bool ok) {
+        chk = ok ? fmaf(t, 0.f, chk) : chk;
+        const bool take = ok && t > bv[0];  // ascending y per thread: ties keep the first
+        bv[0] = take ? t : bv[0];
+        bi[0] = take ? y : bi[0];
+      });
+    }
+    float mv = bv[0];
+    int mi = bi[0];
+    if (vec4) {
+#pragma unroll
+      for (int e = 1; e < 4; ++e) am_combine(mv, mi, bv[e], bi[e] == 0x7fffffff ? bi[e] : bi[e] + e);
+    }
+    block_argmax(mv, mi, shv, shi);
+    if (threadIdx.x < 2) ll_put(tm, int(threadIdx.x), threadIdx.x == 0 ? __float_as_uint(mv) : uint32_t(mi), s_words);
+    if (!ll_gather(tm, 2, s_words)) return;
+    float gv = -INFINITY;
+    int gi = 0x7fffffff;
+    for (int m = 0; m < tm.W; ++m) am_combine(gv, gi, __uint_as_float(s_words[2 * m]), int(s_words[2 * m + 1]));
+    const int y = __builtin_amdgcn_readfirstlane(gi == 0x7fffffff ? 0 : gi);
+    // Every child of v is tested (member 0 writes the flags); the first
+    // match in draw order is the next node. The first visit scans every
+    // row, so member 0 checks every parent link then.
+    if (threadIdx.x < kWave) {
+      int found = -1;
+      for (int b = v + 1; b < N; b += kWave) {
+        const int i = b + int(threadIdx.x);
+        const int pi = i < N ? par[i] : v - 1;
+        if (writer && v == 0 && i < N && (pi < 0 || pi >= i)) raise_status(p.status, TV_DEV_TREE);
+        const bool child = i < N && pi == v;
+        const bool match = child && par.tok(i) == y;
+        if (writer && child) p.flag[nbeg + i] = match ? 1 : 0;
+        const unsigned long long m = __ballot(match);
+        if (m && found < 0) found = b + __ffsll(static_cast<long long>(m)) - 1;
+      }
+      if (threadIdx.x == 0) {
+        *s_c = found;
+        if (writer) p.next_token[nbeg + v] = y;
+      }
+    }
+    __syncthreads();
+    const int c = __builtin_amdgcn_readfirstlane(*s_c);
+    __syncthreads();  // s_c is rewritten at the next visit
+    if (c < 0) break;
+    v = c;
+  }
+  if (!(chk == 0.f)) raise_status(p.status, TV_DEV_LOGITS);
+}
+
 __global__ __launch_bounds__(kThreads, 4) void sample_kernel(SampleParams p) {
   __shared__ double tbl[64];
   __shared__ double tblz[kZTable];
@@ -1424,6 +1529,29 @@ __global__ __launch_bounds__(kThreads, 4) void sample_kernel(SampleParams p) {
   tm.wait_ticks = p.wait_ticks;
   tm.s_dead = &s_dead;
 
+  // Member slices: vectorised rows are split in chunks of 1024 logits
+  // (kThreads float4), member m taking chunks [m C / W, (m + 1) C / W) of the
+  // C in a row, so only the row's last chunk is ever partial.
+  int lo, hi, nch = 0;
+  const int C = (V + 4 * kThreads - 1) / (4 * kThreads);
+  if (vec4) {
+    const int c0 = member * C / p.W, c1 = (member + 1) * C / p.W;
+    nch = c1 - c0;
+    lo = min(V, 4 * kThreads * c0);
+    hi = min(V, 4 * kThreads * c1);
+  } else {
+    const int slice = (V + p.W - 1) / p.W;
+    lo = min(V, member * slice);
+    hi = min(V, lo + slice);
+  }
+
+  if (T == 0.f && p.greedy_path) {
+    greedy_path(p, tm, nbeg, N, par, lo, hi, vec4, shv, shi, s_words, &s_int);
+    // the request's sequence moves past every tag this call used (as below)
+    if (member == 0 && threadIdx.x == 0 && p.W > 1)
+      __hip_atomic_store(seq_word, tm.seq + uint32_t(tm.phase), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
   if (T == 0.f) {
     Barrier bar{reinterpret_cast<uint32_t*>(rq), 0u, p.W, p.status, p.wait_ticks, &s_dead};
     // Greedy exact match: argmax of every row, then the match flags.
@@ -1485,23 +1613,8 @@ __global__ __launch_bounds__(kThreads, 4) void sample_kernel(SampleParams p) {
     return;
   }
 
-  // Sampled walk (T > 0). Member slices in float4 units when V % 4 == 0.
+  // Sampled walk (T > 0).
   const double invT = 1.0 / double(T);
-  // Vectorised rows are split in chunks of 1024 logits (kThreads float4),
-  // member m taking chunks [m C / W, (m + 1) C / W) of the C in a row, so
-  // only the row's last chunk is ever partial.
-  int lo, hi, nch = 0;
-  const int C = (V + 4 * kThreads - 1) / (4 * kThreads);
-  if (vec4) {
-    const int c0 = member * C / p.W, c1 = (member + 1) * C / p.W;
-    nch = c1 - c0;
-    lo = min(V, 4 * kThreads * c0);
-    hi = min(V, 4 * kThreads * c1);
-  } else {
-    const int slice = (V + p.W - 1) / p.W;
-    lo = min(V, member * slice);
-    hi = min(V, lo + slice);
-  }
   WalkLds L{tbl, tblz, sh, shf, s_slice, s_words, s_kid, s_kt, s_kd, s_ku, &s_nk, &s_int, s_res, s_draw};
   const bool resident = vec4 && (C + p.W - 1) / p.W <= kResCh;  // the same for every member
   if (resident)
@@ -1521,6 +1634,7 @@ bool plan_sample(const tv_sample_desc& d, SamplePlan* out) {
   if (d.batch < 1 || d.vocab < 1 || d.max_nodes < 1 || d.max_nodes > 65536 || d.max_depth < 0)
     return false;
   if (d.rule != TV_RULE_WITHOUT_REPLACEMENT && d.rule != TV_RULE_WITH_REPLACEMENT) return false;
+  if (d.greedy != TV_GREEDY_EVERY_NODE && d.greedy != TV_GREEDY_PATH) return false;
   SamplePlan pl{};
   pl.threads = kThreads;
   pl.off_req = kHeaderBytes;
@@ -1617,6 +1731,7 @@ hipError_t launch_sample_core(const tv_sample_desc& d, const SampleArgs& a, uint
   p.W = W;
   p.max_nodes = d.max_nodes;
   p.with_replacement = d.rule == TV_RULE_WITH_REPLACEMENT;
+  p.greedy_path = d.greedy == TV_GREEDY_PATH;
   p.wait_ticks = wait_ticks();
   const dim3 grid(unsigned(grid_for(W))), block(kThreads);
   hipLaunchKernelGGL(sample_kernel, grid, block, 0, stream, p);
