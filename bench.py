@@ -2,7 +2,8 @@
 
 One step = one pass of the whole hot path over one batch:
   tree_verify_attn (one attention layer, every tree row of every request)
-  -> tree_spec_sample (greedy / rejection walk without or with replacement)
+  -> tree_spec_sample (greedy / rejection walk without or with replacement; greedy
+     requests read only the rows their walk visits unless --greedy every)
   -> tree_accept_path (longest accepted path, emitted tokens, KV keep-list).
 Workload (default): "highload" — 64 requests, prefixes U{512..8192}, per-request
 budget from {8-row chain, 16-row tree, 32-row tree}, 32 q / 8 kv heads, D 128,
@@ -54,15 +55,16 @@ def attn_algorithmic_flops(cfg):
     return f
 
 
-def sampler_algorithmic_bytes(sinp, out_len):
-    """Rows the walk must read: every target row at T = 0 (eager greedy
-    flags); the target and draft row of each visited node at T > 0."""
+def sampler_algorithmic_bytes(sinp, out_len, greedy_path=False):
+    """Rows the walk must read: at T = 0 every target row (the every-node
+    form) or the target row of each visited node (the walk-only form); the
+    target and draft row of each visited node at T > 0."""
     V = sinp.vocab
     total = 0
     for r in range(sinp.batch):
         n = int(sinp.node_indptr[r + 1] - sinp.node_indptr[r])
         if float(sinp.temperature[r]) == 0.0:
-            total += n * V * 4
+            total += (int(out_len[r]) if greedy_path else n) * V * 4
         else:
             total += int(out_len[r]) * V * 4 * 2
     return total
@@ -94,7 +96,7 @@ def _cpu_model():
     return "unknown"
 
 
-def cpu_baseline(cfg, budget_s=12.0, replacement=False, requests=32, repeats=3):
+def cpu_baseline(cfg, budget_s=12.0, replacement=False, requests=32, repeats=3, greedy_path=False):
     """The oracle as it stands (fp64 NumPy attention + sampling walk + path)
     on a fixed sample of the workload's requests (the first `requests`),
     timed with perf_counter, median of `repeats` runs, once with the BLAS
@@ -119,7 +121,7 @@ def cpu_baseline(cfg, budget_s=12.0, replacement=False, requests=32, repeats=3):
                                 tokens=s.tokens[a:b], node_indptr=np.array([0, b - a], np.int32),
                                 parent=s.parent[a:b], temperature=s.temperature[r:r + 1],
                                 uniforms=s.uniforms[a:b])
-            f, nt, _ = oracle.tree_spec_sample(one, replacement=replacement)
+            f, nt, _ = oracle.tree_spec_sample(one, replacement=replacement, greedy_path=greedy_path)
             oracle.tree_accept_path(one.node_indptr, one.parent, one.tokens, f, nt,
                                     [int(inp.prefix_len[r])], 16)
         return time.perf_counter() - t0
@@ -524,6 +526,9 @@ def main():
                     help="comma-separated workloads: time tree_verify_attn alone on each, "
                          "rotating >= --rotate-bytes of distinct copies (one JSON line each)")
     ap.add_argument("--rotate-bytes", type=int, default=1 << 30)
+    ap.add_argument("--greedy", choices=("every", "path"), default="path",
+                    help="greedy (T = 0) requests: argmax of the rows the walk visits (path, "
+                         "the default) or of every row (every)")
     ap.add_argument("--replacement", action="store_true",
                     help="siblings drawn independently (with replacement) and verified by "
                          "the with-replacement rule")
@@ -592,7 +597,8 @@ def main():
     if have_sampler:
         st = sampler_tensors(s, dev)
         md = max(8, inp.max_depth)
-        sdesc = tv.sample_desc(s.batch, s.vocab, s.max_nodes, md, replacement=args.replacement)
+        sdesc = tv.sample_desc(s.batch, s.vocab, s.max_nodes, md, replacement=args.replacement,
+                               greedy_path=args.greedy == "path")
         sws = tv.alloc_workspace(tv.sample_workspace_size(sdesc), dev)
         T = int(s.node_indptr[-1])
         flag = torch.empty(T, dtype=torch.int8, device=dev)
@@ -666,7 +672,8 @@ def main():
                                f"Hq {inp.num_q_heads}/Hkv {inp.num_kv_heads}/D {inp.head_dim} "
                                f"{inp.dtype} paged KV"
                                + (f"; sampler V {s.vocab}, T {args.temperature}" if have_sampler else "")
-                               + ("; siblings with replacement, rule (b)" if args.replacement else ""),
+                               + ("; siblings with replacement, rule (b)" if args.replacement else "")
+                               + ("; greedy along the walk only" if args.greedy == "path" else ""),
                    "batch": inp.batch, "tree_rows": nodes, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
@@ -681,12 +688,13 @@ def main():
     }
     if have_sampler:
         out_len = ol.cpu().numpy()
-        sbytes = sampler_algorithmic_bytes(s, out_len)
+        sbytes = sampler_algorithmic_bytes(s, out_len, greedy_path=args.greedy == "path")
         res["sampler"] = {"algorithmic_bytes": sbytes,
                           "achieved_GBs": sbytes / (samp_ms * 1e-3) / 1e9 if samp_ms > 0 else None,
                           "mean_emitted": float(out_len.mean()), "dtype": "f64"}
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget, args.replacement)
+        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget, args.replacement,
+                                           greedy_path=args.greedy == "path")
     print(json.dumps(res))
 
 
