@@ -1391,8 +1391,11 @@ __device__ __attribute__((always_inline)) inline void greedy_path(const SamplePa
       for (int b0 = 0; b0 < n4; b0 += kPathLoads * kThreads) {
         float4 buf[kPathLoads];
 #pragma unroll
-        for (int u = 0; u < kPathLoads; ++u)  // past the slice: 0, no memory access
-          buf[u] = load4_bounded(base, 16 * n4, 16 * (b0 + u * kThreads + int(threadIdx.x)));
+        for (int u = 0; u < kPathLoads; ++u) {  // past the slice: 0, no memory access
+          const int s0 = b0 + u * kThreads;      // the block's first float4
+          const int in = min(kThreads, max(0, n4 - s0));
+          buf[u] = load4_bounded(base + 4 * size_t(s0), 16 * in, 16 * int(threadIdx.x));
+        }
 #pragma unroll
         for (int u = 0; u < kPathLoads; ++u) {
           const int i4 = b0 + u * kThreads + int(threadIdx.x);
