@@ -59,16 +59,16 @@ def test_attention_relabelled_random_small(dtype, kind):
         assert err <= TOL[dtype], err
 
 
-def _sample(inp, md, prefix_lens):
+def _sample(inp, md, prefix_lens, greedy_path=False):
     from gpu_run import run_sampler
-    got = run_sampler(inp, max_depth=md, prefix_lens=prefix_lens)
+    got = run_sampler(inp, max_depth=md, prefix_lens=prefix_lens, greedy_path=greedy_path)
     assert got["status"] == 0, (got["status"], got["bits"])
     return got
 
 
-def _check_sampler(inp, got, prefix_lens):
+def _check_sampler(inp, got, prefix_lens, greedy_path=False):
     from test_gpu_sampler import compare_walk
-    flags, nts, logs = oracle.tree_spec_sample(inp)
+    flags, nts, logs = oracle.tree_spec_sample(inp, greedy_path=greedy_path)
     pn, ot, ol, kk = oracle.tree_accept_path(inp.node_indptr, inp.parent, inp.tokens, flags,
                                              nts, prefix_lens, got["max_depth"])
     skipped, _ = compare_walk(inp, got, flags, nts, logs, pn, ot, ol, kk)
@@ -99,6 +99,23 @@ def test_sampler_and_path_relabelled(kind, temp):
         n = base["out_len"][r]
         mapped = perm[a + base["path_nodes"][r, :n]] - a
         np.testing.assert_array_equal(got["path_nodes"][r, :n], mapped)
+
+
+@pytest.mark.parametrize("kind", ["dfs", "random"])
+def test_greedy_walk_relabelled(kind):
+    """Greedy requests verified along the walk only, on the renumbered
+    highload trees (T = 0): equal to the oracle on the relabelled inputs and
+    to the BFS run after mapping the rows."""
+    cfg = make_config("highload", attention=False, temperature=0.0)
+    maps = relabel_trees(cfg.trees, kind, np.random.default_rng(13))
+    rel = relabel_sampler(cfg.sampler, maps)
+    got = _sample(rel, 8, cfg.prefix_lens, greedy_path=True)
+    _check_sampler(rel, got, cfg.prefix_lens, greedy_path=True)
+    base = _sample(cfg.sampler, 8, cfg.prefix_lens, greedy_path=True)
+    perm = global_perm(cfg.sampler.node_indptr, maps)
+    np.testing.assert_array_equal(got["flag"][perm], base["flag"])
+    np.testing.assert_array_equal(got["next_token"][perm], base["next_token"])
+    np.testing.assert_array_equal(got["out_tokens"], base["out_tokens"])
 
 
 @pytest.mark.parametrize("kind", ["dfs", "random"])

@@ -443,16 +443,17 @@ def test_topk_siblings_are_biased_on_gpu(replacement):
     _compare(inp, got, replacement=replacement)
 
 
-@pytest.mark.parametrize("temp", [1.0, 0.0])
-def test_team_wait_gives_up_when_forced_from_the_host(temp, monkeypatch):
+@pytest.mark.parametrize("temp,greedy_path", [(1.0, False), (0.0, False), (0.0, True)])
+def test_team_wait_gives_up_when_forced_from_the_host(temp, greedy_path, monkeypatch):
     """A team wait limit of 0 (set from the host for these launches only)
-    makes the exchange (T > 0) and the greedy barrier (T = 0) give up at
-    once: the kernel still ends normally and reports TV_DEV_TIMEOUT
-    (status 10). Each run uses a fresh workspace."""
+    makes the exchange (T > 0, and the greedy walk's argmax exchange) and the
+    greedy barrier (T = 0, every node) give up at once: the kernel still ends
+    normally and reports TV_DEV_TIMEOUT (status 10). Each run uses a fresh
+    workspace."""
     cfg = make_config("highload", attention=False, batch=32, vocab=8192, temperature=temp)
     monkeypatch.setenv("TREEVERIFY_TEAM_WAIT_US", "0")
-    got = _run(cfg.sampler, max_depth=8)
+    got = _run(cfg.sampler, max_depth=8, greedy_path=greedy_path)
     monkeypatch.delenv("TREEVERIFY_TEAM_WAIT_US")
     assert got["bits"] & (1 << 4) and got["status"] == 10, (got["bits"], got["status"])
     # the default limit again: a fresh workspace verifies normally
-    _compare(cfg.sampler, _run(cfg.sampler, max_depth=8))
+    _compare(cfg.sampler, _run(cfg.sampler, max_depth=8, greedy_path=greedy_path), greedy_path=greedy_path)
