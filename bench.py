@@ -543,9 +543,9 @@ def main():
                          "layers (one JSON line)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU; --gpus must be 1 "
-                                   "(requests and kv heads shard across GPUs with no "
-                                   "exchange, see the design notes)"}))
+        print(json.dumps({"error": "bench.py measures one GPU; --gpus must be 1 "
+                                   "(requests and kv heads would shard across GPUs with no "
+                                   "exchange between them)"}))
         sys.exit(2)
 
     import torch

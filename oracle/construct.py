@@ -8,7 +8,7 @@ top-k nodes by path-product value and reranking to keep the top-m nodes;
 [survey, Taxonomy / construction policy] the signal is the cumulative draft
 probability along the root path.
 
-Readings of points the pages leave open (each also listed in the design notes):
+Readings of points the pages leave open:
   * a node's value is the sum of log q along its root path (the log of the
     path product), q = softmax of the node's draft row (temperature 1);
   * one expansion round gives every frontier node its k most probable

@@ -18,7 +18,7 @@ Sources:
                        greedy decoding uses exact target-token matching.
   [explainer, Red flags] exactly one path is accepted.
 
-Readings of points the pages leave open (each also listed in the design notes):
+Readings of points the pages leave open:
   * row i of the logits is the distribution of the token after node i
     ([TreeSpark §3.1] LM-shifted alignment);
   * children of v are tested in ascending row index (= draw order);

@@ -24,7 +24,7 @@ Sources (TreeSpark: Markov-conditioned draft trees, paper 2609.22098):
   §3.3  siblings are drawn without replacement from q_T and their draw order
         is what the verifier replays.
 
-Readings of points the pages leave open (each also listed in the design notes):
+Readings of points the pages leave open:
   * node counts exclude the root: the cap N bounds the drafted nodes;
   * U[d-1] is the base row of depth d (d = 1..b); a node at depth b has no
     child slot;
