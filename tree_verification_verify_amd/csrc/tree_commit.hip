@@ -60,17 +60,21 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(CommitParams 
   const int r = blockIdx.x / p.L;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  // The request's scalars and this thread's keep-list entry load together
+  // (every entry j < W of the row is in the array), one round trip.
+  const int32_t* keep = p.kv_keep + size_t(r) * p.W;
   const int n = p.out_len[r];
+  const int P = p.prefix_len[r];
+  const int pbase = p.page_indptr[r];
+  const int npg = p.page_indptr[r + 1] - pbase;
+  const int keep_t = tid < p.W ? keep[tid] : 0;
+  const int keep_prev = tid >= 1 && tid - 1 < p.W ? keep[tid - 1] : 0;
   if (n < 1) return;  // nothing accepted (or a path error reported upstream)
   const bool reporter = layer == 0 && tid == 0;
   if (n > p.W) {
     if (reporter) raise_status(p.status, TV_DEV_SHAPE);
     return;
   }
-  const int P = p.prefix_len[r];
-  const int pbase = p.page_indptr[r];
-  const int npg = p.page_indptr[r + 1] - pbase;
-  const int32_t* keep = p.kv_keep + size_t(r) * p.W;
 
   // Entry j is valid when the list starts at P, increases strictly, stays
   // in [P + j, P + max_nodes) and its source and destination lie in listed
@@ -78,8 +82,8 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(CommitParams 
   // anything moves, so every workgroup of the request takes the same
   // decision: lists longer than one block get a checking pass of their own;
   // a shorter list is checked while its moving entries are gathered.
-  auto check = [&](int j, int s, int& ps, int& pd) -> int {
-    bool ok = P >= 0 && s >= P + j && s < P + p.max_nodes && (j == 0 ? s == P : s > keep[j - 1]);
+  auto check = [&](int j, int s, int prev, int& ps, int& pd) -> int {
+    bool ok = P >= 0 && s >= P + j && s < P + p.max_nodes && (j == 0 ? s == P : s > prev);
     ok = ok && s / kPage < npg && (P + j) / kPage < npg;
     if (!ok) return 1;
     ps = p.page_indices[pbase + s / kPage];
@@ -91,7 +95,7 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(CommitParams 
   if (n > kCommitThreads) {
     for (int j = tid; j < n; j += kCommitThreads) {
       int ps, pd;
-      const int bad = check(j, keep[j], ps, pd);
+      const int bad = check(j, keep[j], j > 0 ? keep[j - 1] : 0, ps, pd);
       if (bad) atomicOr(&s_bad, bad);
     }
     __syncthreads();
@@ -112,8 +116,8 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(CommitParams 
     int s = 0, spg = 0, dpg = 0;
     bool mv = false;
     if (j < n) {
-      s = keep[j];
-      const int bad = check(j, s, spg, dpg);
+      s = j0 == 0 ? keep_t : keep[j];
+      const int bad = check(j, s, j0 == 0 ? keep_prev : keep[j - 1], spg, dpg);
       if (bad) atomicOr(&s_bad, bad);
       mv = !bad && s != P + j;
     }
