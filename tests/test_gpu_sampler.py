@@ -295,6 +295,10 @@ def test_workspace_reused_across_calls():
     ws = tv.alloc_workspace(tv.sample_workspace_size(desc))
     for inp in [big, _subset(big, [46, 19, 3]), many, big, big, _subset(big, list(range(63, -1, -1)))]:
         _compare(inp, _run(inp, max_depth=8, ws=ws))
+    # both greedy forms and the walk, alternating on the same workspace
+    for gp in (True, False, True, True, False):
+        for inp in (big, _subset(big, [5, 60, 33, 2])):
+            _compare(inp, _run(inp, max_depth=8, ws=ws, greedy_path=gp), greedy_path=gp)
 
 
 def test_streamed_slices():

@@ -67,6 +67,13 @@ def load():
         raise ImportError(
             f"{LIB_PATH} is missing: build it with "
             "`python -m tree_verification_verify_amd.build` (hipcc, gfx950)")
+    # PyTorch's wheel ships its own HIP runtime under the same sonames as the
+    # one the library links (libamdhip64.so.7, libhsa-runtime64.so.1), and a
+    # process keeps whichever loads first. Importing torch first makes the
+    # library bind to torch's runtime, the one torch's device memory and
+    # streams belong to; loaded the other way round, the library's first
+    # HIP call can find no device.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.c_void_p
     I32 = ctypes.c_int32
