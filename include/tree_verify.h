@@ -427,7 +427,12 @@ tv_status tree_rerank(int32_t batch, int32_t num_cand, int32_t cand_capacity, in
  * log-sum-exp in fp32 combined in fp64, the calibration in fp64: decisions
  * agree with an fp64 evaluation except where two keys, two logits or two
  * draw scores lie within ~1e-5. Non-finite logits set TV_DEV_LOGITS, an
- * anchor outside [0, V) TV_DEV_SHAPE. */
+ * anchor outside [0, V) TV_DEV_SHAPE. The call is one launch of as many
+ * workgroups as the device keeps resident at once, which meet at grid
+ * barriers: with no other kernels running alongside all of them are
+ * resident together; workgroups held back longer than the wait limit
+ * (0.2 s) by concurrent work make the call set TV_DEV_TIMEOUT (outputs then
+ * unspecified; re-initialise the workspace) instead of hanging. */
 typedef struct {
   int32_t batch;         /* B, 1..256 */
   int32_t vocab;         /* V: max_siblings + 1 .. 4194304 */

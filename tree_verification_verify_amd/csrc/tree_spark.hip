@@ -14,8 +14,12 @@
 // K siblings); expansion stops when the best key falls below log theta or
 // the tree holds N drafted nodes (§3.5).
 //
-// GPU design: one persistent cooperative kernel runs every round, phases
-// separated by grid barriers (bounded waits):
+// GPU design: one persistent kernel runs every round, phases separated by
+// grid barriers (bounded waits). The launch is a plain one of as many
+// workgroups as the device keeps resident at once (a cooperative launch
+// costs more to start): on a device running nothing else they are all
+// resident together; workgroups held back past the wait limit by other work
+// make the call report TV_DEV_TIMEOUT instead of waiting on.
 //  A select   one workgroup per request merges the statistics of the nodes
 //             expanded last round, then pops slots while the best exact key
 //             exceeds every pending node's bound (a node not yet expanded can
@@ -1031,9 +1035,8 @@ hipError_t launch(SparkParams& p, hipStream_t stream) {
   hipError_t e = resident_workgroups<L>(&nwg);
   if (e != hipSuccess) return e;
   p.nwg = nwg;
-  void* args[] = {&p};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(spark_kernel<L>), dim3(unsigned(nwg)),
-                                    dim3(kSpThreads), args, 0, stream);
+  hipLaunchKernelGGL(spark_kernel<L>, dim3(unsigned(nwg)), dim3(kSpThreads), 0, stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace
