@@ -104,3 +104,20 @@ def test_bad_anchor_and_nonfinite_logits_are_reported():
     inp.base_logits[0, 0, 7] = np.nan
     _, st, bits = _run(inp, 8, 4)
     assert bits & (1 << 2)
+
+
+def test_barrier_wait_gives_up_when_forced_from_the_host(monkeypatch):
+    """A wait limit of 0 (set from the host for this launch only) makes the
+    grid barrier give up at once: the kernel still ends normally and reports
+    TV_DEV_TIMEOUT (status 10); a fresh workspace then builds normally."""
+    rng = np.random.default_rng(8)
+    inp = make_spark_inputs(rng, 8, vocab=2048, rank=64, temperatures=np.array([0.0, 1.0] * 4, np.float32),
+                            thetas=0.02)
+    monkeypatch.setenv("TREEVERIFY_TEAM_WAIT_US", "0")
+    _, st, bits = _run(inp, 16, 4)
+    monkeypatch.delenv("TREEVERIFY_TEAM_WAIT_US")
+    assert bits & (1 << 4) and st == 10, (st, bits)
+    got, st, bits = _run(inp, 16, 4)
+    assert st == 0, (st, bits)
+    near, total = _compare(inp, got, 16, 4)
+    assert total == 8 and near == 0

@@ -1685,9 +1685,12 @@ hipError_t device_facts(int* blocks_per_cu, int* num_cus) {
   return hipSuccess;
 }
 
-// Team wait limit: kWaitTicksDefault, or TREEVERIFY_TEAM_WAIT_US
-// microseconds when that variable is set (a diagnostic: read at every launch,
-// so a test can force waits to give up from the host).
+}  // namespace
+
+// Limit of every bounded wait (the sampler's team exchanges and barrier,
+// TreeSpark's grid barrier): kWaitTicksDefault, or TREEVERIFY_TEAM_WAIT_US
+// microseconds when that variable is set (a diagnostic: read at every
+// launch, so a test can force waits to give up from the host).
 uint64_t wait_ticks() {
   const char* v = getenv("TREEVERIFY_TEAM_WAIT_US");
   if (!v || !*v) return kWaitTicksDefault;
@@ -1695,8 +1698,6 @@ uint64_t wait_ticks() {
   const unsigned long long us = strtoull(v, &end, 10);
   return (end && *end == 0) ? uint64_t(us) * 100ull : kWaitTicksDefault;
 }
-
-}  // namespace
 
 // One launch of the walk with its status word and per-request blocks given.
 hipError_t launch_sample_core(const tv_sample_desc& d, const SampleArgs& a, uint32_t* status,

@@ -78,7 +78,6 @@ constexpr int kMaxRank = 256;
 constexpr int kGroupRows = 64;                // W1 rows staged per group
 constexpr int kW1Stride = kMaxRank + 8;       // bf16 per staged row (528 B: 16-byte shift per row)
 constexpr int kStatBatch = 8;                 // float4 loads per thread in flight (stats)
-constexpr uint64_t kSpWaitTicks = 20000000ull;  // 0.2 s of the 100 MHz counter
 
 // A request's tree, one entry per node (workspace and LDS).
 struct ReqState {
@@ -133,6 +132,7 @@ struct SparkParams {
   int B, V, r, depths, N, K, nwg;
   float a, b;
   uint32_t stream, key0, key1;
+  uint64_t wait_ticks;      // limit of the grid barrier's waits
 };
 
 // The kernel's parameters read in place (kernel-argument segment, constant
@@ -195,7 +195,7 @@ __device__ bool grid_sync(KParams& p, uint32_t& gen, int* s_dead, During&& durin
         __hip_atomic_store(p.bar + 1, gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
       } else {
         while (__hip_atomic_load(p.bar + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == gen) {
-          if (__builtin_amdgcn_s_memrealtime() - t0 > kSpWaitTicks) {
+          if (__builtin_amdgcn_s_memrealtime() - t0 > p.wait_ticks) {
             dead = true;
             break;
           }
@@ -206,7 +206,7 @@ __device__ bool grid_sync(KParams& p, uint32_t& gen, int* s_dead, During&& durin
       __hip_atomic_store(xg, gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
       while (__hip_atomic_load(xg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
-        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpWaitTicks) {
+        if (__builtin_amdgcn_s_memrealtime() - t0 > p.wait_ticks) {
           dead = true;
           break;
         }
@@ -1093,6 +1093,7 @@ hipError_t launch_spark(const tv_spark_desc& d, const SparkArgs& a, hipStream_t 
   p.stream = a.stream_id;
   p.key0 = uint32_t(a.seed);
   p.key1 = uint32_t(a.seed >> 32);
+  p.wait_ticks = wait_ticks();
   if (d.max_siblings + 1 <= 9) return launch<9>(p, stream);
   return launch<17>(p, stream);
 }

@@ -40,6 +40,10 @@ struct SamplePlan {
 bool plan_attn(const tv_attn_desc& d, AttnPlan* out);
 bool plan_sample(const tv_sample_desc& d, SamplePlan* out);
 
+// Limit of the kernels' bounded waits in real-time counter ticks (100 MHz):
+// 0.2 s, or TREEVERIFY_TEAM_WAIT_US microseconds when that variable is set.
+uint64_t wait_ticks();
+
 struct AttnArgs {
   const void* q;
   const void* k_pages;
