@@ -16,9 +16,10 @@
 // One workgroup of 512 threads per row streams the row once (float4 loads,
 // two ahead of the one being scored; one Philox call per float4). Each thread
 // keeps its K best (score, id) in registers, sorted (K = the next power of
-// two >= k). Per float4 the four score bounds (-ln u >= 1 - u gives
-// g <= -ln(1 - u), fast hardware log plus a margin) are tested against the
-// wave's threshold (below) at once: a wave executes per-token work when any
+// two >= k). Per float4 one score bound for its four tokens (-ln u >= 1 - u
+// gives g <= -ln(1 - u); the largest logit with the smallest 1 - u, one fast
+// hardware log plus a margin) is tested against the wave's threshold
+// (below): a wave executes per-token work when any
 // lane needs it, so it is entered only for the few float4 that can enter a
 // list; there each token is scored exactly (log1p for u near 1, where ln u
 // loses its relative precision) and inserted. The threads' lists are merged
@@ -168,11 +169,12 @@ __device__ void draw_row(const SibParams& p, int r, int k, float T, int32_t* out
         }
       } else {
         const uint4 w = philox4x32_10(make_uint4(uint32_t(c4), uint32_t(r), p.stream, 0u), p.key0, p.key1);
-        auto bound = [&](float dv, uint32_t wv) __attribute__((always_inline)) {
-          const float x = (float(16777216u - (wv >> 8)) - 0.5f) * (1.f / 16777216.f);  // 1 - u
-          return dv * invT - __logf(x) + 1e-3f;  // g <= -ln(1 - u)
-        };
-        const float bmax = fmaxf(fmaxf(bound(d.x, w.x), bound(d.y, w.y)), fmaxf(bound(d.z, w.z), bound(d.w, w.w)));
+        // One bound for the four tokens: the largest logit with the largest
+        // noise bound (the smallest 1 - u: the largest 24-bit word), so one
+        // logarithm instead of four; the per-token bounds follow if it passes.
+        const uint32_t wm = max(max(w.x, w.y), max(w.z, w.w)) >> 8;
+        const float xm = (float(16777216u - wm) - 0.5f) * (1.f / 16777216.f);  // smallest 1 - u
+        const float bmax = fmaxf(fmaxf(d.x, d.y), fmaxf(d.z, d.w)) * invT - __logf(xm) + 1e-3f;
         if (bmax >= theta) {
           consider(d.x, w.x, 4 * c4);
           consider(d.y, w.y, 4 * c4 + 1);
