@@ -20,9 +20,10 @@ constexpr int kPathStage = 1024;
 
 // One wave per request: from the root, find the unique flagged child with a
 // ballot over the request's rows, descend, repeat. A request of at most
-// kPathStage rows has its parents and flags staged in LDS first (one load
-// per row instead of one per row and level) and its path kept there, so
-// the outputs are written by all lanes after the walk.
+// kPathStage rows has its parents, flags, tokens and next tokens staged in
+// LDS first (one load round trip for the request instead of one per level
+// and one for the emitted tokens) and its path kept there, so the outputs
+// are written by all lanes after the walk.
 __global__ __launch_bounds__(64) void accept_path_kernel(
     int32_t batch, int32_t width, const int32_t* node_indptr, const int32_t* parent,
     const int32_t* tokens, const int8_t* flag, const int32_t* next_token,
@@ -31,6 +32,7 @@ __global__ __launch_bounds__(64) void accept_path_kernel(
   __shared__ int s_par[kPathStage];
   __shared__ int8_t s_flag[kPathStage];
   __shared__ int s_path[kPathStage];
+  __shared__ int s_tok[kPathStage], s_nt[kPathStage];
   const int r = blockIdx.x;
   const int lane = threadIdx.x;
   const int nbeg = node_indptr[r];
@@ -44,6 +46,8 @@ __global__ __launch_bounds__(64) void accept_path_kernel(
     for (int i = lane; i < N; i += 64) {
       s_par[i] = parent[nbeg + i];
       s_flag[i] = flag[nbeg + i];
+      s_tok[i] = tokens[nbeg + i];
+      s_nt[i] = next_token[nbeg + i];
     }
   }
   for (int i = lane; i < width; i += 64) {
@@ -107,7 +111,7 @@ __global__ __launch_bounds__(64) void accept_path_kernel(
       const int node = s_path[i];
       pn[i] = node;
       kk[i] = P + node;
-      ot[i] = i + 1 < len ? tokens[nbeg + s_path[i + 1]] : next_token[nbeg + v];
+      ot[i] = i + 1 < len ? s_tok[s_path[i + 1]] : s_nt[v];
     }
   }
   if (lane == 0) {
