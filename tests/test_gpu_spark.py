@@ -121,3 +121,18 @@ def test_barrier_wait_gives_up_when_forced_from_the_host(monkeypatch):
     assert st == 0, (st, bits)
     near, total = _compare(inp, got, 16, 4)
     assert total == 8 and near == 0
+
+
+def test_largest_vocabulary():
+    """V = 4,194,304, the largest the boundary accepts, at rank 256: W2 is
+    2 GB, so the largest W1/W2 row offsets come within a few MB of 2^31.
+    Two requests (T 0 and 1), anchors and drawn tokens anywhere in the
+    vocabulary, against the oracle."""
+    rng = np.random.default_rng(12)
+    inp = make_spark_inputs(rng, 2, vocab=4194304, depths=2, rank=256,
+                            temperatures=np.array([0.0, 1.0], np.float32), thetas=0.05)
+    inp.anchor[:] = [4194303, 3000001]
+    got, st, bits = _run(inp, 6, 2)
+    assert st == 0, (st, bits)
+    near, total = _compare(inp, got, 6, 2)
+    assert total == 2 and near == 0
