@@ -227,7 +227,9 @@ tv_status tree_verify_attn(const tv_attn_desc* desc,
  * device keeps resident at once, so with no other kernels running alongside
  * every team is resident together. Members held back longer than the wait
  * limit (0.2 s) by concurrent work make the call set TV_DEV_TIMEOUT (outputs
- * then unspecified) instead of hanging. */
+ * then unspecified) instead of hanging. The environment variable
+ * TREEVERIFY_TEAM_WAIT_US (microseconds), read at every launch, sets another
+ * limit for this call and tree_spark_build. */
 tv_status tree_spec_sample(const tv_sample_desc* desc,
                            const float* target_logits, const float* draft_logits,
                            const int32_t* tokens, const int32_t* node_indptr,
@@ -431,8 +433,9 @@ tv_status tree_rerank(int32_t batch, int32_t num_cand, int32_t cand_capacity, in
  * workgroups as the device keeps resident at once, which meet at grid
  * barriers: with no other kernels running alongside all of them are
  * resident together; workgroups held back longer than the wait limit
- * (0.2 s) by concurrent work make the call set TV_DEV_TIMEOUT (outputs then
- * unspecified; re-initialise the workspace) instead of hanging. */
+ * (0.2 s; TREEVERIFY_TEAM_WAIT_US, as for tree_spec_sample) by concurrent
+ * work make the call set TV_DEV_TIMEOUT (outputs then unspecified;
+ * re-initialise the workspace) instead of hanging. */
 typedef struct {
   int32_t batch;         /* B, 1..256 */
   int32_t vocab;         /* V: max_siblings + 1 .. 4194304 */
